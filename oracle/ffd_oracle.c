@@ -1,0 +1,319 @@
+/*
+ * ffd_oracle.c -- CPU oracle for Faster Flash Decoding (FFD) sparse decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is a plain, slow, obviously-correct reference that the
+ * tests, the package's smoke check and the benchmark's CPU-baseline leg call to check the HIP
+ * library.  The product path never links, loads or calls it, and it shares no code, header,
+ * table or constant generator with the HIP library.
+ *
+ * Source: the paper "Faster Than Flash: Exploiting Attention Sparsity for Efficient
+ * Long-Context Decoding" (arXiv 2609.00097), cited below as FTF.
+ *
+ * What it computes, for one new token per sequence (one query vector per query head):
+ *   O1  quantize     App. A, Eqs. 5-7: symmetric mid-rise (zero-free) uniform quantizer of each
+ *                    channel vector of a block of keys, generalized from 4 levels to 2^bits levels.
+ *   O2  scan         Alg. 1, top-delta selection stage: estimated score of every token of every
+ *                    full block from the low-bit keys; block score = max over the block.
+ *   O5  pseudo-max   Eq. 3 and Alg. 1, pseudo-max stage: max estimated score over the sink block
+ *                    and the local block.
+ *   O6/O7 select     Eq. 1 with the pseudo-max in place of the true max: keep block j iff its
+ *                    estimated max >= pseudo-max - delta.
+ *   O8  attention    Alg. 1, refinement stage: exact softmax(q K^T / sqrt(d)) V over the tokens of
+ *                    the kept blocks, in double precision.
+ *   O9  dense        the same over every token (FlashAttention-style exact decode, FTF Sec. 2).
+ *
+ * Readings of points the paper leaves open (each is also listed in the design notes):
+ *   - Quantizer levels: value of code u is (u - (2^bits-1)/2) * s, s = amax / ((2^bits-1)/2).
+ *     For bits = 2 this is exactly App. A (codebook {-1.5,-0.5,+0.5,+1.5}, s = max|x| / 1.5).
+ *   - Quantizer rounding: s = RN(amax/half), inv = RN(half/amax), y = RN(x*inv),
+ *     u = clamp(floor(y) + 2^(bits-1), 0, 2^bits - 1).  floor(y) + 2^(bits-1) is the index of the
+ *     nearest codeword (Eq. 7); a value exactly on a bin boundary goes to the upper bin.
+ *     amax == 0 gives s = 0 and every code = 2^(bits-1).
+ *   - Scale group: one scale per (block of T tokens, channel).
+ *   - Scan arithmetic (integer-exact): per (query head, block) w_c = RN(q_c * s_c),
+ *     W = max_c |w_c|; if W == 0 all estimates are 0; otherwise rho = RN(127/W),
+ *     wi_c = rint_even(RN(w_c*rho)) clamped to [-127,127], E_t = sum_c wi_c * (2u_tc - (2^bits-1))
+ *     (exact integer), f = RN(W * kappa) with kappa = (float)(0.5 / (127 * sqrt(d))) and the
+ *     estimated score shat_t = RN((float)E_t * f).  The 1/sqrt(d) of Eq. 1 is included so that
+ *     estimates, pseudo-max and delta share logit units.
+ *   - Pseudo-max source: the estimated scores (as in Alg. 1's pseudo-max stage), over sink block 0
+ *     and the last full block (the local block).
+ *   - Forced blocks: block 0, the last full block and a partial tail block are always kept; the
+ *     tail has no low-bit copy and is not part of the pseudo-max.  With no full block every token
+ *     is kept.
+ *   - Threshold: theta = RN(mtilde - delta) in float; keep iff shat_block >= theta.
+ *   - Exact scores use the stored key (bf16 or fp32 values), not the dequantized low-bit key.
+ *
+ * All float operations above are single IEEE binary32 operations, round-to-nearest-even; the
+ * file is built with -ffp-contract=off and without fast-math so that none are fused.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define FFDO_DTYPE_F32 0
+#define FFDO_DTYPE_BF16 1
+
+int ffdo_version(void) { return 1; }
+
+/* Element t*ld + c of a key/value array stored as fp32 or as bf16 bit patterns. */
+static float load_elem(const void* base, int dtype, size_t idx)
+{
+    if (dtype == FFDO_DTYPE_F32) return ((const float*)base)[idx];
+    uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16; /* bf16 = top half of fp32 */
+    float v;
+    memcpy(&v, &bits, sizeof v);
+    return v;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* O1: App. A quantizer for one channel vector x[0..n) (stride `stride` floats).               */
+/* ------------------------------------------------------------------------------------------ */
+void ffdo_quantize_channel(const float* x, int n, int stride, int bits, uint8_t* codes,
+                           float* scale_out)
+{
+    const int levels = 1 << bits;
+    const float half = (float)(levels - 1) * 0.5f; /* 1.5 for 2 bits, 7.5 for 4 bits */
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float a = fabsf(x[(size_t)i * stride]);
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+        *scale_out = 0.0f;
+        for (int i = 0; i < n; ++i) codes[i] = (uint8_t)(levels / 2);
+        return;
+    }
+    const float s = amax / half;   /* Eq. 6, one rounding */
+    const float inv = half / amax; /* one rounding */
+    *scale_out = s;
+    for (int i = 0; i < n; ++i) {
+        const float y = x[(size_t)i * stride] * inv; /* one rounding */
+        int u = (int)floorf(y) + levels / 2;        /* nearest codeword index, Eq. 7 */
+        if (u < 0) u = 0;
+        if (u > levels - 1) u = levels - 1;
+        codes[i] = (uint8_t)u;
+    }
+}
+
+/*
+ * O1 for one (batch, kv-head) slice.  K is [L_cap][d] (fp32 or bf16 bits).  Every full block j
+ * whose last token index (j+1)*T-1 lies in [tok_begin, tok_end) is quantized:
+ *   Kq[t][i] = code(t, 2i) | code(t, 2i+1) << 4      (4-bit codes, two channels per byte)
+ *   scales[j][c] = s of channel c of block j.
+ * Returns the number of blocks written.
+ */
+int ffdo_quantize_k(const void* K, int dtype, int L_cap, int d, int T, int tok_begin,
+                    int tok_end, uint8_t* Kq, float* scales)
+{
+    if (d % 2 || T <= 0 || L_cap % T) return -1;
+    const int n_cap_blocks = L_cap / T;
+    float* x = (float*)malloc(sizeof(float) * (size_t)T);
+    uint8_t* codes = (uint8_t*)malloc((size_t)T * (size_t)d);
+    uint8_t* col = (uint8_t*)malloc((size_t)T);
+    int written = 0;
+    for (int j = 0; j < n_cap_blocks; ++j) {
+        const int last = (j + 1) * T - 1;
+        if (last < tok_begin || last >= tok_end) continue;
+        for (int c = 0; c < d; ++c) {
+            for (int t = 0; t < T; ++t) x[t] = load_elem(K, dtype, (size_t)(j * T + t) * d + c);
+            ffdo_quantize_channel(x, T, 1, 4, col, &scales[(size_t)j * d + c]);
+            for (int t = 0; t < T; ++t) codes[(size_t)t * d + c] = col[t];
+        }
+        for (int t = 0; t < T; ++t) {
+            uint8_t* row = Kq + (size_t)(j * T + t) * (d / 2);
+            for (int i = 0; i < d / 2; ++i)
+                row[i] = (uint8_t)(codes[(size_t)t * d + 2 * i] |
+                                   (codes[(size_t)t * d + 2 * i + 1] << 4));
+        }
+        ++written;
+    }
+    free(x);
+    free(codes);
+    free(col);
+    return written;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* O2: integer-exact scan.                                                                     */
+/* ------------------------------------------------------------------------------------------ */
+float ffdo_kappa(int d) { return (float)(0.5 / (127.0 * sqrt((double)d))); }
+
+/*
+ * Requantization of w = q (.) s for one (query head, block): writes wi[0..d) and returns
+ * f = RN(W*kappa) (0 when W == 0, in which case every wi is 0).
+ */
+float ffdo_requant(const float* qh, const float* s, int d, int32_t* wi)
+{
+    float W = 0.0f;
+    for (int c = 0; c < d; ++c) {
+        const float w = qh[c] * s[c];
+        if (fabsf(w) > W) W = fabsf(w);
+    }
+    if (W == 0.0f) {
+        for (int c = 0; c < d; ++c) wi[c] = 0;
+        return 0.0f;
+    }
+    const float rho = 127.0f / W;
+    for (int c = 0; c < d; ++c) {
+        const float w = qh[c] * s[c];
+        float v = rintf(w * rho); /* ties to even under the default rounding mode */
+        if (v > 127.0f) v = 127.0f;
+        if (v < -127.0f) v = -127.0f;
+        wi[c] = (int32_t)v;
+    }
+    return W * ffdo_kappa(d);
+}
+
+/*
+ * Scan of one query head over the full blocks of its kv-head slice.
+ *   qh[d]                      query (fp32 values)
+ *   Kq[n_full*T][d/2]          packed 4-bit codes
+ *   scales[n_full][d]
+ * Outputs: shat_block[n_full] (block estimate = max over its tokens) and, if non-NULL,
+ * shat_tok[n_full*T] and E_tok[n_full*T] (the exact integer sums).
+ */
+void ffdo_scan_head(const float* qh, const uint8_t* Kq, const float* scales, int n_full, int T,
+                    int d, float* shat_block, float* shat_tok, int32_t* E_tok)
+{
+    int32_t* wi = (int32_t*)malloc(sizeof(int32_t) * (size_t)d);
+    for (int j = 0; j < n_full; ++j) {
+        const float f = ffdo_requant(qh, scales + (size_t)j * d, d, wi);
+        float best = -INFINITY;
+        for (int t = 0; t < T; ++t) {
+            const uint8_t* row = Kq + (size_t)(j * T + t) * (d / 2);
+            int64_t E = 0;
+            for (int c = 0; c < d; ++c) {
+                const int u = (c & 1) ? (row[c / 2] >> 4) : (row[c / 2] & 15);
+                E += (int64_t)wi[c] * (int64_t)(2 * u - 15);
+            }
+            const float sh = (float)E * f;
+            if (shat_tok) shat_tok[(size_t)j * T + t] = sh;
+            if (E_tok) E_tok[(size_t)j * T + t] = (int32_t)E;
+            if (sh > best) best = sh;
+        }
+        shat_block[j] = best;
+    }
+    free(wi);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* O5-O7: pseudo-max, threshold and block mask for one query head.                             */
+/* ------------------------------------------------------------------------------------------ */
+/*
+ * n_full full blocks, n_blocks = ceil(L/T) blocks in total (the last one may be a partial tail).
+ * keep[n_blocks] receives 0/1.  mtilde/theta receive the pseudo-max and threshold (NaN when
+ * n_full == 0: then every block is kept).
+ */
+void ffdo_select_head(const float* shat_block, int n_full, int n_blocks, float delta,
+                      uint8_t* keep, float* mtilde_out, float* theta_out)
+{
+    if (n_full == 0) {
+        for (int j = 0; j < n_blocks; ++j) keep[j] = 1;
+        if (mtilde_out) *mtilde_out = NAN;
+        if (theta_out) *theta_out = NAN;
+        return;
+    }
+    const float s_global = shat_block[0];          /* sink block */
+    const float s_local = shat_block[n_full - 1];  /* last full block */
+    const float mtilde = s_global > s_local ? s_global : s_local;
+    const float theta = mtilde - delta;            /* delta = +inf gives -inf */
+    for (int j = 0; j < n_blocks; ++j) {
+        if (j == 0 || j >= n_full - 1) keep[j] = 1; /* sink, local, tail */
+        else keep[j] = shat_block[j] >= theta ? 1 : 0;
+    }
+    if (mtilde_out) *mtilde_out = mtilde;
+    if (theta_out) *theta_out = theta;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* O8/O9: exact attention over the tokens of kept blocks, in double precision.                 */
+/* ------------------------------------------------------------------------------------------ */
+/*
+ * One query head.  K, V: [L_cap][d] slices (fp32 or bf16 bits), tokens 0..L-1 valid.
+ * keep: [ceil(L/T)] block mask, or NULL for dense.  out[d] and lse receive
+ * o = sum_t p_t V_t with p = softmax over kept tokens of s_t = q.K_t / sqrt(d), and
+ * lse = log sum_t exp(s_t).
+ */
+void ffdo_attend_head(const float* qh, const void* K, const void* V, int dtype, int L, int d,
+                      int T, const uint8_t* keep, double* out, double* lse)
+{
+    double* s = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    double m = -INFINITY;
+    for (int t = 0; t < L; ++t) {
+        if (keep && !keep[t / T]) { s[t] = -INFINITY; continue; }
+        double acc = 0.0;
+        for (int c = 0; c < d; ++c)
+            acc += (double)qh[c] * (double)load_elem(K, dtype, (size_t)t * d + c);
+        s[t] = acc * inv_sqrt_d;
+        if (s[t] > m) m = s[t];
+    }
+    double l = 0.0;
+    for (int c = 0; c < d; ++c) out[c] = 0.0;
+    for (int t = 0; t < L; ++t) {
+        if (s[t] == -INFINITY) continue;
+        const double p = exp(s[t] - m);
+        l += p;
+        for (int c = 0; c < d; ++c) out[c] += p * (double)load_elem(V, dtype, (size_t)t * d + c);
+    }
+    for (int c = 0; c < d; ++c) out[c] /= l;
+    *lse = m + log(l);
+    free(s);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Batch driver: the whole decode step, OpenMP over (batch, query head).                       */
+/* ------------------------------------------------------------------------------------------ */
+/*
+ * q       [B][Hq][d]              fp32 or bf16 bits
+ * K, V    [B][Hkv][L_cap][d]      fp32 or bf16 bits
+ * Kq      [B][Hkv][L_cap][d/2]    packed codes      (sparse mode only)
+ * scales  [B][Hkv][L_cap/T][d]                      (sparse mode only)
+ * sparse  1: O2-O8, 0: O9 (dense)
+ * out     [B][Hq][d] double, lse [B][Hq] double
+ * keep    [B][Hq][ceil(L/T)] (sparse, may be NULL)
+ * shat    [B][Hq][floor(L/T)] block estimates (sparse, may be NULL)
+ * mtilde  [B][Hq] (sparse, may be NULL)
+ * Query head h reads kv head h / (Hq/Hkv).  Returns the number of (b, h) rows done.
+ */
+int ffdo_decode(int B, int Hq, int Hkv, int d, int L, int L_cap, int T, int dtype,
+                const void* q, const void* K, const void* V, const uint8_t* Kq,
+                const float* scales, float delta, int sparse, double* out, double* lse,
+                uint8_t* keep, float* shat, float* mtilde, int n_threads)
+{
+    if (Hkv <= 0 || Hq % Hkv || d % 2 || T <= 0 || L < 0 || L > L_cap || L_cap % T) return -1;
+    const int G = Hq / Hkv;
+    const int n_full = L / T;
+    const int n_blocks = (L + T - 1) / T;
+    const size_t esz = dtype == FFDO_DTYPE_F32 ? 4 : 2;
+    const int rows = B * Hq;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads > 0 ? n_threads : 1)
+    for (int r = 0; r < rows; ++r) {
+        const int b = r / Hq, h = r % Hq, g = h / G;
+        float* qh = (float*)malloc(sizeof(float) * (size_t)d);
+        for (int c = 0; c < d; ++c) qh[c] = load_elem(q, dtype, (size_t)r * d + c);
+        const size_t kv_off = ((size_t)b * Hkv + g) * (size_t)L_cap * d;
+        const char* Kbg = (const char*)K + kv_off * esz;
+        const char* Vbg = (const char*)V + kv_off * esz;
+        uint8_t* kp = NULL;
+        if (sparse) {
+            const uint8_t* Kq_bg = Kq + ((size_t)b * Hkv + g) * (size_t)L_cap * (d / 2);
+            const float* sc_bg = scales + ((size_t)b * Hkv + g) * (size_t)(L_cap / T) * d;
+            float* sb = (float*)malloc(sizeof(float) * (size_t)(n_full > 0 ? n_full : 1));
+            kp = (uint8_t*)malloc((size_t)(n_blocks > 0 ? n_blocks : 1));
+            ffdo_scan_head(qh, Kq_bg, sc_bg, n_full, T, d, sb, NULL, NULL);
+            float mt;
+            ffdo_select_head(sb, n_full, n_blocks, delta, kp, &mt, NULL);
+            if (keep) memcpy(keep + (size_t)r * n_blocks, kp, (size_t)n_blocks);
+            if (shat) memcpy(shat + (size_t)r * n_full, sb, sizeof(float) * (size_t)n_full);
+            if (mtilde) mtilde[r] = mt;
+            free(sb);
+        }
+        ffdo_attend_head(qh, Kbg, Vbg, dtype, L, d, T, kp, out + (size_t)r * d, lse + r);
+        free(kp);
+        free(qh);
+    }
+    return rows;
+}

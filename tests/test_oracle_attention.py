@@ -1,0 +1,122 @@
+"""Pins for the oracle's exact attention and for the whole sparse decode step.
+
+"Faster Than Flash" Alg. 1 (refinement stage) runs exact softmax(q K^T / sqrt(d)) V over the
+tokens of the kept blocks.  Pins: the dense oracle against PyTorch's scaled_dot_product_attention
+in fp64 on the CPU (a library routine), delta = +inf equal to dense, a planted one-hot block and a
+planted single token, lse(sparse) <= lse(dense), and Eq. 2's guarantee carried through the scan
+error: every dropped token is at least delta - 2*eps below a kept token, so
+0 <= lse_dense - lse_sparse <= ln(1 + n_drop * e^(2*eps - delta)).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_decoding_amd import workloads as W
+
+
+def vals(a):
+    return oracle.to_f32(a).astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("L,T", [(64, 64), (200, 64), (3 * 128 + 5, 128)])
+def test_dense_matches_torch_sdpa_fp64(dtype, L, T):
+    w = W.small("t", B=2, Hq=8, Hkv=2, L=L, T=T, dtype=dtype, seed=L)
+    q, K, V, _ = W.make_inputs(w)
+    res = oracle.decode(q, K, V, L, T, sparse=False)
+    G = w.G
+    qt = torch.from_numpy(vals(q))[:, :, None, :]                     # [B,Hq,1,d]
+    Kt = torch.from_numpy(vals(K[:, :, :L])).repeat_interleave(G, 1)   # [B,Hq,L,d]
+    Vt = torch.from_numpy(vals(V[:, :, :L])).repeat_interleave(G, 1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt)[:, :, 0]
+    np.testing.assert_allclose(res["out"], ref.numpy(), rtol=0, atol=1e-12)
+    logits = torch.einsum("bhd,bhld->bhl", qt[:, :, 0], Kt) / math.sqrt(w.d)
+    np.testing.assert_allclose(res["lse"], torch.logsumexp(logits, -1).numpy(), atol=1e-12)
+
+
+def test_delta_inf_equals_dense():
+    w = W.small("t", B=1, Hq=4, Hkv=1, L=9 * 64 + 3, T=64, seed=2)
+    q, K, V, _ = W.make_inputs(w)
+    Kq, sc = oracle.quantize_k(K, w.T)
+    sp = oracle.decode(q, K, V, w.L, w.T, delta=float("inf"), Kq=Kq, scales=sc)
+    de = oracle.decode(q, K, V, w.L, w.T, sparse=False)
+    assert sp["keep"].all()
+    np.testing.assert_array_equal(sp["out"], de["out"])
+    np.testing.assert_array_equal(sp["lse"], de["lse"])
+
+
+def test_one_hot_planted_block():
+    """One block of identical keys at a logit >= 60 above everything else: the output is the
+    mean of that block's value rows."""
+    rng = np.random.default_rng(4)
+    T, d, n = 64, 128, 12
+    q = rng.standard_normal(d).astype(np.float32)
+    K = rng.standard_normal((n * T, d)).astype(np.float32) * 0.5
+    j_star = 7
+    key = (q / np.linalg.norm(q)) * (70 * math.sqrt(d) / np.linalg.norm(q))
+    K[j_star * T:(j_star + 1) * T] = key.astype(np.float32)
+    V = rng.standard_normal((n * T, d)).astype(np.float32)
+    Kq, sc = oracle.quantize_k(K[None, None], T)
+    res = oracle.decode(q[None, None], K[None, None], V[None, None], n * T, T, delta=5.0,
+                        Kq=Kq, scales=sc)
+    assert res["keep"][0, 0, j_star] == 1
+    expect = V[j_star * T:(j_star + 1) * T].astype(np.float64).mean(axis=0)
+    np.testing.assert_allclose(res["out"][0, 0], expect, atol=1e-12)
+
+
+def test_single_planted_token():
+    rng = np.random.default_rng(9)
+    T, d, n = 64, 128, 6
+    q = rng.standard_normal(d).astype(np.float32)
+    K = rng.standard_normal((n * T, d)).astype(np.float32) * 0.2
+    t_star = 3 * T + 17
+    K[t_star] = (q * (80 * math.sqrt(d) / float(q @ q))).astype(np.float32)
+    V = rng.standard_normal((n * T, d)).astype(np.float32)
+    Kq, sc = oracle.quantize_k(K[None, None], T)
+    res = oracle.decode(q[None, None], K[None, None], V[None, None], n * T, T, delta=5.0,
+                        Kq=Kq, scales=sc)
+    np.testing.assert_allclose(res["out"][0, 0], V[t_star].astype(np.float64), atol=1e-12)
+
+
+def scan_eps(q, K, Kq, sc, w, b, h):
+    """max over tokens of full blocks of |shat_t - s_t| for one head."""
+    g = h // w.G
+    _, st, _ = oracle.scan_head(q[b, h], Kq[b, g], sc[b, g], w.n_full, w.T, per_token=True)
+    exact = vals(K[b, g, : w.n_full * w.T]) @ vals(q[b, h]) / math.sqrt(w.d)
+    return float(np.abs(st - exact).max())
+
+
+@pytest.mark.parametrize("plant", ["needles", "powerlaw", "flat"])
+@pytest.mark.parametrize("delta", [0.5, 2.0, 5.0])
+def test_dropped_mass_bound(plant, delta):
+    w = W.small("t", B=2, Hq=8, Hkv=2, L=48 * 64, T=64, seed=17, plant=plant)
+    q, K, V, _ = W.make_inputs(w)
+    Kq, sc = oracle.quantize_k(K, w.T)
+    sp = oracle.decode(q, K, V, w.L, w.T, delta=delta, Kq=Kq, scales=sc)
+    de = oracle.decode(q, K, V, w.L, w.T, sparse=False)
+    vmax = np.abs(vals(V[:, :, : w.L])).max()
+    for b in range(w.B):
+        for h in range(w.Hq):
+            eps = scan_eps(q, K, Kq, sc, w, b, h)
+            n_drop = int((1 - sp["keep"][b, h]).sum()) * w.T
+            gap = de["lse"][b, h] - sp["lse"][b, h]
+            assert gap >= -1e-12
+            r = n_drop * math.exp(2 * eps - delta + 1e-6)
+            assert gap <= math.log1p(r) + 1e-12, (b, h, gap, r)
+            err = np.abs(de["out"][b, h] - sp["out"][b, h]).max()
+            assert err <= 2 * vmax * r / (1 + r) + 1e-12
+
+
+def test_needle_workload_keeps_needles():
+    """On the sink + needle recipe at delta=5 the needle blocks are kept and most blocks are not."""
+    w = W.WORKLOADS["gqa4_32k_sink_needles"].with_(L=4096, n_needles=4)
+    q, K, V, info = W.make_inputs(w)
+    Kq, sc = oracle.quantize_k(K, w.T)
+    res = oracle.decode(q, K, V, w.L, w.T, delta=5.0, Kq=Kq, scales=sc)
+    hits = [res["keep"][0, g * w.G:(g + 1) * w.G, j]
+            for g in range(w.Hkv) for j in info["needles"][(0, g)]]
+    assert np.mean(hits) > 0.75  # needle max ~ 6 + 2.5 vs threshold ~ 12.5 - 5: most pass
+    assert res["keep"].mean() < 0.3

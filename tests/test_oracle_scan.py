@@ -1,0 +1,155 @@
+"""Pins for the oracle's low-bit scan (estimated scores).
+
+"Faster Than Flash" Alg. 1 (top-delta selection stage) estimates each block's scores as the dot
+product of the query with the low-bit keys; App. B (Eq. 8) writes the estimate as the exact score
+plus q.eps/sqrt(d), eps being the key quantization error.  The oracle evaluates that dot product
+in exact integer arithmetic after an int8 requantization of q (.) s.  Pins:
+
+* an exactly-representable construction (keys on the codebook grid, power-of-two scales, integer
+  queries) where the estimate must equal the exact score q.k/sqrt(d) to a few ulps;
+* a one-hot query, where the estimate is the dequantized key channel (closed form);
+* an independent int64 recomputation of the integer sums from the unpacked nibbles;
+* a deterministic version of App. B's error bound, asserted for every token;
+* exact scaling by powers of two.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from long_context_decoding_amd import workloads as W
+
+
+def unpack(Kq):
+    """[..., d/2] packed bytes -> [..., d] codes (low nibble = even channel)."""
+    lo = Kq & 15
+    hi = Kq >> 4
+    return np.stack([lo, hi], axis=-1).reshape(*Kq.shape[:-1], Kq.shape[-1] * 2).astype(np.int64)
+
+
+def grid_keys(rng, n_blocks, T, d, exps):
+    """Keys exactly on the 4-bit grid: x = (u - 7.5) * 2^e_j, each channel reaching |x| = 7.5*2^e."""
+    u = rng.integers(0, 16, size=(n_blocks, T, d))
+    u[:, 0, :] = np.where(rng.random((n_blocks, d)) < 0.5, 0, 15)  # pin amax per channel
+    s = np.asarray([2.0 ** e for e in exps])[:, None, None]
+    x = ((u - 7.5) * s).reshape(n_blocks * T, d).astype(np.float32)
+    return x, u.reshape(n_blocks * T, d)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_scan_exact_on_grid(seed):
+    rng = np.random.default_rng(seed)
+    T, d, n = 64, 128, 6
+    exps = rng.integers(-4, 3, size=n)
+    x, u = grid_keys(rng, n, T, d, exps)
+    K = x[None, None]
+    Kq, sc = oracle.quantize_k(K, T)
+    assert (unpack(Kq[0, 0]) == u).all(), "quantizer must recover grid codes exactly"
+    assert (sc[0, 0] == (2.0 ** exps)[:, None]).all()
+    q = rng.integers(-127, 128, size=d).astype(np.float32)
+    q[rng.integers(d)] = 127.0 * (1 if rng.random() < 0.5 else -1)
+    sb, st, Et = oracle.scan_head(q, Kq[0, 0], sc[0, 0], n, T, per_token=True)
+    exact = (x.astype(np.float64) @ q.astype(np.float64)) / math.sqrt(d)
+    err = np.abs(st - exact)
+    assert (err <= 4 * 2.0 ** -24 * np.abs(exact) + 1e-30).all(), err.max()
+    np.testing.assert_array_equal(sb, st.reshape(n, T).max(axis=1))
+
+
+@pytest.mark.parametrize("c", [0, 1, 64, 127])
+def test_scan_one_hot_query(c):
+    """q = alpha * e_c: the estimate is the dequantized key (u - 7.5) * s_c * alpha / sqrt(d)."""
+    rng = np.random.default_rng(c)
+    T, d, n = 64, 128, 3
+    K = W.f32_to_bf16_bits(rng.standard_normal((1, 1, n * T, d)).astype(np.float32) * 2)
+    Kq, sc = oracle.quantize_k(K, T)
+    alpha = 1.75
+    q = np.zeros(d, np.float32)
+    q[c] = alpha
+    sb, st, _ = oracle.scan_head(q, Kq[0, 0], sc[0, 0], n, T, per_token=True)
+    codes = unpack(Kq[0, 0])[:, c]
+    s_c = np.repeat(sc[0, 0, :, c], T).astype(np.float64)
+    expect = (codes - 7.5) * s_c * alpha / math.sqrt(d)
+    np.testing.assert_allclose(st, expect, rtol=4 * 2.0 ** -24, atol=0)
+
+
+def test_integer_sums_recomputed_int64():
+    rng = np.random.default_rng(11)
+    T, d, n = 128, 128, 4
+    K = W.f32_to_bf16_bits(rng.standard_normal((1, 1, n * T, d)).astype(np.float32))
+    Kq, sc = oracle.quantize_k(K, T)
+    q = W.bf16_bits_to_f32(W.f32_to_bf16_bits(rng.standard_normal(d).astype(np.float32)))
+    _, st, Et = oracle.scan_head(q, Kq[0, 0], sc[0, 0], n, T, per_token=True)
+    codes = unpack(Kq[0, 0])
+    for j in range(n):
+        wi, f = oracle.requant(q, sc[0, 0, j])
+        # requantization: max |wi| is 127 and wi * W/127 is within half a step of q (.) s
+        w = q.astype(np.float64) * sc[0, 0, j].astype(np.float64)
+        Wmax = np.abs(w).max()
+        assert np.abs(wi).max() == 127
+        assert (np.abs(wi * Wmax / 127 - w) <= Wmax / 127 * (0.5 + 2 ** -18)).all()
+        assert abs(f - Wmax * 0.5 / (127 * math.sqrt(d))) <= 2 * 2.0 ** -24 * f
+        E = (codes[j * T:(j + 1) * T] * 2 - 15) @ wi.astype(np.int64)
+        np.testing.assert_array_equal(Et[j * T:(j + 1) * T], E)
+        np.testing.assert_array_equal(st[j * T:(j + 1) * T], (E.astype(np.float32) * np.float32(f)))
+
+
+def test_zero_query_and_zero_block():
+    T, d = 64, 128
+    rng = np.random.default_rng(0)
+    K32 = rng.standard_normal((1, 1, 2 * T, d)).astype(np.float32)
+    K32[0, 0, T:] = 0.0  # block 1 all zero -> zero scales
+    Kq, sc = oracle.quantize_k(K32, T)
+    assert (sc[0, 0, 1] == 0).all()
+    q = rng.standard_normal(d).astype(np.float32)
+    sb, st, Et = oracle.scan_head(q, Kq[0, 0], sc[0, 0], 2, T, per_token=True)
+    assert (st[T:] == 0).all() and (Et[T:] == 0).all() and sb[1] == 0
+    sb0 = oracle.scan_head(np.zeros(d, np.float32), Kq[0, 0], sc[0, 0], 2, T)
+    assert (sb0 == 0).all()
+
+
+def test_power_of_two_scaling():
+    rng = np.random.default_rng(5)
+    T, d, n = 64, 128, 5
+    K = W.f32_to_bf16_bits(rng.standard_normal((1, 1, n * T, d)).astype(np.float32))
+    Kq, sc = oracle.quantize_k(K, T)
+    q = rng.standard_normal(d).astype(np.float32)
+    _, st1, E1 = oracle.scan_head(q, Kq[0, 0], sc[0, 0], n, T, per_token=True)
+    _, st2, E2 = oracle.scan_head(q * 4, Kq[0, 0], sc[0, 0], n, T, per_token=True)
+    np.testing.assert_array_equal(E1, E2)
+    np.testing.assert_array_equal(st1 * 4, st2)
+
+
+def error_bound(q, x, codes, s_tok, sigma_tok, shat, d):
+    """Deterministic bound on |shat_t - s_t| (App. B, Eq. 8, with worst-case instead of
+    sub-Gaussian noise): key quantization error <= s/2 per channel, requantization error of
+    q (.) s <= sigma/2 per channel (sigma = W/127), a few float roundings."""
+    qa = np.abs(q.astype(np.float64))
+    cu = np.abs(codes - 7.5)
+    key_term = (qa[None, :] * s_tok / 2).sum(axis=1)
+    req_term = sigma_tok[:, 0] / 2 * cu.sum(axis=1)
+    w_round = (qa[None, :] * s_tok * cu).sum(axis=1) * 2.0 ** -23
+    return (key_term + req_term) * (1 + 2 ** -14) / math.sqrt(d) + w_round / math.sqrt(d) + \
+        4 * 2.0 ** -24 * np.abs(shat) + 1e-12
+
+
+@pytest.mark.parametrize("name,T", [("gqa4_32k_sink_needles", 64), ("gqa4_256k_sink_needles", 128)])
+def test_error_bound_on_workload_slices(name, T):
+    w = W.WORKLOADS[name].with_(L=32 * T, B=1, Hkv=1, Hq=4)
+    q, K, V, _ = W.make_inputs(w)
+    Kq, sc = oracle.quantize_k(K, T)
+    x = W.bf16_bits_to_f32(K[0, 0]).astype(np.float64)
+    codes = unpack(Kq[0, 0])
+    n = w.n_full
+    for h in range(4):
+        qh = W.bf16_bits_to_f32(q[0, h])
+        _, st, _ = oracle.scan_head(qh, Kq[0, 0], sc[0, 0], n, T, per_token=True)
+        exact = x[: n * T] @ qh.astype(np.float64) / math.sqrt(w.d)
+        s_tok = np.repeat(sc[0, 0, :n].astype(np.float64), T, axis=0)
+        sig = np.repeat(np.abs(qh[None, :] * sc[0, 0, :n]).max(axis=1, keepdims=True) / 127, T,
+                        axis=0)
+        bound = error_bound(qh, x, codes[: n * T], s_tok, sig, st, w.d)
+        err = np.abs(st - exact)
+        assert (err <= bound).all(), (h, (err / bound).max())
+        # and the estimate is useful: typical error well under a logit
+        assert np.median(err) < 0.5
