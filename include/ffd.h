@@ -1,0 +1,140 @@
+/*
+ * ffd.h -- C ABI of libffd, MI355X-native (gfx950) Faster Flash Decoding.
+ *
+ * Source of the method: "Faster Than Flash: Exploiting Attention Sparsity for Efficient
+ * Long-Context Decoding" (arXiv 2609.00097).  For one new token per sequence, a decode step
+ *   1. scans a low-bit copy of every full key block (Sec. 3.1, App. A),
+ *   2. estimates a pseudo-max from the sink block and the local block (Sec. 3.2, Eq. 3),
+ *   3. keeps a block when its estimated maximum logit is within delta of the pseudo-max
+ *      (Sec. 3.2, Eq. 1; no sort, no cross-block synchronization),
+ *   4. runs exact softmax(q K^T / sqrt(d)) V over the kept blocks only (Alg. 1, refinement), and
+ *   5. merges the per-split partial softmax states with a log-sum-exp combine (the split-KV
+ *      decoding of Sec. 2, FlashDecoding).
+ *
+ * Conventions shared by every call
+ *   - All tensors are dense, row-major, contiguous device allocations owned by the caller.
+ *     The library allocates and frees nothing and keeps no state between calls.
+ *   - Every pointer must be 16-byte aligned.
+ *   - Shapes (B = batch, Hq = query heads, Hkv = kv heads, d = head_dim = 128, T = block):
+ *         q        [B, Hq, d]             dims.dtype (fp32 or bf16)
+ *         K, V     [B, Hkv, seq_cap, d]   dims.dtype
+ *         Kq       [B, Hkv, seq_cap, d/2] uint8: byte i of a token row holds the 4-bit code of
+ *                                         channel 2i in bits 0-3 and of channel 2i+1 in bits 4-7
+ *         scales   [B, Hkv, seq_cap/T, d] fp32: one scale per (block, channel)
+ *         out      [B, Hq, d]             fp32
+ *         lse      [B, Hq]                fp32, natural log of the softmax denominator
+ *         keep_mask[B, Hq, ceil(L/T)]     uint8, 1 = block used for that query head
+ *     Query head h reads kv head h / (Hq/Hkv) (contiguous groups).
+ *   - Calls are asynchronous on `stream` and never synchronize.  They are thread-safe: no
+ *     mutable global state.  No C++ exception crosses the ABI.
+ *   - Argument validation runs before any HIP call: on failure a call returns
+ *     FFD_ERR_INVALID_ARG or FFD_ERR_UNSUPPORTED and launches nothing.  A HIP error reported
+ *     right after a launch returns FFD_ERR_HIP.
+ *   - NaN or Inf in q, K or V gives unspecified results.
+ *
+ * Low-bit code and scan definitions (fixed readings of what the paper leaves open):
+ *   code u in 0..15 of channel c of a token in block j stands for (u - 7.5) * s[j][c] with
+ *   s = RN(amax / 7.5) and amax = max |K| over the block's T tokens in that channel (App. A,
+ *   Eqs. 5-7 with 16 levels instead of 4); u = clamp(floor(RN(x * RN(7.5 / amax))) + 8, 0, 15);
+ *   amax = 0 gives s = 0 and u = 8.
+ *   Estimated block score of query head h (Alg. 1 scan): w_c = RN(q_c * s_c), W = max|w_c|,
+ *   wi_c = rint(RN(w_c * RN(127 / W))), E_t = sum_c wi_c * (2 u_tc - 15) in exact integers,
+ *   shat_j = RN(float(max_t E_t) * RN(W * kappa)) with kappa = (float)(0.5 / (127 sqrt(d))),
+ *   and shat_j = 0 when W = 0.  Pseudo-max: mtilde = max(shat_0, shat_{nf-1}), nf = floor(L/T).
+ *   Block j is kept iff j = 0, j >= nf - 1 (local block and a partial tail), or
+ *   shat_j >= RN(mtilde - delta).  With nf = 0 every token is kept.
+ */
+#ifndef FFD_H
+#define FFD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FFD_ABI_VERSION 1
+#define FFD_BITS 4          /* bits per key channel in the scanned copy */
+#define FFD_SINK_BLOCKS 1   /* S_global of Eq. 3: block 0 */
+#define FFD_LOCAL_BLOCKS 1  /* S_local of Eq. 3: the last full block */
+#define FFD_HEAD_DIM 128    /* the only supported head dimension */
+
+typedef enum {
+    FFD_OK = 0,
+    FFD_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, NaN/negative delta */
+    FFD_ERR_UNSUPPORTED = 2, /* valid but not implemented: head_dim != 128, block not 64/128,
+                                Hq/Hkv not in {1, 2, 4, 8} */
+    FFD_ERR_WORKSPACE = 3,   /* workspace missing or smaller than ffd_workspace_bytes() */
+    FFD_ERR_HIP = 4          /* the HIP runtime reported an error for a launch */
+} ffd_status;
+
+typedef enum { FFD_F32 = 0, FFD_BF16 = 1 } ffd_dtype;
+
+typedef struct {
+    int32_t batch;      /* B >= 0 (B = 0: every call is a no-op returning FFD_OK) */
+    int32_t n_q_heads;  /* Hq >= 1, a multiple of n_kv_heads */
+    int32_t n_kv_heads; /* Hkv >= 1 */
+    int32_t head_dim;   /* d, must be 128 */
+    int32_t seq_len;    /* L >= 1 valid tokens per sequence (the same for every sequence) */
+    int32_t seq_cap;    /* row stride of K, V and Kq in tokens: >= seq_len, multiple of block */
+    int32_t dtype;      /* ffd_dtype of q, K and V */
+} ffd_dims;
+
+/*
+ * Low-bit copy of the keys (App. A quantizer; the "K quantization" stage of Fig. 2).
+ * Quantizes every block j (0 <= j < seq_cap/block) whose last token index (j+1)*block-1 lies in
+ * [tok_begin, tok_end): those are the blocks that become complete when tokens tok_begin..tok_end-1
+ * are appended.  Writes rows j*block..(j+1)*block-1 of Kq and row j of scales; leaves every other
+ * byte untouched.  Requires 0 <= tok_begin <= tok_end <= seq_len.  Calling it once with (0, L)
+ * quantizes a whole cache; calling it once per appended token gives the same bytes.
+ */
+ffd_status ffd_quantize_k_append(const ffd_dims* dims, const void* K, int32_t tok_begin,
+                                 int32_t tok_end, int32_t block, uint8_t* Kq, float* scales,
+                                 hipStream_t stream);
+
+/*
+ * Sparse decode step: scan, pseudo-max, top-delta selection, exact attention over kept blocks
+ * and split-KV log-sum-exp combine (Alg. 1; Sec. 3.2-3.3).
+ *   delta      >= 0, or +inf (keeps every block); NaN is rejected.
+ *   block      T in {64, 128}; Kq and scales must hold the quantized full blocks of K.
+ *   out, lse   results; lse may be NULL.
+ *   keep_mask  optional (NULL) per-(b, query head, block) selection, written as 0/1.
+ *   workspace  caller-owned device memory of at least ffd_workspace_bytes(dims, block) bytes;
+ *              its contents on entry do not matter; it holds per-split partials during the call.
+ */
+ffd_status ffd_decode_sparse(const ffd_dims* dims, const void* q, const void* K, const void* V,
+                             const uint8_t* Kq, const float* scales, float delta, int32_t block,
+                             float* out, float* lse, uint8_t* keep_mask, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Dense decode step (the exact flash-decoding baseline of Sec. 4.2): softmax(q K^T / sqrt(d)) V
+ * over all seq_len tokens, split along the sequence and merged with the same combine.
+ * `block` only sets the work granularity (64 or 128); results do not depend on it beyond
+ * floating-point rounding.
+ */
+ffd_status ffd_decode_dense(const ffd_dims* dims, const void* q, const void* K, const void* V,
+                            int32_t block, float* out, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by ffd_decode_sparse / ffd_decode_dense for these dims and block
+ * (the maximum of the two); 0 for invalid dims. */
+size_t ffd_workspace_bytes(const ffd_dims* dims, int32_t block);
+
+/* Number of sequence splits (work-groups per (sequence, kv head)) the decode calls use. */
+int32_t ffd_num_splits(const ffd_dims* dims, int32_t block, int32_t sparse);
+
+/* Static description of a status code. */
+const char* ffd_status_string(ffd_status status);
+
+/* FFD_ABI_VERSION of the loaded library. */
+int32_t ffd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFD_H */

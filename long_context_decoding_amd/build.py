@@ -1,0 +1,59 @@
+"""Build libffd.so (gfx950) in-tree with hipcc.
+
+    python -m long_context_decoding_amd.build
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+LIB = PKG / "libffd.so"
+SOURCES = [CSRC / "ffd_kernels.hip", CSRC / "ffd_api.cpp"]
+HEADERS = [CSRC / "ffd_internal.h", ROOT / "include" / "ffd.h"]
+ARCH = os.environ.get("FFD_OFFLOAD_ARCH", "gfx950")
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-Wall",
+    # no packed fp32 math in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the selection arithmetic must not be contracted into FMAs (explicit __f*_rn ops are used
+    # there as well); attention math uses explicit fmaf where a fused op is wanted
+    "-ffp-contract=off",
+]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
+        if c and (Path(c).exists() or c == "hipcc"):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False) -> Path:
+    tmp = LIB.with_suffix(".so.tmp")
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", str(tmp), *map(str, SOURCES)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = [l for l in (res.stdout + res.stderr).splitlines() if noise not in l]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,191 @@
+// ffd_api.cpp -- C ABI of libffd (declared in include/ffd.h): argument validation, the split
+// heuristic, workspace layout and kernel launches.  Validation happens before any HIP call.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/ffd.h"
+#include "ffd_internal.h"
+
+namespace {
+
+using ffd::kHeadDim;
+using ffd::kMaxBlocksPerSplit;
+using ffd::kPartStride;
+using ffd::kWaves;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by every call.  `block` must be known (64/128) for the decode calls.
+ffd_status check_dims(const ffd_dims* d, int32_t block)
+{
+    if (!d) return FFD_ERR_INVALID_ARG;
+    if (d->batch < 0 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 1 ||
+        d->seq_len < 1 || d->seq_cap < d->seq_len || block < 1)
+        return FFD_ERR_INVALID_ARG;
+    if (d->n_q_heads % d->n_kv_heads) return FFD_ERR_INVALID_ARG;
+    if (d->dtype != FFD_F32 && d->dtype != FFD_BF16) return FFD_ERR_INVALID_ARG;
+    if (d->head_dim != kHeadDim) return FFD_ERR_UNSUPPORTED;
+    if (block != 64 && block != 128) return FFD_ERR_UNSUPPORTED;
+    if (d->seq_cap % block) return FFD_ERR_INVALID_ARG;
+    const int G = d->n_q_heads / d->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return FFD_ERR_UNSUPPORTED;
+    // grid limits: batch * kv heads rows of work-groups, block counts in 16-bit tables
+    if ((int64_t)d->batch * d->n_kv_heads > 65535) return FFD_ERR_UNSUPPORTED;
+    return FFD_OK;
+}
+
+int splits_for(const ffd_dims* d, int32_t block)
+{
+    const int n_blocks = (d->seq_len + block - 1) / block;
+    const int64_t bh = (int64_t)d->batch * d->n_kv_heads;
+    if (const char* env = getenv("FFD_NUM_SPLITS")) {
+        int s = atoi(env);
+        if (s >= 1) {
+            if (s > n_blocks) s = n_blocks;
+            const int min_s = (n_blocks + kMaxBlocksPerSplit - 1) / kMaxBlocksPerSplit;
+            return s < min_s ? min_s : s;
+        }
+    }
+    // enough work-groups to fill 256 CUs a few times over, at least two blocks per wave, and
+    // no more blocks per split than the kernel's tables hold
+    const int64_t target_wgs = 1024;
+    int64_t s = bh > 0 ? (target_wgs + bh - 1) / bh : 1;
+    const int64_t max_s = n_blocks / (2 * kWaves) > 0 ? n_blocks / (2 * kWaves) : 1;
+    if (s > max_s) s = max_s;
+    const int64_t min_s = (n_blocks + kMaxBlocksPerSplit - 1) / kMaxBlocksPerSplit;
+    if (s < min_s) s = min_s;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
+size_t part_bytes(const ffd_dims* d, int S)
+{
+    return (size_t)d->batch * d->n_q_heads * (size_t)S * kPartStride * sizeof(float);
+}
+
+ffd_status finish(hipError_t e) { return e == hipSuccess ? FFD_OK : FFD_ERR_HIP; }
+
+ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, const void* V,
+                         const uint8_t* Kq, const float* scales, float delta, int32_t block,
+                         float* out, float* lse, uint8_t* keep_mask, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream, bool sparse)
+{
+    ffd_status st = check_dims(dims, block);
+    if (st != FFD_OK) return st;
+    if (dims->batch == 0) return FFD_OK;
+    if (!q || !K || !V || !out) return FFD_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(out) ||
+        (lse && !aligned16(lse)) || (keep_mask && !aligned16(keep_mask)))
+        return FFD_ERR_INVALID_ARG;
+    if (sparse) {
+        if (!Kq || !scales || !aligned16(Kq) || !aligned16(scales)) return FFD_ERR_INVALID_ARG;
+        if (isnan(delta) || delta < 0.0f) return FFD_ERR_INVALID_ARG;
+    }
+    const int S = splits_for(dims, block);
+    if (!workspace || !aligned16(workspace)) return FFD_ERR_WORKSPACE;
+    if (workspace_bytes < part_bytes(dims, S)) return FFD_ERR_WORKSPACE;
+
+    ffd::DecodeParams p{};
+    p.q = q;
+    p.K = K;
+    p.V = V;
+    p.Kq = Kq;
+    p.scales = scales;
+    p.out = out;
+    p.lse = lse;
+    p.keep_mask = keep_mask;
+    p.part = static_cast<float*>(workspace);
+    p.B = dims->batch;
+    p.Hq = dims->n_q_heads;
+    p.Hkv = dims->n_kv_heads;
+    p.G = dims->n_q_heads / dims->n_kv_heads;
+    p.L = dims->seq_len;
+    p.cap = dims->seq_cap;
+    p.T = block;
+    p.n_full = dims->seq_len / block;
+    p.n_blocks = (dims->seq_len + block - 1) / block;
+    p.S = S;
+    p.R = (p.n_blocks + S - 1) / S;
+    p.delta = delta;
+    p.kappa = (float)(0.5 / (127.0 * sqrt((double)kHeadDim)));
+    p.c_log2 = (float)(1.4426950408889634 / sqrt((double)kHeadDim));
+    return finish(ffd::launch_decode(p, dims->dtype == FFD_BF16, sparse, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ffd_abi_version(void) { return FFD_ABI_VERSION; }
+
+const char* ffd_status_string(ffd_status s)
+{
+    switch (s) {
+    case FFD_OK: return "ok";
+    case FFD_ERR_INVALID_ARG: return "invalid argument";
+    case FFD_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FFD_ERR_WORKSPACE: return "workspace missing or too small";
+    case FFD_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t ffd_workspace_bytes(const ffd_dims* dims, int32_t block)
+{
+    if (check_dims(dims, block) != FFD_OK) return 0;
+    return part_bytes(dims, splits_for(dims, block));
+}
+
+int32_t ffd_num_splits(const ffd_dims* dims, int32_t block, int32_t sparse)
+{
+    (void)sparse;
+    if (check_dims(dims, block) != FFD_OK) return 0;
+    return splits_for(dims, block);
+}
+
+ffd_status ffd_quantize_k_append(const ffd_dims* dims, const void* K, int32_t tok_begin,
+                                 int32_t tok_end, int32_t block, uint8_t* Kq, float* scales,
+                                 hipStream_t stream)
+{
+    ffd_status st = check_dims(dims, block);
+    if (st != FFD_OK) return st;
+    if (tok_begin < 0 || tok_end < tok_begin || tok_end > dims->seq_len) return FFD_ERR_INVALID_ARG;
+    if (dims->batch == 0) return FFD_OK;
+    if (!K || !Kq || !scales || !aligned16(K) || !aligned16(Kq) || !aligned16(scales))
+        return FFD_ERR_INVALID_ARG;
+    // blocks j with tok_begin <= (j+1)*block - 1 < tok_end
+    const int j_first = (tok_begin + 1 + block - 1) / block - 1;
+    const int j_last = tok_end / block - 1;
+    if (j_last < j_first) return FFD_OK;
+    ffd::QuantParams p{};
+    p.K = K;
+    p.Kq = Kq;
+    p.scales = scales;
+    p.B = dims->batch;
+    p.Hkv = dims->n_kv_heads;
+    p.cap = dims->seq_cap;
+    p.T = block;
+    p.j_first = j_first;
+    p.n_blocks = j_last - j_first + 1;
+    return finish(ffd::launch_quantize(p, dims->dtype == FFD_BF16, stream));
+}
+
+ffd_status ffd_decode_sparse(const ffd_dims* dims, const void* q, const void* K, const void* V,
+                             const uint8_t* Kq, const float* scales, float delta, int32_t block,
+                             float* out, float* lse, uint8_t* keep_mask, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream)
+{
+    return decode_common(dims, q, K, V, Kq, scales, delta, block, out, lse, keep_mask, workspace,
+                         workspace_bytes, stream, true);
+}
+
+ffd_status ffd_decode_dense(const ffd_dims* dims, const void* q, const void* K, const void* V,
+                            int32_t block, float* out, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream)
+{
+    return decode_common(dims, q, K, V, nullptr, nullptr, 0.0f, block, out, lse, nullptr,
+                         workspace, workspace_bytes, stream, false);
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// ffd_internal.h -- launch parameters shared by the C-ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace ffd {
+
+constexpr int kHeadDim = 128;
+constexpr int kPartStride = kHeadDim + 4;  // per-split record: o[128], m (log2 units), l, pad
+constexpr int kWaves = 4;                  // waves per work-group of the decode kernels
+constexpr int kMaxBlocksPerSplit = 256;    // LDS sizing of the per-split block tables
+
+struct DecodeParams {
+    const void* q;
+    const void* K;
+    const void* V;
+    const uint8_t* Kq;
+    const float* scales;
+    float* out;
+    float* lse;
+    uint8_t* keep_mask;
+    float* part;    // [B*Hq][S][kPartStride]
+    int B, Hq, Hkv, G;
+    int L, cap, T;
+    int n_full, n_blocks;
+    int S, R;       // splits per (b, kv head), blocks per split
+    float delta;    // top-delta threshold (logit units)
+    float kappa;    // (float)(0.5 / (127 sqrt(d)))
+    float c_log2;   // (float)(log2(e) / sqrt(d))
+};
+
+struct QuantParams {
+    const void* K;
+    uint8_t* Kq;
+    float* scales;
+    int B, Hkv, cap, T;
+    int j_first, n_blocks;  // blocks j_first .. j_first + n_blocks - 1
+};
+
+// Launchers (ffd_kernels.hip).  Return the hipError_t of the launch.
+hipError_t launch_decode(const DecodeParams& p, bool bf16, bool sparse, hipStream_t stream);
+hipError_t launch_quantize(const QuantParams& p, bool bf16, hipStream_t stream);
+
+}  // namespace ffd

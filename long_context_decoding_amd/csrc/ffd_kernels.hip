@@ -1,0 +1,741 @@
+// ffd_kernels.hip -- gfx950 (CDNA4) kernels of libffd.
+//
+// Method: "Faster Than Flash: Exploiting Attention Sparsity for Efficient Long-Context Decoding"
+// (arXiv 2609.00097), written FTF below.
+//
+//   quantize_kernel  App. A quantizer (16 levels) of each completed key block -> packed int4 codes
+//                    and one fp32 scale per (block, channel).
+//   decode_kernel    one work-group per (sequence, kv head, split of the sequence):
+//                      scan     int4 codes x int8-requantized (q . s) on the int8 MFMA (Alg. 1 scan)
+//                      select   pseudo-max over the sink and local blocks (Eq. 3), keep a block
+//                               iff its estimated max >= pseudo-max - delta (Eq. 1)
+//                      exact    bf16/fp32 MFMA for the G x 16 score tile, online softmax with
+//                               fp32 probabilities, PV on the VALU in fp32 (Alg. 1 refinement)
+//                    then writes one partial (o, m, l) per query head (split-KV, FTF Sec. 2).
+//                    The dense baseline is the same kernel with every block kept and no scan.
+//   combine_kernel   log-sum-exp merge of the splits -> out, lse.
+//
+// Wave layout conventions (wave64):
+//   lane = 16 * kg + col, kg = lane >> 4 in 0..3, col = lane & 15.
+//   16x16 MFMA outputs: lane holds rows 4*kg + v (v = 0..3) of column col.
+//   The A and B operands of a 16x16 MFMA hold row/column `col` and the k-slice selected by kg;
+//   any assignment of channels to k works as long as A and B use the same one.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ffd_internal.h"
+
+namespace ffd {
+namespace {
+
+constexpr int D = kHeadDim;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned int u32;
+
+__device__ __forceinline__ float as_f(int x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ int as_i(float x) { return __builtin_bit_cast(int, x); }
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x)
+{
+    return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false);
+}
+
+// Reductions over the 16 lanes of a row (all lanes receive the result):
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+__device__ __forceinline__ float row16_max(float x)
+{
+    x = fmaxf(x, as_f(dpp<0xB1>(as_i(x))));
+    x = fmaxf(x, as_f(dpp<0x4E>(as_i(x))));
+    x = fmaxf(x, as_f(dpp<0x141>(as_i(x))));
+    x = fmaxf(x, as_f(dpp<0x140>(as_i(x))));
+    return x;
+}
+
+__device__ __forceinline__ int row16_sum(int x)
+{
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    x += dpp<0x140>(x);
+    return x;
+}
+
+// Orders this wave's LDS accesses (LDS executes one wave's instructions in order; this only
+// stops the compiler from moving accesses across the point).
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float bf16_lo(u32 x) { return as_f((int)(x << 16)); }
+__device__ __forceinline__ float bf16_hi(u32 x) { return as_f((int)(x & 0xFFFF0000u)); }
+
+// ------------------------------------------------------------------------------------------
+// Per-wave LDS scratch
+// ------------------------------------------------------------------------------------------
+template <int G>
+struct __attribute__((aligned(16))) WaveScratch {
+    int8_t wB[2][G][4][16];  // scan MFMA B operand: [k-step][head][kg][16 int8]
+    v4f P[4][16];            // probabilities exchanged from the score layout: [kg][col]
+    float f[G];              // per-head scan factor RN(W * kappa)
+    int wsum[G];             // per-head sum of the requantized weights
+    float alpha[16];         // per-head rescale factor of the current tile
+};
+
+// ------------------------------------------------------------------------------------------
+// Scan of one full block (FTF Alg. 1, scan stage; App. B Eq. 8 for what it approximates).
+// ------------------------------------------------------------------------------------------
+template <int T>
+struct ScanRegs {
+    uint4 kq[T / 16];  // 16 packed bytes of token row (16*i + col), bytes kg*16 .. kg*16+15
+    float4 s0, s1;     // scales of channels 8*col .. 8*col+7
+};
+
+template <int T>
+__device__ __forceinline__ void scan_load(ScanRegs<T>& r, const uint8_t* __restrict__ kq_blk,
+                                          const float* __restrict__ sc_blk, int lane)
+{
+    const int col = lane & 15, kg = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < T / 16; ++i)
+        r.kq[i] = *reinterpret_cast<const uint4*>(kq_blk + (size_t)(i * 16 + col) * (D / 2) +
+                                                  kg * 16);
+    const float4* sp = reinterpret_cast<const float4*>(sc_blk + col * 8);
+    r.s0 = sp[0];
+    r.s1 = sp[1];
+}
+
+// Estimated block maximum of every query head of the group.  Requantization lanes: row kg
+// handles head kg (+4 for G = 8), 8 channels 8*col..8*col+7.  Result valid in lanes with
+// col < G (head col), identical across kg.
+//
+// The A operand unpacks each packed dword d (channels c..c+7, two per byte) into
+// lo = d & 0x0F0F0F0F (channels c, c+2, c+4, c+6) and hi = (d >> 4) & 0x0F0F0F0F (c+1, c+3,
+// c+5, c+7); the B operand stores the requantized weights in that same channel order.
+// Codes enter as u in 0..15 (positive int8), so D_t = sum_c wi_c u_tc and
+// E_t = sum_c wi_c (2 u_tc - 15) = 2 D_t - 15 sum_c wi_c, all exact in int32.
+template <int T, int G>
+__device__ __forceinline__ float scan_compute(const ScanRegs<T>& r, const float (&qw)[(G + 3) / 4][8],
+                                              float kappa, WaveScratch<G>& ws, int lane)
+{
+    constexpr int HPL = (G + 3) / 4;
+    const int col = lane & 15, kg = lane >> 4;
+    const float s[8] = {r.s0.x, r.s0.y, r.s0.z, r.s0.w, r.s1.x, r.s1.y, r.s1.z, r.s1.w};
+#pragma unroll
+    for (int k = 0; k < HPL; ++k) {
+        const int h = kg + 4 * k;
+        float w[8];
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            w[i] = __fmul_rn(qw[k][i], s[i]);
+            amax = fmaxf(amax, fabsf(w[i]));
+        }
+        const float W = row16_max(amax);
+        int wi[8];
+        if (W > 0.0f) {
+            const float rho = __fdiv_rn(127.0f, W);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float v = rintf(__fmul_rn(w[i], rho));
+                v = fminf(fmaxf(v, -127.0f), 127.0f);
+                wi[i] = (int)v;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) wi[i] = 0;
+        }
+        const int wsum =
+            row16_sum(wi[0] + wi[1] + wi[2] + wi[3] + wi[4] + wi[5] + wi[6] + wi[7]);
+        const u32 d0 = (u32)(wi[0] & 255) | ((u32)(wi[2] & 255) << 8) |
+                       ((u32)(wi[4] & 255) << 16) | ((u32)(wi[6] & 255) << 24);
+        const u32 d1 = (u32)(wi[1] & 255) | ((u32)(wi[3] & 255) << 8) |
+                       ((u32)(wi[5] & 255) << 16) | ((u32)(wi[7] & 255) << 24);
+        if (G >= 4 || h < G) {
+            // channel c = 8*col: kg' = c / 32, k-step = (c % 32) / 16, byte offset (c % 16)
+            const int kgw = col >> 2, ks = (col & 3) >> 1;
+            *reinterpret_cast<uint2*>(&ws.wB[ks][h][kgw][(col & 1) * 8]) = make_uint2(d0, d1);
+            if (col == 0) {
+                ws.f[h] = __fmul_rn(W, kappa);
+                ws.wsum[h] = wsum;
+            }
+        }
+    }
+    wave_sync();
+    const int hB = col % G;
+    const v4i B0 = *reinterpret_cast<const v4i*>(&ws.wB[0][hB][kg][0]);
+    const v4i B1 = *reinterpret_cast<const v4i*>(&ws.wB[1][hB][kg][0]);
+    constexpr u32 M = 0x0F0F0F0Fu;
+    int dmax = -2147483647 - 1;
+#pragma unroll
+    for (int i = 0; i < T / 16; ++i) {
+        const uint4 p = r.kq[i];
+        const v4i A0 = {(int)(p.x & M), (int)((p.x >> 4) & M), (int)(p.y & M),
+                        (int)((p.y >> 4) & M)};
+        const v4i A1 = {(int)(p.z & M), (int)((p.z >> 4) & M), (int)(p.w & M),
+                        (int)((p.w >> 4) & M)};
+        v4i acc = {0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, B0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, B1, acc, 0, 0, 0);
+        dmax = max(dmax, max(max(acc[0], acc[1]), max(acc[2], acc[3])));
+    }
+    dmax = max(dmax, __shfl_xor(dmax, 16));
+    dmax = max(dmax, __shfl_xor(dmax, 32));
+    const int E = 2 * dmax - 15 * ws.wsum[hB];
+    const float shat = __fmul_rn((float)E, ws.f[hB]);
+    wave_sync();
+    return shat;
+}
+
+// ------------------------------------------------------------------------------------------
+// Exact attention on one 16-token tile (FTF Alg. 1, refinement stage).
+// ------------------------------------------------------------------------------------------
+template <bool BF16>
+struct TileRegs;
+template <>
+struct TileRegs<true> {
+    uint4 k[4];  // k-step ks: 8 bf16 of token row col, channels 32*ks + 8*kg ..
+    uint4 v[4];  // token 4*kg + i, 8 bf16 channels 8*col ..
+};
+template <>
+struct TileRegs<false> {
+    float4 k[8];  // token row col, channels 32*kg + 4*i ..
+    float4 v[8];  // token 4*kg + i/2, channels 8*col + 4*(i%2) ..
+};
+
+template <bool BF16>
+__device__ __forceinline__ void tile_load(TileRegs<BF16>& r, const void* __restrict__ Kbg,
+                                          const void* __restrict__ Vbg, int t0, int lane)
+{
+    const int col = lane & 15, kg = lane >> 4;
+    if constexpr (BF16) {
+        const __bf16* Kp = static_cast<const __bf16*>(Kbg);
+        const __bf16* Vp = static_cast<const __bf16*>(Vbg);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            r.k[ks] = *reinterpret_cast<const uint4*>(Kp + (size_t)(t0 + col) * D + ks * 32 + kg * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r.v[i] = *reinterpret_cast<const uint4*>(Vp + (size_t)(t0 + 4 * kg + i) * D + col * 8);
+    } else {
+        const float* Kp = static_cast<const float*>(Kbg);
+        const float* Vp = static_cast<const float*>(Vbg);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            r.k[i] = *reinterpret_cast<const float4*>(Kp + (size_t)(t0 + col) * D + kg * 32 + i * 4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            r.v[i] = *reinterpret_cast<const float4*>(Vp + (size_t)(t0 + 4 * kg + i / 2) * D +
+                                                      col * 8 + (i & 1) * 4);
+    }
+}
+
+template <bool BF16>
+struct QueryRegs;
+template <>
+struct QueryRegs<true> {
+    v8bf b[4];  // head col % G, channels 32*ks + 8*kg ..
+};
+template <>
+struct QueryRegs<false> {
+    float b[32];  // head col % G, channels 32*kg + i
+};
+
+template <int G>
+struct SoftState {
+    float o[G][8];  // unnormalized output, channels 8*col.., summed over this lane's tokens
+    float m;        // running max (log2 units) of head col % G
+    float l;        // running sum of exp2(s - m) of head col % G
+};
+
+template <int G, bool BF16>
+__device__ __forceinline__ void tile_compute(const TileRegs<BF16>& r, const QueryRegs<BF16>& qr,
+                                             SoftState<G>& st, WaveScratch<G>& ws, int t0, int L,
+                                             u32 kbits, float c_log2, int lane)
+{
+    const int col = lane & 15, kg = lane >> 4;
+    // scores S[token t0 + 4 kg + v][head col % G]
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (BF16) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, r.k[ks]),
+                                                          qr.b[ks], acc, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r.k[i].x, qr.b[4 * i + 0], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r.k[i].y, qr.b[4 * i + 1], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r.k[i].z, qr.b[4 * i + 2], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r.k[i].w, qr.b[4 * i + 3], acc, 0, 0, 0);
+        }
+    }
+    const bool head_keep = (kbits >> (col % G)) & 1u;
+    float s2[4];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const bool valid = head_keep && (t0 + 4 * kg + v) < L;
+        s2[v] = valid ? acc[v] * c_log2 : kNegInf;
+        tmax = fmaxf(tmax, s2[v]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(st.m, tmax);
+    const float alpha = (m_new == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(st.m - m_new);
+    v4f p;
+    float psum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        p[v] = (s2[v] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(s2[v] - m_new);
+        psum += p[v];
+    }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+
+    // move probabilities to the PV layout: lane needs p[h][4 kg + v] for every head h
+    ws.P[kg][col] = p;
+    if (kg == 0) ws.alpha[col] = alpha;
+    wave_sync();
+    v4f pp[G];
+    float al[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        pp[h] = ws.P[kg][h];
+        al[h] = ws.alpha[h];
+    }
+    wave_sync();
+
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) st.o[h][c] *= al[h];
+
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        float vv[8];
+        if constexpr (BF16) {
+            const uint4 x = r.v[v];
+            vv[0] = bf16_lo(x.x); vv[1] = bf16_hi(x.x);
+            vv[2] = bf16_lo(x.y); vv[3] = bf16_hi(x.y);
+            vv[4] = bf16_lo(x.z); vv[5] = bf16_hi(x.z);
+            vv[6] = bf16_lo(x.w); vv[7] = bf16_hi(x.w);
+        } else {
+            const float4 a = r.v[2 * v], b = r.v[2 * v + 1];
+            vv[0] = a.x; vv[1] = a.y; vv[2] = a.z; vv[3] = a.w;
+            vv[4] = b.x; vv[5] = b.y; vv[6] = b.z; vv[7] = b.w;
+        }
+        if (t0 + 4 * kg + v >= L) {  // rows past the sequence may hold anything (even NaN)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) vv[c] = 0.0f;
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) st.o[h][c] = fmaf(pp[h][v], vv[c], st.o[h][c]);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode kernel (sparse and dense)
+// ------------------------------------------------------------------------------------------
+template <int G>
+struct __attribute__((aligned(16))) DecodeShared {
+    WaveScratch<G> wave[kWaves];
+    union {
+        float shat[G][kMaxBlocksPerSplit];                 // scan results of the split's blocks
+        struct {
+            float o[kWaves][G][D];
+            float m[kWaves][G];
+            float l[kWaves][G];
+        } merge;
+    } u;
+    float pro[2][G];                       // estimates of the sink and local blocks
+    uint8_t kbits[kMaxBlocksPerSplit];     // per-block head mask (bit h = query head h of group)
+    uint16_t list[kMaxBlocksPerSplit];     // kept blocks (offsets in the split)
+    int n_kept;
+};
+
+template <int T, int G, bool BF16, bool SPARSE>
+__global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p)
+{
+    __shared__ DecodeShared<G> sh;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int col = lane & 15, kg = lane >> 4;
+
+    // work-group -> (b, kv head, split); sparse: the splits holding the sink (0) and the local
+    // block (S-1) are dispatched first, they always carry exact work.
+    const int bh = p.B * p.Hkv;
+    const int id = blockIdx.x;
+    const int bg = id % bh;
+    const int rank = id / bh;
+    int split = rank;
+    if (SPARSE && p.S > 1) split = rank == 0 ? 0 : (rank == 1 ? p.S - 1 : rank - 1);
+    const int b = bg / p.Hkv, g = bg % p.Hkv;
+    const int jb = split * p.R;
+    const int je = min(p.n_blocks, jb + p.R);
+
+    const size_t esz = BF16 ? 2 : 4;
+    const size_t kv_off = (size_t)bg * p.cap * D;
+    const char* Kbg = static_cast<const char*>(p.K) + kv_off * esz;
+    const char* Vbg = static_cast<const char*>(p.V) + kv_off * esz;
+    const int h0 = b * p.Hq + g * G;  // first query row of the group
+
+    // query registers for the exact stage (head col % G)
+    QueryRegs<BF16> qr;
+    {
+        const int hq = h0 + col % G;
+        if constexpr (BF16) {
+            const __bf16* qp = static_cast<const __bf16*>(p.q) + (size_t)hq * D;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                qr.b[ks] = __builtin_bit_cast(
+                    v8bf, *reinterpret_cast<const uint4*>(qp + ks * 32 + kg * 8));
+        } else {
+            const float* qp = static_cast<const float*>(p.q) + (size_t)hq * D;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float4 x = *reinterpret_cast<const float4*>(qp + kg * 32 + 4 * i);
+                qr.b[4 * i] = x.x;
+                qr.b[4 * i + 1] = x.y;
+                qr.b[4 * i + 2] = x.z;
+                qr.b[4 * i + 3] = x.w;
+            }
+        }
+    }
+
+    WaveScratch<G>& ws = sh.wave[w];
+    const int NT = p.T / 16;
+    int n_kept;
+
+    if constexpr (SPARSE) {
+        constexpr int HPL = (G + 3) / 4;
+        float qw[HPL][8];
+#pragma unroll
+        for (int k = 0; k < HPL; ++k) {
+            const int h = (G >= 4) ? (kg + 4 * k) : (kg % G);
+            const int hq = h0 + h;
+            if constexpr (BF16) {
+                const uint4 x = *reinterpret_cast<const uint4*>(
+                    static_cast<const __bf16*>(p.q) + (size_t)hq * D + col * 8);
+                qw[k][0] = bf16_lo(x.x); qw[k][1] = bf16_hi(x.x);
+                qw[k][2] = bf16_lo(x.y); qw[k][3] = bf16_hi(x.y);
+                qw[k][4] = bf16_lo(x.z); qw[k][5] = bf16_hi(x.z);
+                qw[k][6] = bf16_lo(x.w); qw[k][7] = bf16_hi(x.w);
+            } else {
+                const float* qp = static_cast<const float*>(p.q) + (size_t)hq * D + col * 8;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) qw[k][i] = qp[i];
+            }
+        }
+
+        const uint8_t* kq_bg = p.Kq + (size_t)bg * p.cap * (D / 2);
+        const float* sc_bg = p.scales + (size_t)bg * (p.cap / p.T) * D;
+        const int nf = p.n_full;
+        // scan items of this wave: [prologue block], then blocks j_lo + w + NW*i of the split
+        // that are neither forced nor beyond the full blocks
+        const bool has_pro = (w < 2) && nf >= 1;
+        const int j_pro = (w == 0) ? 0 : nf - 1;
+        const int j_lo = max(jb, 1);
+        const int j_hi = min(je, nf - 1);
+        const int n_range = (j_hi - j_lo - w > 0) ? (j_hi - j_lo - w + kWaves - 1) / kWaves : 0;
+        const int n_items = (has_pro ? 1 : 0) + n_range;
+        auto item_block = [&](int i) -> int {
+            if (has_pro) {
+                if (i == 0) return j_pro;
+                --i;
+            }
+            return j_lo + w + i * kWaves;
+        };
+        auto store = [&](int i, float shat) {
+            if (lane < G) {
+                if (has_pro && i == 0) sh.pro[w][lane] = shat;
+                else sh.u.shat[lane][item_block(i) - jb] = shat;
+            }
+        };
+        ScanRegs<T> ra, rb;
+        if (n_items > 0) {
+            const int j = item_block(0);
+            scan_load<T>(ra, kq_bg + (size_t)j * T * (D / 2), sc_bg + (size_t)j * D, lane);
+        }
+        for (int i = 0; i < n_items; i += 2) {
+            if (i + 1 < n_items) {
+                const int j = item_block(i + 1);
+                scan_load<T>(rb, kq_bg + (size_t)j * T * (D / 2), sc_bg + (size_t)j * D, lane);
+            }
+            store(i, scan_compute<T, G>(ra, qw, p.kappa, ws, lane));
+            if (i + 1 < n_items) {
+                if (i + 2 < n_items) {
+                    const int j = item_block(i + 2);
+                    scan_load<T>(ra, kq_bg + (size_t)j * T * (D / 2), sc_bg + (size_t)j * D, lane);
+                }
+                store(i + 1, scan_compute<T, G>(rb, qw, p.kappa, ws, lane));
+            }
+        }
+        __syncthreads();
+
+        // selection (Eq. 1 with the Eq. 3 pseudo-max) and compaction of the kept blocks
+        if (w == 0) {
+            float theta[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float mt = nf >= 1 ? fmaxf(sh.pro[0][h], sh.pro[1][h]) : 0.0f;
+                theta[h] = __fsub_rn(mt, p.delta);
+            }
+            int n = 0;
+            for (int base = 0; base < je - jb; base += 64) {
+                const int t = base + lane;
+                const int j = jb + t;
+                u32 bits = 0;
+                if (j < je) {
+                    const bool forced = (j == 0) || (j >= nf - 1);
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        const bool keep = forced || (sh.u.shat[h][t] >= theta[h]);
+                        bits |= (u32)keep << h;
+                        if (p.keep_mask)
+                            p.keep_mask[(size_t)(h0 + h) * p.n_blocks + j] = keep ? 1 : 0;
+                    }
+                    sh.kbits[t] = (uint8_t)bits;
+                }
+                const unsigned long long ball = __ballot(bits != 0);
+                const int pos = __popcll(ball & ((1ull << lane) - 1ull));
+                if (bits != 0) sh.list[n + pos] = (uint16_t)t;
+                n += __popcll(ball);
+            }
+            if (lane == 0) sh.n_kept = n;
+        }
+        __syncthreads();
+        n_kept = sh.n_kept;
+    } else {
+        n_kept = je - jb;
+    }
+
+    // exact attention over the kept blocks, 16-token tiles dealt round-robin to the waves
+    SoftState<G> st;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) st.o[h][c] = 0.0f;
+    st.m = kNegInf;
+    st.l = 0.0f;
+    {
+        const int n_tiles = n_kept * NT;
+        auto tile_of = [&](int it, int& t0, u32& kb) {
+            const int k = it / NT;
+            int off;
+            if constexpr (SPARSE) {
+                off = sh.list[k];
+                kb = sh.kbits[off];
+            } else {
+                off = k;
+                kb = 0xFFu;
+            }
+            t0 = (jb + off) * p.T + (it % NT) * 16;
+        };
+        TileRegs<BF16> ta, tb;
+        int t0a = 0, t0b = 0;
+        u32 kba = 0, kbb = 0;
+        int it = w;
+        if (it < n_tiles) {
+            tile_of(it, t0a, kba);
+            tile_load<BF16>(ta, Kbg, Vbg, t0a, lane);
+        }
+        for (; it < n_tiles; it += 2 * kWaves) {
+            const int it1 = it + kWaves;
+            if (it1 < n_tiles) {
+                tile_of(it1, t0b, kbb);
+                tile_load<BF16>(tb, Kbg, Vbg, t0b, lane);
+            }
+            tile_compute<G, BF16>(ta, qr, st, ws, t0a, p.L, kba, p.c_log2, lane);
+            if (it1 < n_tiles) {
+                const int it2 = it1 + kWaves;
+                if (it2 < n_tiles) {
+                    tile_of(it2, t0a, kba);
+                    tile_load<BF16>(ta, Kbg, Vbg, t0a, lane);
+                }
+                tile_compute<G, BF16>(tb, qr, st, ws, t0b, p.L, kbb, p.c_log2, lane);
+            }
+        }
+    }
+
+    // sum the four token subsets (kg) of every lane's channels
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float x = st.o[h][c];
+            x += __shfl_xor(x, 16);
+            x += __shfl_xor(x, 32);
+            st.o[h][c] = x;
+        }
+
+    // merge the waves' softmax states, write this split's partial
+    __syncthreads();  // the shat table is reused as the merge buffer
+    if (kg == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float4* dst = reinterpret_cast<float4*>(&sh.u.merge.o[w][h][col * 8]);
+            dst[0] = make_float4(st.o[h][0], st.o[h][1], st.o[h][2], st.o[h][3]);
+            dst[1] = make_float4(st.o[h][4], st.o[h][5], st.o[h][6], st.o[h][7]);
+        }
+        if (col < G) {
+            sh.u.merge.m[w][col] = st.m;
+            sh.u.merge.l[w][col] = st.l;
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < G * D; e += kWaves * 64) {
+        const int h = e / D, c = e % D;
+        float M = kNegInf;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sh.u.merge.m[v][h]);
+        float o = 0.0f, l = 0.0f;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            const float mv = sh.u.merge.m[v][h];
+            const float sc = (mv == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
+            o = fmaf(sh.u.merge.o[v][h][c], sc, o);
+            l = fmaf(sh.u.merge.l[v][h], sc, l);
+        }
+        float* rec = p.part + ((size_t)(h0 + h) * p.S + split) * kPartStride;
+        rec[c] = o;
+        if (c == 0) {
+            rec[D] = M;
+            rec[D + 1] = l;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Split-KV combine: one work-group of 128 threads (one per channel) per (b, query head).
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ part,
+                                                      float* __restrict__ out,
+                                                      float* __restrict__ lse, int S)
+{
+    const int row = blockIdx.x;
+    const int c = threadIdx.x;
+    const float* rec = part + (size_t)row * S * kPartStride;
+    float M = kNegInf;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, rec[(size_t)s * kPartStride + D]);
+    float o = 0.0f, l = 0.0f;
+    for (int s = 0; s < S; ++s) {
+        const float* r = rec + (size_t)s * kPartStride;
+        const float ms = r[D];
+        const float sc = (ms == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+        o = fmaf(r[c], sc, o);
+        l = fmaf(r[D + 1], sc, l);
+    }
+    out[(size_t)row * D + c] = o / l;
+    if (lse && c == 0) lse[row] = (M + __log2f(l)) * 0.69314718055994530942f;
+}
+
+// ------------------------------------------------------------------------------------------
+// App. A quantizer, 16 levels: one work-group of 128 threads (one per channel) per block.
+// ------------------------------------------------------------------------------------------
+template <int T, bool BF16>
+__global__ __launch_bounds__(128) void quantize_kernel(QuantParams p)
+{
+    const int j = p.j_first + blockIdx.x;
+    const int bg = blockIdx.y;
+    const int c = threadIdx.x;
+    const size_t row0 = (size_t)bg * p.cap + (size_t)j * T;
+    float x[T];
+    float amax = 0.0f;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        if constexpr (BF16) {
+            const unsigned short bits =
+                static_cast<const unsigned short*>(p.K)[(row0 + t) * D + c];
+            x[t] = as_f((int)((u32)bits << 16));
+        } else {
+            x[t] = static_cast<const float*>(p.K)[(row0 + t) * D + c];
+        }
+        amax = fmaxf(amax, fabsf(x[t]));
+    }
+    float s = 0.0f, inv = 0.0f;
+    if (amax > 0.0f) {
+        s = __fdiv_rn(amax, 7.5f);
+        inv = __fdiv_rn(7.5f, amax);
+    }
+    p.scales[((size_t)bg * (p.cap / T) + j) * D + c] = s;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        int u = 8;
+        if (amax > 0.0f) {
+            u = (int)floorf(__fmul_rn(x[t], inv)) + 8;
+            u = min(max(u, 0), 15);
+        }
+        const int partner = __shfl_xor(u, 1);
+        if ((c & 1) == 0) p.Kq[(row0 + t) * (D / 2) + c / 2] = (uint8_t)(u | (partner << 4));
+    }
+}
+
+template <int T, int G, bool BF16>
+hipError_t launch_decode_t(const DecodeParams& p, bool sparse, hipStream_t stream)
+{
+    const dim3 grid(p.B * p.Hkv * p.S), block(kWaves * 64);
+    if (sparse)
+        hipLaunchKernelGGL((decode_kernel<T, G, BF16, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_kernel<T, G, BF16, false>), grid, block, 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(combine_kernel, dim3(p.B * p.Hq), dim3(D), 0, stream, p.part, p.out, p.lse,
+                       p.S);
+    return hipGetLastError();
+}
+
+template <int T, bool BF16>
+hipError_t launch_decode_g(const DecodeParams& p, bool sparse, hipStream_t stream)
+{
+    switch (p.G) {
+    case 1: return launch_decode_t<T, 1, BF16>(p, sparse, stream);
+    case 2: return launch_decode_t<T, 2, BF16>(p, sparse, stream);
+    case 4: return launch_decode_t<T, 4, BF16>(p, sparse, stream);
+    case 8: return launch_decode_t<T, 8, BF16>(p, sparse, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, bool bf16, bool sparse, hipStream_t stream)
+{
+    if (p.T == 64)
+        return bf16 ? launch_decode_g<64, true>(p, sparse, stream)
+                    : launch_decode_g<64, false>(p, sparse, stream);
+    if (p.T == 128)
+        return bf16 ? launch_decode_g<128, true>(p, sparse, stream)
+                    : launch_decode_g<128, false>(p, sparse, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_quantize(const QuantParams& p, bool bf16, hipStream_t stream)
+{
+    if (p.n_blocks <= 0) return hipSuccess;
+    const dim3 grid(p.n_blocks, p.B * p.Hkv), block(D);
+    if (p.T == 64) {
+        if (bf16) hipLaunchKernelGGL((quantize_kernel<64, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((quantize_kernel<64, false>), grid, block, 0, stream, p);
+    } else if (p.T == 128) {
+        if (bf16) hipLaunchKernelGGL((quantize_kernel<128, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((quantize_kernel<128, false>), grid, block, 0, stream, p);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ffd

@@ -1,0 +1,218 @@
+"""Python binding of libffd (include/ffd.h): argument marshalling only.
+
+Every step of the decode path runs in the HIP kernels of ``libffd.so``; this module checks torch
+tensor shapes, dtypes, devices and contiguity, passes ``data_ptr()`` and the current HIP stream
+through ctypes, and raises on a non-OK status.  There is no fallback: if the library is not built
+or cannot be loaded, every call raises.
+
+Names follow the C ABI: ``quantize_k_append``, ``decode_sparse``, ``decode_dense``,
+``workspace_bytes``, ``num_splits``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from pathlib import Path
+
+import torch
+
+LIB_PATH = Path(__file__).resolve().parent / "libffd.so"
+
+FFD_OK, FFD_ERR_INVALID_ARG, FFD_ERR_UNSUPPORTED, FFD_ERR_WORKSPACE, FFD_ERR_HIP = range(5)
+FFD_F32, FFD_BF16 = 0, 1
+HEAD_DIM = 128
+
+
+class FFDError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libffd: {msg} (status {status})")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "n_q_heads", "n_kv_heads", "head_dim", "seq_len", "seq_cap", "dtype")]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libffd (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise FileNotFoundError(
+                f"{LIB_PATH} is not built; run `python -m long_context_decoding_amd.build`")
+        L = ctypes.CDLL(str(LIB_PATH))
+        P, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+        D = ctypes.POINTER(Dims)
+        L.ffd_abi_version.restype = i32
+        L.ffd_status_string.argtypes = [i32]
+        L.ffd_status_string.restype = ctypes.c_char_p
+        L.ffd_workspace_bytes.argtypes = [D, i32]
+        L.ffd_workspace_bytes.restype = sz
+        L.ffd_num_splits.argtypes = [D, i32, i32]
+        L.ffd_num_splits.restype = i32
+        L.ffd_quantize_k_append.argtypes = [D, P, i32, i32, i32, P, P, P]
+        L.ffd_quantize_k_append.restype = i32
+        L.ffd_decode_sparse.argtypes = [D, P, P, P, P, P, f32, i32, P, P, P, P, sz, P]
+        L.ffd_decode_sparse.restype = i32
+        L.ffd_decode_dense.argtypes = [D, P, P, P, i32, P, P, P, sz, P]
+        L.ffd_decode_dense.restype = i32
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return int(lib().ffd_abi_version())
+
+
+def status_string(status: int) -> str:
+    return lib().ffd_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != FFD_OK:
+        raise FFDError(status, status_string(status))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FFD_BF16
+    if t.dtype == torch.float32:
+        return FFD_F32
+    raise TypeError(f"q, K and V must be bfloat16 or float32, got {t.dtype}")
+
+
+def make_dims(B: int, Hq: int, Hkv: int, seq_len: int, seq_cap: int, dtype: int,
+              head_dim: int = HEAD_DIM) -> Dims:
+    return Dims(B, Hq, Hkv, head_dim, seq_len, seq_cap, dtype)
+
+
+def dims_of(q: torch.Tensor, K: torch.Tensor, seq_len: int) -> Dims:
+    if q.dim() != 3 or K.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and K [B, Hkv, seq_cap, d]")
+    B, Hq, d = q.shape
+    B2, Hkv, cap, d2 = K.shape
+    if B2 != B or d2 != d:
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} vs K {tuple(K.shape)}")
+    return make_dims(B, Hq, Hkv, seq_len, cap, _dtype_code(K), d)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def workspace_bytes(dims: Dims, block: int) -> int:
+    return int(lib().ffd_workspace_bytes(ctypes.byref(dims), block))
+
+
+def num_splits(dims: Dims, block: int, sparse: bool = True) -> int:
+    return int(lib().ffd_num_splits(ctypes.byref(dims), block, 1 if sparse else 0))
+
+
+def alloc_workspace(dims: Dims, block: int, device) -> torch.Tensor:
+    n = workspace_bytes(dims, block)
+    if n == 0:
+        raise FFDError(FFD_ERR_INVALID_ARG, "invalid dims for workspace")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def alloc_kq(K: torch.Tensor, block: int):
+    """Zero-filled Kq [B, Hkv, seq_cap, d/2] u8 and scales [B, Hkv, seq_cap/block, d] fp32."""
+    B, Hkv, cap, d = K.shape
+    Kq = torch.zeros((B, Hkv, cap, d // 2), dtype=torch.uint8, device=K.device)
+    sc = torch.zeros((B, Hkv, cap // block, d), dtype=torch.float32, device=K.device)
+    return Kq, sc
+
+
+def quantize_k_append(K: torch.Tensor, tok_begin: int, tok_end: int, block: int,
+                      Kq: torch.Tensor, scales: torch.Tensor, seq_len: int | None = None,
+                      stream=None) -> None:
+    """Quantize the blocks of K completed by tokens [tok_begin, tok_end) into Kq / scales."""
+    B, Hkv, cap, d = K.shape
+    _need(K, "K")
+    _need(Kq, "Kq", torch.uint8, (B, Hkv, cap, d // 2), K.device)
+    _need(scales, "scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d),
+          K.device)
+    dims = make_dims(B, Hkv, Hkv, seq_len if seq_len is not None else cap, cap, _dtype_code(K), d)
+    _check(lib().ffd_quantize_k_append(ctypes.byref(dims), _ptr(K), tok_begin, tok_end, block,
+                                       _ptr(Kq), _ptr(scales), _stream(stream)))
+
+
+def _decode_outputs(q, out, lse, want_lse):
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, Hq, d), q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hq), q.device)
+    return out, lse
+
+
+def decode_sparse(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, Kq: torch.Tensor,
+                  scales: torch.Tensor, delta: float, block: int, seq_len: int,
+                  out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                  keep_mask: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                  want_lse: bool = True, stream=None):
+    """Sparse decode step.  Returns (out [B,Hq,d] fp32, lse [B,Hq] fp32 or None)."""
+    dims = dims_of(q, K, seq_len)
+    for name, t in (("q", q), ("K", K), ("V", V)):
+        _need(t, name, K.dtype, None, K.device)
+    _need(V, "V", K.dtype, K.shape, K.device)
+    B, Hkv, cap, d = K.shape
+    _need(Kq, "Kq", torch.uint8, (B, Hkv, cap, d // 2), K.device)
+    _need(scales, "scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d),
+          K.device)
+    out, lse = _decode_outputs(q, out, lse, want_lse)
+    if keep_mask is not None:
+        _need(keep_mask, "keep_mask", torch.uint8,
+              (q.shape[0], q.shape[1], math.ceil(seq_len / block)), q.device)
+    if workspace is None:
+        workspace = alloc_workspace(dims, block, q.device)
+    _need(workspace, "workspace", torch.uint8, None, q.device)
+    _check(lib().ffd_decode_sparse(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V), _ptr(Kq),
+                                   _ptr(scales), float(delta), block, _ptr(out), _ptr(lse),
+                                   _ptr(keep_mask), _ptr(workspace), workspace.numel(),
+                                   _stream(stream)))
+    return out, lse
+
+
+def decode_dense(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, block: int, seq_len: int,
+                 out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None, want_lse: bool = True, stream=None):
+    """Dense (exact flash-decoding) step.  Returns (out, lse)."""
+    dims = dims_of(q, K, seq_len)
+    for name, t in (("q", q), ("K", K), ("V", V)):
+        _need(t, name, K.dtype, None, K.device)
+    _need(V, "V", K.dtype, K.shape, K.device)
+    out, lse = _decode_outputs(q, out, lse, want_lse)
+    if workspace is None:
+        workspace = alloc_workspace(dims, block, q.device)
+    _need(workspace, "workspace", torch.uint8, None, q.device)
+    _check(lib().ffd_decode_dense(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V), block,
+                                  _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                  _stream(stream)))
+    return out, lse

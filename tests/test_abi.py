@@ -1,0 +1,132 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function declared in
+include/ffd.h, and rejects bad arguments before any HIP call (so nothing is launched)."""
+import ctypes
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+
+from long_context_decoding_amd import ffd
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "ffd.h"
+
+# fake, 16-byte aligned device addresses: validation must fail before anything dereferences them
+A = ctypes.c_void_p(0x10000)
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(ffd_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not ffd.LIB_PATH.exists():
+        pytest.skip("libffd.so not built")
+    return ffd.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"ffd_quantize_k_append", "ffd_decode_sparse", "ffd_decode_dense",
+            "ffd_workspace_bytes", "ffd_status_string", "ffd_abi_version"} <= set(names)
+    nm = subprocess.run(["nm", "-D", "--defined-only", str(ffd.LIB_PATH)], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ffd_\w+)", nm))
+    for n in names:
+        assert n in exported, f"{n} declared in ffd.h but not exported"
+        assert hasattr(L, n)
+
+
+def test_version_and_status_strings(L):
+    assert ffd.abi_version() == 1
+    for s in range(5):
+        assert ffd.status_string(s)
+    assert ffd.status_string(99) == "unknown status"
+
+
+def dims(**kw):
+    base = dict(B=1, Hq=32, Hkv=8, seq_len=4096, seq_cap=4096, dtype=ffd.FFD_BF16)
+    base.update(kw)
+    return ffd.make_dims(base["B"], base["Hq"], base["Hkv"], base["seq_len"], base["seq_cap"],
+                         base["dtype"], base.get("head_dim", 128))
+
+
+def sparse_call(L, d, block=64, delta=5.0, q=A, ws=A, ws_bytes=1 << 30, K=A, keep=None):
+    return L.ffd_decode_sparse(ctypes.byref(d), q, K, A, A, A, delta, block, A, A, keep, ws,
+                               ws_bytes, None)
+
+
+def test_workspace_and_splits(L):
+    d = dims()
+    S = ffd.num_splits(d, 64)
+    assert S >= 1
+    assert ffd.workspace_bytes(d, 64) == 1 * 32 * S * (128 + 4) * 4
+    big = dims(B=8, seq_len=131072, seq_cap=131072)
+    S = ffd.num_splits(big, 64)
+    assert -(-2048 // S) <= 256
+    assert ffd.workspace_bytes(dims(head_dim=64), 64) == 0
+    assert ffd.workspace_bytes(d, 96) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), ffd.FFD_ERR_UNSUPPORTED),
+    (dict(Hq=24, Hkv=8), ffd.FFD_ERR_UNSUPPORTED),      # G = 3
+    (dict(Hq=30, Hkv=8), ffd.FFD_ERR_INVALID_ARG),      # not a multiple
+    (dict(seq_len=0), ffd.FFD_ERR_INVALID_ARG),
+    (dict(seq_cap=4000), ffd.FFD_ERR_INVALID_ARG),      # < seq_len
+    (dict(seq_len=100, seq_cap=100), ffd.FFD_ERR_INVALID_ARG),  # cap not a block multiple
+    (dict(dtype=7), ffd.FFD_ERR_INVALID_ARG),
+    (dict(B=-1), ffd.FFD_ERR_INVALID_ARG),
+])
+def test_bad_dims(L, kw, status):
+    assert sparse_call(L, dims(**kw)) == status
+
+
+def test_bad_arguments(L):
+    d = dims()
+    assert sparse_call(L, d, block=96) == ffd.FFD_ERR_UNSUPPORTED
+    assert sparse_call(L, d, block=0) == ffd.FFD_ERR_INVALID_ARG
+    assert sparse_call(L, d, delta=float("nan")) == ffd.FFD_ERR_INVALID_ARG
+    assert sparse_call(L, d, delta=-1.0) == ffd.FFD_ERR_INVALID_ARG
+    assert sparse_call(L, d, q=None) == ffd.FFD_ERR_INVALID_ARG
+    assert sparse_call(L, d, K=MISALIGNED) == ffd.FFD_ERR_INVALID_ARG
+    assert sparse_call(L, d, keep=MISALIGNED) == ffd.FFD_ERR_INVALID_ARG
+    assert sparse_call(L, d, ws=None) == ffd.FFD_ERR_WORKSPACE
+    assert sparse_call(L, d, ws_bytes=ffd.workspace_bytes(d, 64) - 1) == ffd.FFD_ERR_WORKSPACE
+    assert L.ffd_decode_dense(ctypes.byref(d), A, A, A, 64, A, A, A, 16, None) == \
+        ffd.FFD_ERR_WORKSPACE
+    assert L.ffd_decode_dense(ctypes.byref(d), A, A, None, 64, A, A, A, 1 << 30, None) == \
+        ffd.FFD_ERR_INVALID_ARG
+
+
+def test_quantize_validation(L):
+    d = dims()
+    q = L.ffd_quantize_k_append
+    assert q(ctypes.byref(d), A, 0, 4097, 64, A, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert q(ctypes.byref(d), A, 10, 5, 64, A, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert q(ctypes.byref(d), A, -1, 5, 64, A, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert q(ctypes.byref(d), None, 0, 64, 64, A, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert q(ctypes.byref(d), A, 0, 64, 128, A, MISALIGNED, None) == ffd.FFD_ERR_INVALID_ARG
+    # ranges that complete no block launch nothing and succeed
+    assert q(ctypes.byref(d), A, 0, 63, 64, A, A, None) == ffd.FFD_OK
+    assert q(ctypes.byref(d), A, 64, 127, 64, A, A, None) == ffd.FFD_OK
+
+
+def test_empty_batch_is_a_noop(L):
+    d = dims(B=0)
+    assert sparse_call(L, d, q=None, ws=None, ws_bytes=0) == ffd.FFD_OK
+    assert L.ffd_decode_dense(ctypes.byref(d), None, None, None, 64, None, None, None, 0,
+                              None) == ffd.FFD_OK
+    assert L.ffd_quantize_k_append(ctypes.byref(d), None, 0, 4096, 64, None, None, None) == \
+        ffd.FFD_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(ffd, "LIB_PATH", tmp_path / "missing.so")
+    monkeypatch.setattr(ffd, "_lib", None)
+    with pytest.raises(FileNotFoundError):
+        ffd.lib()

@@ -1,0 +1,203 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Bar: Kq / scales byte-exact, keep masks bit-exact, out and lse within 2e-3 (bf16 q/K/V) or 1e-5
+(fp32) absolute.  Small cases span several blocks, every group size, both block sizes and a
+ragged tail; the named workloads run at full size in the same launch configuration as the
+benchmark, with masks compared for every head and outputs for sampled heads.
+"""
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import log
+from helpers import (DEV, TOL, assert_close, gpu_dense, gpu_quantize, gpu_sparse, oracle_attend,
+                     oracle_masks, sample_heads, upload)
+from long_context_decoding_amd import ffd
+from long_context_decoding_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+INF = float("inf")
+DELTAS = (0.0, 0.5, 2.0, 5.0, INF)
+
+CASES = [(dt, G, T, L)
+         for dt in ("bf16", "f32")
+         for G in (1, 2, 4, 8)
+         for T in (64, 128)
+         for L in (T, 2 * T, 3 * T + 17, 20 * T + 5)]
+
+
+def small_case(dt, G, T, L):
+    B = 2 if (G + L) % 2 == 0 else 1
+    Hkv = 2 if G <= 4 else 1
+    plant = "powerlaw" if (L // T) % 2 == 0 else "needles"
+    seed = 1000 * G + 7 * T + L + (0 if dt == "bf16" else 1)
+    return W.small(f"case_{dt}_G{G}_T{T}_L{L}", B=B, Hq=G * Hkv, Hkv=Hkv, L=L, T=T, dtype=dt,
+                   seed=seed, plant=plant)
+
+
+def oracle_quantize(w, K):
+    return oracle.quantize_k(K, w.T, 0, w.L)
+
+
+@pytest.mark.parametrize("dt,G,T,L", CASES)
+def test_small_sparse_and_dense(dt, G, T, L):
+    w = small_case(dt, G, T, L)
+    q, K, V, _ = W.make_inputs(w)
+    log(f"[gpu] {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv}")
+    qd, Kd, Vd = upload(w, q, K, V)
+    Kq_d, sc_d = gpu_quantize(w, Kd)
+    Kq, sc = oracle_quantize(w, K)
+    np.testing.assert_array_equal(Kq_d.cpu().numpy(), Kq)
+    np.testing.assert_array_equal(sc_d.cpu().numpy(), sc)
+    tol = TOL[dt]
+    for delta in DELTAS:
+        out, lse, keep = gpu_sparse(w, qd, Kd, Vd, Kq_d, sc_d, delta)
+        ref = oracle.decode(q, K, V, w.L, w.T, delta=delta, Kq=Kq, scales=sc)
+        np.testing.assert_array_equal(keep, ref["keep"], err_msg=f"mask delta={delta}")
+        assert_close(out, ref["out"], tol, f"out delta={delta}")
+        assert_close(lse, ref["lse"], tol, f"lse delta={delta}")
+    out, lse = gpu_dense(w, qd, Kd, Vd)
+    ref = oracle.decode(q, K, V, w.L, w.T, sparse=False)
+    assert_close(out, ref["out"], tol, "dense out")
+    assert_close(lse, ref["lse"], tol, "dense lse")
+
+
+def test_append_incremental_equals_one_shot():
+    w = W.small("append", B=2, Hq=8, Hkv=2, L=9 * 64 + 30, T=64, seed=5)
+    q, K, V, _ = W.make_inputs(w)
+    _, Kd, _ = upload(w, q, K, V)
+    Kq1, sc1 = gpu_quantize(w, Kd)
+    Kq2, sc2 = ffd.alloc_kq(Kd, w.T)
+    bounds = [0, 1, 63, 64, 65, 200, 383, 384, 500, w.L]
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        ffd.quantize_k_append(Kd, a, b, w.T, Kq2, sc2, seq_len=w.L)
+    torch.cuda.synchronize()
+    assert torch.equal(Kq1, Kq2) and torch.equal(sc1, sc2)
+    Kq, sc = oracle.quantize_k(K, w.T, 0, w.L)
+    np.testing.assert_array_equal(Kq2.cpu().numpy(), Kq)
+
+
+def oracle_quantize_threaded(w, K, slices):
+    Kq = np.zeros((w.B, w.Hkv, w.cap, w.d // 2), np.uint8)
+    sc = np.zeros((w.B, w.Hkv, w.cap // w.T, w.d), np.float32)
+
+    def one(bg):
+        b, g = bg
+        oracle.quantize_k(K[b:b + 1, g:g + 1], w.T, 0, w.L, Kq=Kq[b:b + 1, g:g + 1],
+                          scales=sc[b:b + 1, g:g + 1])
+
+    with ThreadPoolExecutor(16) as ex:
+        list(ex.map(one, slices))
+    return Kq, sc
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_named_workload_full_size(name):
+    w = W.WORKLOADS[name]
+    log(f"[gpu] full-size {name}: generating")
+    q, K, V, info = W.make_inputs(w)
+    all_slices = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    log(f"[gpu] full-size {name}: oracle quantize")
+    Kq, sc = oracle_quantize_threaded(w, K, all_slices)
+    log(f"[gpu] full-size {name}: upload + quantize on GPU")
+    qd, Kd, Vd = upload(w, q, K, V)
+    Kq_d, sc_d = gpu_quantize(w, Kd)
+    torch.cuda.synchronize()
+    assert torch.equal(Kq_d.cpu(), torch.from_numpy(Kq)), "Kq bytes differ"
+    assert torch.equal(sc_d.cpu(), torch.from_numpy(sc)), "scales differ"
+    heads = sample_heads(w, 12, seed=w.seed)
+    tol = TOL[w.dtype]
+    for delta in w.deltas:
+        log(f"[gpu] full-size {name}: sparse delta={delta}")
+        out, lse, keep = gpu_sparse(w, qd, Kd, Vd, Kq_d, sc_d, delta)
+        ref_keep = oracle_masks(w, q, Kq, sc, delta)
+        np.testing.assert_array_equal(keep, ref_keep, err_msg=f"{name} mask delta={delta}")
+        ref = oracle_attend(w, q, K, V, heads, keep=ref_keep)
+        for (b, h) in heads:
+            assert_close(out[b, h], ref[(b, h)][0], tol, f"{name} out b={b} h={h}")
+            assert_close(lse[b, h], ref[(b, h)][1], tol, f"{name} lse b={b} h={h}")
+        log(f"[gpu] full-size {name}: delta={delta} union keep "
+            f"{keep.reshape(w.B, w.Hkv, w.G, -1).max(axis=2).mean():.4f}")
+    log(f"[gpu] full-size {name}: dense")
+    out, lse = gpu_dense(w, qd, Kd, Vd)
+    ref = oracle_attend(w, q, K, V, heads, keep=None)
+    for (b, h) in heads:
+        assert_close(out[b, h], ref[(b, h)][0], tol, f"{name} dense out b={b} h={h}")
+        assert_close(lse[b, h], ref[(b, h)][1], tol, f"{name} dense lse b={b} h={h}")
+    del qd, Kd, Vd, Kq_d, sc_d
+    torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------------------------
+# Properties of the HIP path itself
+# --------------------------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def mid_case():
+    w = W.WORKLOADS["gqa4_32k_sink_needles"].with_(L=200 * 64 + 33, B=2)
+    q, K, V, _ = W.make_inputs(w)
+    qd, Kd, Vd = upload(w, q, K, V)
+    Kq_d, sc_d = gpu_quantize(w, Kd)
+    return w, (q, K, V), (qd, Kd, Vd, Kq_d, sc_d)
+
+
+def test_delta_inf_equals_dense(mid_case):
+    w, _, (qd, Kd, Vd, Kq_d, sc_d) = mid_case
+    out, lse, keep = gpu_sparse(w, qd, Kd, Vd, Kq_d, sc_d, INF)
+    assert keep.all()
+    out2, lse2 = gpu_dense(w, qd, Kd, Vd)
+    assert_close(out, out2, 1e-5, "sparse(inf) vs dense out")
+    assert_close(lse, lse2, 1e-5, "sparse(inf) vs dense lse")
+
+
+def test_masks_nested_in_delta(mid_case):
+    w, _, (qd, Kd, Vd, Kq_d, sc_d) = mid_case
+    prev = None
+    for delta in (0.0, 1.0, 3.0, 5.0, 8.0, 12.0):
+        _, _, keep = gpu_sparse(w, qd, Kd, Vd, Kq_d, sc_d, delta)
+        if prev is not None:
+            assert (keep >= prev).all(), f"mask not monotone at delta={delta}"
+        prev = keep
+
+
+@pytest.mark.parametrize("splits", ["1", "2", "7", "33"])
+def test_split_invariance(mid_case, splits, monkeypatch):
+    w, _, (qd, Kd, Vd, Kq_d, sc_d) = mid_case
+    out0, lse0, keep0 = gpu_sparse(w, qd, Kd, Vd, Kq_d, sc_d, 5.0)
+    d0, dl0 = gpu_dense(w, qd, Kd, Vd)
+    monkeypatch.setenv("FFD_NUM_SPLITS", splits)
+    dims = ffd.dims_of(qd, Kd, w.L)
+    log(f"[gpu] split invariance S={ffd.num_splits(dims, w.T)}")
+    out, lse, keep = gpu_sparse(w, qd, Kd, Vd, Kq_d, sc_d, 5.0)
+    np.testing.assert_array_equal(keep, keep0)
+    assert_close(out, out0, 1e-5, "out vs default split")
+    assert_close(lse, lse0, 1e-5, "lse vs default split")
+    d, dl = gpu_dense(w, qd, Kd, Vd)
+    assert_close(d, d0, 1e-5, "dense out vs default split")
+
+
+def test_deterministic(mid_case):
+    w, _, (qd, Kd, Vd, Kq_d, sc_d) = mid_case
+    a = gpu_sparse(w, qd, Kd, Vd, Kq_d, sc_d, 5.0)
+    b = gpu_sparse(w, qd, Kd, Vd, Kq_d, sc_d, 5.0)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_errors_launch_nothing(mid_case):
+    w, _, (qd, Kd, Vd, Kq_d, sc_d) = mid_case
+    with pytest.raises(ffd.FFDError) as e:
+        ffd.decode_sparse(qd, Kd, Vd, Kq_d, sc_d, float("nan"), w.T, w.L)
+    assert e.value.status == ffd.FFD_ERR_INVALID_ARG
+    small_ws = torch.empty(64, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ffd.FFDError) as e:
+        ffd.decode_sparse(qd, Kd, Vd, Kq_d, sc_d, 5.0, w.T, w.L, workspace=small_ws)
+    assert e.value.status == ffd.FFD_ERR_WORKSPACE
+    with pytest.raises(ffd.FFDError) as e:
+        ffd.decode_dense(qd, Kd, Vd, 96, w.L)
+    assert e.value.status in (ffd.FFD_ERR_UNSUPPORTED, ffd.FFD_ERR_INVALID_ARG)
