@@ -1,0 +1,347 @@
+"""Benchmark of one sparse decode step (scan -> top-delta select -> exact attention on kept blocks
+-> split-KV combine) on one MI355X, against the dense flash-decoding step of the same library and
+the CPU oracle.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--delta D] [--no-secondary]
+
+Prints ONE JSON line.  `value` is the device time of one decode step in microseconds: HIP
+events around one replay of a HIP graph holding `--steps` consecutive steps that rotate over
+copies of the KV cache (as consecutive layers of a model would), so that every input is resident
+in HBM and none is in the 256 MiB Infinity Cache when its step starts.  Eager back-to-back
+launches and same-cache (warm) figures are reported beside it.
+The bytes behind the bandwidth figures are algorithmic: packed int4 keys and their scales for
+every full block, bf16 K and V for every block that some query head of its group keeps, and q.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+METRIC = ("µs/decode step + effective HBM GB/s (% peak) at 128K/256K; speedup vs dense")
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E vendor peak
+PRIMARY = "gqa4_256k_sink_needles"
+SECONDARY = "b8_gqa4_128k_powerlaw"
+KERNEL_SRC = ROOT / "long_context_decoding_amd" / "csrc" / "ffd_kernels.hip"
+TRAFFIC_FILE = ROOT / "profiles" / "traffic_decode_sparse.json"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()[:16]
+
+
+# ------------------------------------------------------------------------------------------
+# Byte accounting
+# ------------------------------------------------------------------------------------------
+def bytes_sparse(w, keep: np.ndarray) -> dict:
+    """Algorithmic bytes read by one sparse step, from the kept-block mask [B, Hq, n_blocks]."""
+    e, d, T = w.elem_bytes, w.d, w.T
+    scan = w.B * w.Hkv * w.n_full * (T * d // 2 + 4 * d)
+    union = keep.reshape(w.B, w.Hkv, w.G, w.n_blocks).max(axis=2)       # [B, Hkv, n_blocks]
+    tokens = np.full(w.n_blocks, T, dtype=np.int64)
+    if w.L % T:
+        tokens[-1] = w.L % T
+    kept_tokens = int((union.astype(np.int64) * tokens[None, None, :]).sum())
+    exact = kept_tokens * 2 * d * e
+    qb = w.B * w.Hq * d * e
+    return {"scan": scan, "exact": exact, "q": qb, "total": scan + exact + qb,
+            "union_keep": float(union.mean()), "head_keep": float(keep.mean())}
+
+
+def bytes_dense(w) -> int:
+    return 2 * w.B * w.Hkv * w.L * w.d * w.elem_bytes + w.B * w.Hq * w.d * w.elem_bytes
+
+
+# ------------------------------------------------------------------------------------------
+# GPU measurement
+# ------------------------------------------------------------------------------------------
+def run_workload(w, delta: float, steps: int, warmup: int, min_rotation_mib: int = 1024):
+    """Time one decode step of workload w on cuda:0.
+
+    Steps run back to back over R copies of the KV cache (like R layers of a model, each with
+    its own cache), so that a step never finds its inputs in the 256 MiB Infinity Cache; R is
+    chosen so that R steps read at least `min_rotation_mib`.  The timed region is `steps`
+    consecutive steps between two HIP events on the stream the library launches on."""
+    import torch
+
+    from long_context_decoding_amd import ffd
+    from long_context_decoding_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    q, K, V, _ = W.make_inputs(w)
+    log(f"{w.name}: inputs generated in {time.time() - t0:.1f}s "
+        f"(K {K.nbytes / 2**20:.0f} MiB)")
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    qd, Kd, Vd = up(q), up(K), up(V)
+    Kq, sc = ffd.alloc_kq(Kd, w.T)
+    stream = torch.cuda.current_stream()
+
+    # quantize (append of the whole cache): off the per-step path, timed for reference
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    ffd.quantize_k_append(Kd, 0, w.L, w.T, Kq, sc, seq_len=w.L)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    quant_us = ev0.elapsed_time(ev1) * 1e3
+
+    dims = ffd.dims_of(qd, Kd, w.L)
+    ws = ffd.alloc_workspace(dims, w.T, dev)
+    out_s = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+    lse_s = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+    out_d = torch.empty_like(out_s)
+    lse_d = torch.empty_like(lse_s)
+    keep = torch.zeros((w.B, w.Hq, w.n_blocks), dtype=torch.uint8, device=dev)
+
+    # mask and diagnostics (untimed call with the optional mask output)
+    ffd.decode_sparse(qd, Kd, Vd, Kq, sc, delta, w.T, w.L, out=out_s, lse=lse_s,
+                      keep_mask=keep, workspace=ws)
+    ffd.decode_dense(qd, Kd, Vd, w.T, w.L, out=out_d, lse=lse_d, workspace=ws)
+    torch.cuda.synchronize()
+    keep_np = keep.cpu().numpy()
+    o_s, o_d = out_s.double().cpu().numpy(), out_d.double().cpu().numpy()
+    cos = (o_s * o_d).sum(-1) / (np.linalg.norm(o_s, axis=-1) * np.linalg.norm(o_d, axis=-1))
+    lse_err = float(np.abs(lse_s.double().cpu().numpy() - lse_d.double().cpu().numpy()).max())
+    bs = bytes_sparse(w, keep_np)
+    bd = bytes_dense(w)
+
+    # copies of the cache ("layers")
+    R = max(2, math.ceil(min_rotation_mib * 2**20 / bs["total"]) + 1)
+    reps = [(Kd, Vd, Kq, sc)]
+    for _ in range(R - 1):
+        reps.append(tuple(t.clone() for t in (Kd, Vd, Kq, sc)))
+    torch.cuda.synchronize()
+
+    def sparse(r):
+        Kr, Vr, Kqr, scr = reps[r % R]
+        ffd.decode_sparse(qd, Kr, Vr, Kqr, scr, delta, w.T, w.L, out=out_s, lse=lse_s,
+                          workspace=ws)
+
+    def dense(r):
+        Kr, Vr, _, _ = reps[r % R]
+        ffd.decode_dense(qd, Kr, Vr, w.T, w.L, out=out_d, lse=lse_d, workspace=ws)
+
+    def timed_eager(fn, n, rotate=True):
+        """Device time per step (us) of n back-to-back eager steps."""
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(n):
+            fn(i if rotate else 0)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    def timed_graph(fn, n, rotate=True):
+        """Device time per step (us) of n steps recorded in one HIP graph and replayed: the
+        launch cost of a decode loop that submits its steps as a graph."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n):
+                fn(i if rotate else 0)
+        graph.replay()  # warm-up replay
+        torch.cuda.synchronize()
+        cur = torch.cuda.current_stream()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(cur)
+        graph.replay()
+        b.record(cur)
+        torch.cuda.synchronize()
+        del graph
+        return a.elapsed_time(b) * 1e3 / n
+
+    timed_eager(sparse, warmup)
+    timed_eager(dense, warmup)
+    us_s = timed_graph(sparse, steps)
+    us_d = timed_graph(dense, steps)
+    us_s_eager = timed_eager(sparse, steps)
+    us_d_eager = timed_eager(dense, steps)
+    us_s_warm = timed_graph(sparse, steps, rotate=False)
+    us_d_warm = timed_graph(dense, steps, rotate=False)
+
+    res = {
+        "workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "L": w.L,
+        "block": w.T, "delta": delta, "kv_dtype": w.dtype, "scan_bits": 4,
+        "splits": ffd.num_splits(dims, w.T), "cache_copies": R,
+        "sparse_us": us_s, "dense_us": us_d,
+        "sparse_us_eager": us_s_eager, "dense_us_eager": us_d_eager,
+        "sparse_us_warm_cache": us_s_warm, "dense_us_warm_cache": us_d_warm,
+        "speedup_vs_dense": us_d / us_s,
+        "bytes_read_sparse": bs["total"], "bytes_scan": bs["scan"], "bytes_exact": bs["exact"],
+        "bytes_read_dense": bd,
+        "sparse_GBps": bs["total"] / us_s * 1e-3, "dense_GBps": bd / us_d * 1e-3,
+        "sparse_hbm_frac": bs["total"] / us_s * 1e-3 / HBM_PEAK_GBPS,
+        "dense_hbm_frac": bd / us_d * 1e-3 / HBM_PEAK_GBPS,
+        "union_keep": bs["union_keep"], "head_keep": bs["head_keep"],
+        "recall_cos_min": float(cos.min()), "recall_cos_mean": float(cos.mean()),
+        "lse_err_vs_dense": lse_err,
+        "quantize_us": quant_us,
+    }
+    del reps, qd, Kd, Vd, Kq, sc, ws
+    torch.cuda.empty_cache()
+    return res, (q, K, V)
+
+
+# ------------------------------------------------------------------------------------------
+# CPU baseline: the oracle, unchanged, on the host cores
+# ------------------------------------------------------------------------------------------
+def cpu_baseline(w, delta: float, host, budget_s: float = 12.0) -> dict:
+    import oracle
+
+    q, K, V = host
+    nthreads = min(16, max(1, len(os.sched_getaffinity(0))))
+    t0 = time.time()
+    Kq, sc = oracle.quantize_k(K, w.T, 0, w.L)
+    quant_s = time.time() - t0
+    times = []
+    t_start = time.time()
+    while len(times) < 3 or (time.time() - t_start < budget_s and len(times) < 100):
+        t0 = time.perf_counter()
+        oracle.decode(q, K, V, w.L, w.T, delta=delta, Kq=Kq, scales=sc, n_threads=nthreads)
+        times.append(time.perf_counter() - t0)
+    med = float(np.median(times[1:])) if len(times) > 1 else times[0]
+    return {"value": med * 1e6, "unit": "µs/decode step", "cores": nthreads,
+            "kind": "oracle",
+            "sample": (f"whole sparse decode step of {w.name} (all {w.B * w.Hq} query heads: "
+                       f"integer scan, select, fp64 exact attention over kept blocks), "
+                       f"{len(times)} runs, median of runs 2..; oracle quantize of the cache "
+                       f"{quant_s:.2f}s not included")}
+
+
+def traffic_entry(bytes_alg: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel source; else None."""
+    try:
+        rec = json.loads(TRAFFIC_FILE.read_text())
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_src_sha256_16") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=PRIMARY)
+    ap.add_argument("--delta", type=float, default=None)
+    ap.add_argument("--secondary", default=SECONDARY,
+                    help="second workload reported alongside ('' for none)")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--rotation-mib", type=int, default=1024,
+                    help="minimum bytes read by one rotation over the cache copies")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this method runs on one GPU; multi-GPU runs are not supported "
+              "(kv heads shard across GPUs with no exchange, so per-GPU work is the single-GPU "
+              "step at Hkv/N heads)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from long_context_decoding_amd import ffd
+    from long_context_decoding_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    ffd.lib()  # fail loudly if the HIP library is missing
+
+    w = W.WORKLOADS[args.workload]
+    delta = args.delta if args.delta is not None else w.deltas[0]
+    t_wall = time.time()
+    prim, host = run_workload(w, delta, args.steps, args.warmup, args.rotation_mib)
+    log(f"{w.name}: sparse {prim['sparse_us']:.1f} us, dense {prim['dense_us']:.1f} us, "
+        f"{prim['sparse_GBps']:.0f} GB/s, keep {prim['union_keep']:.4f}")
+    sec = None
+    if args.secondary and not args.no_secondary and args.secondary != args.workload:
+        w2 = W.WORKLOADS[args.secondary]
+        sec, _ = run_workload(w2, w2.deltas[0], args.steps, args.warmup, args.rotation_mib)
+        log(f"{w2.name}: sparse {sec['sparse_us']:.1f} us, dense {sec['dense_us']:.1f} us, "
+            f"{sec['sparse_GBps']:.0f} GB/s, keep {sec['union_keep']:.4f}")
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(w, delta, host)
+    del host
+
+    us = prim["sparse_us"]
+    traffic = traffic_entry(prim["bytes_read_sparse"])
+    line = {
+        "metric": METRIC,
+        "value": round(us, 3),
+        "unit": "µs/decode step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": us * 1e-3,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.d, "context": w.L, "block": w.T, "delta": delta,
+                   "scan": "int4 keys x int8 query weights", "kv_dtype": w.dtype},
+        "effective_GBps": round(prim["sparse_GBps"], 1),
+        "hbm_frac": round(prim["sparse_hbm_frac"], 4),
+        "dense_us": round(prim["dense_us"], 3),
+        "speedup_vs_dense": round(prim["speedup_vs_dense"], 3),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "ffd sparse decode step",
+            "achieved": round(prim["sparse_GBps"], 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(prim["sparse_hbm_frac"], 4),
+            "traffic": traffic,
+            "bytes_per_launch": prim["bytes_read_sparse"],
+        },
+        "cpu_baseline": cpu,
+        "primary": prim,
+        "secondary": sec,
+        "pages_context": {
+            "kernel_speedup_peak": "11.6x over FlashAttention-2 (RTX 4090, 2-bit scan + 8-bit "
+                                   "residual, real Llama-3.1 traces)",
+            "kernel_speedup_256k_delta5": "6.58x (RTX 4090)",
+            "end_to_end": "2.37x over FlashAttention-2 at 16K (RTX 4090, Llama-3.1-8B)",
+        },
+        "kernel_src_sha256_16": kernel_hash(),
+        "wall_s": round(time.time() - t_wall, 1),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

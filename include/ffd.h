@@ -9,7 +9,8 @@
  *      (Sec. 3.2, Eq. 1; no sort, no cross-block synchronization),
  *   4. runs exact softmax(q K^T / sqrt(d)) V over the kept blocks only (Alg. 1, refinement), and
  *   5. merges the per-split partial softmax states with a log-sum-exp combine (the split-KV
- *      decoding of Sec. 2, FlashDecoding).
+ *      decoding of Sec. 2, FlashDecoding).  Steps 1-5 run in one kernel launch; the merge is done
+ *      by the last work-group of each (sequence, kv head) to finish.
  *
  * Conventions shared by every call
  *   - All tensors are dense, row-major, contiguous device allocations owned by the caller.
@@ -102,8 +103,11 @@ ffd_status ffd_quantize_k_append(const ffd_dims* dims, const void* K, int32_t to
  *   block      T in {64, 128}; Kq and scales must hold the quantized full blocks of K.
  *   out, lse   results; lse may be NULL.
  *   keep_mask  optional (NULL) per-(b, query head, block) selection, written as 0/1.
- *   workspace  caller-owned device memory of at least ffd_workspace_bytes(dims, block) bytes;
- *              its contents on entry do not matter; it holds per-split partials during the call.
+ *   workspace  caller-owned device memory of at least ffd_workspace_bytes(dims, block) bytes,
+ *              prepared once by ffd_workspace_init (for the same dims and block); it holds a
+ *              counter per (sequence, kv head), which every call returns to zero, and the
+ *              per-split partial softmax states.  Calls that share a workspace must not overlap
+ *              in time (run them on one stream).
  */
 ffd_status ffd_decode_sparse(const ffd_dims* dims, const void* q, const void* K, const void* V,
                              const uint8_t* Kq, const float* scales, float delta, int32_t block,
@@ -121,8 +125,15 @@ ffd_status ffd_decode_dense(const ffd_dims* dims, const void* q, const void* K, 
                             size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes needed by ffd_decode_sparse / ffd_decode_dense for these dims and block
- * (the maximum of the two); 0 for invalid dims. */
+ * (the maximum of the two); 0 for invalid dims.  The size depends on the split count, which the
+ * environment variable FFD_NUM_SPLITS (a positive integer) overrides. */
 size_t ffd_workspace_bytes(const ffd_dims* dims, int32_t block);
+
+/* Prepares a workspace for the decode calls: zeroes its per-(sequence, kv head) counters with a
+ * small kernel on `stream` (no memset, so it may be recorded into a graph).  Needed once per new
+ * allocation; a completed decode call leaves the workspace prepared. */
+ffd_status ffd_workspace_init(const ffd_dims* dims, int32_t block, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 /* Number of sequence splits (work-groups per (sequence, kv head)) the decode calls use. */
 int32_t ffd_num_splits(const ffd_dims* dims, int32_t block, int32_t sparse);

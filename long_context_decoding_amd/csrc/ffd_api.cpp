@@ -11,7 +11,7 @@ namespace {
 
 using ffd::kHeadDim;
 using ffd::kMaxBlocksPerSplit;
-using ffd::kPartStride;
+using ffd::kMaxSplits;
 using ffd::kWaves;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -30,8 +30,10 @@ ffd_status check_dims(const ffd_dims* d, int32_t block)
     if (d->seq_cap % block) return FFD_ERR_INVALID_ARG;
     const int G = d->n_q_heads / d->n_kv_heads;
     if (G != 1 && G != 2 && G != 4 && G != 8) return FFD_ERR_UNSUPPORTED;
-    // grid limits: batch * kv heads rows of work-groups, block counts in 16-bit tables
+    // grid and table limits: at most kMaxSplits splits of at most kMaxBlocksPerSplit blocks
     if ((int64_t)d->batch * d->n_kv_heads > 65535) return FFD_ERR_UNSUPPORTED;
+    const int64_t n_blocks = ((int64_t)d->seq_len + block - 1) / block;
+    if (n_blocks > (int64_t)kMaxSplits * kMaxBlocksPerSplit) return FFD_ERR_UNSUPPORTED;
     return FFD_OK;
 }
 
@@ -39,29 +41,42 @@ int splits_for(const ffd_dims* d, int32_t block)
 {
     const int n_blocks = (d->seq_len + block - 1) / block;
     const int64_t bh = (int64_t)d->batch * d->n_kv_heads;
-    if (const char* env = getenv("FFD_NUM_SPLITS")) {
-        int s = atoi(env);
-        if (s >= 1) {
-            if (s > n_blocks) s = n_blocks;
-            const int min_s = (n_blocks + kMaxBlocksPerSplit - 1) / kMaxBlocksPerSplit;
-            return s < min_s ? min_s : s;
-        }
+    const int min_s = (n_blocks + kMaxBlocksPerSplit - 1) / kMaxBlocksPerSplit;
+    int64_t s;
+    const char* env = getenv("FFD_NUM_SPLITS");
+    if (env && atoi(env) >= 1) {
+        s = atoi(env);
+        if (s > n_blocks) s = n_blocks;
+    } else {
+        // enough work-groups to fill 256 CUs a few times over, at least two blocks per wave
+        const int64_t target_wgs = 768;  // 3 resident work-groups on each of 256 CUs
+        s = bh > 0 ? (target_wgs + bh - 1) / bh : 1;
+        const int64_t max_s = n_blocks / (2 * kWaves) > 0 ? n_blocks / (2 * kWaves) : 1;
+        if (s > max_s) s = max_s;
     }
-    // enough work-groups to fill 256 CUs a few times over, at least two blocks per wave, and
-    // no more blocks per split than the kernel's tables hold
-    const int64_t target_wgs = 1024;
-    int64_t s = bh > 0 ? (target_wgs + bh - 1) / bh : 1;
-    const int64_t max_s = n_blocks / (2 * kWaves) > 0 ? n_blocks / (2 * kWaves) : 1;
-    if (s > max_s) s = max_s;
-    const int64_t min_s = (n_blocks + kMaxBlocksPerSplit - 1) / kMaxBlocksPerSplit;
+    if (s > kMaxSplits) s = kMaxSplits;
     if (s < min_s) s = min_s;
     if (s < 1) s = 1;
     return (int)s;
 }
 
-size_t part_bytes(const ffd_dims* d, int S)
+// Workspace layout: counters [B*Hkv] u32 | ml [B*Hkv*S*G] float2 | o [B*Hkv*S*G*d] fp32,
+// each region starting on a 256-byte boundary.
+struct WsLayout {
+    size_t off_ml, off_o, total;
+};
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const ffd_dims* d, int S)
 {
-    return (size_t)d->batch * d->n_q_heads * (size_t)S * kPartStride * sizeof(float);
+    const size_t bh = (size_t)d->batch * d->n_kv_heads;
+    const size_t rec = bh * (size_t)S * (size_t)(d->n_q_heads / d->n_kv_heads);
+    WsLayout w;
+    w.off_ml = round256(bh * sizeof(uint32_t));
+    w.off_o = w.off_ml + round256(rec * 2 * sizeof(float));
+    w.total = w.off_o + rec * kHeadDim * sizeof(float);
+    return w;
 }
 
 ffd_status finish(hipError_t e) { return e == hipSuccess ? FFD_OK : FFD_ERR_HIP; }
@@ -83,8 +98,9 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
         if (isnan(delta) || delta < 0.0f) return FFD_ERR_INVALID_ARG;
     }
     const int S = splits_for(dims, block);
+    const WsLayout lay = ws_layout(dims, S);
     if (!workspace || !aligned16(workspace)) return FFD_ERR_WORKSPACE;
-    if (workspace_bytes < part_bytes(dims, S)) return FFD_ERR_WORKSPACE;
+    if (workspace_bytes < lay.total) return FFD_ERR_WORKSPACE;
 
     ffd::DecodeParams p{};
     p.q = q;
@@ -95,7 +111,10 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
     p.out = out;
     p.lse = lse;
     p.keep_mask = keep_mask;
-    p.part = static_cast<float*>(workspace);
+    char* wsb = static_cast<char*>(workspace);
+    p.counters = reinterpret_cast<uint32_t*>(wsb);
+    p.part_ml = reinterpret_cast<float2*>(wsb + lay.off_ml);
+    p.part_o = reinterpret_cast<float*>(wsb + lay.off_o);
     p.B = dims->batch;
     p.Hq = dims->n_q_heads;
     p.Hkv = dims->n_kv_heads;
@@ -134,7 +153,19 @@ const char* ffd_status_string(ffd_status s)
 size_t ffd_workspace_bytes(const ffd_dims* dims, int32_t block)
 {
     if (check_dims(dims, block) != FFD_OK) return 0;
-    return part_bytes(dims, splits_for(dims, block));
+    return ws_layout(dims, splits_for(dims, block)).total;
+}
+
+ffd_status ffd_workspace_init(const ffd_dims* dims, int32_t block, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream)
+{
+    ffd_status st = check_dims(dims, block);
+    if (st != FFD_OK) return st;
+    if (dims->batch == 0) return FFD_OK;
+    if (!workspace || !aligned16(workspace)) return FFD_ERR_WORKSPACE;
+    if (workspace_bytes < ws_layout(dims, splits_for(dims, block)).total) return FFD_ERR_WORKSPACE;
+    return finish(ffd::launch_zero_counters(static_cast<uint32_t*>(workspace),
+                                            dims->batch * dims->n_kv_heads, stream));
 }
 
 int32_t ffd_num_splits(const ffd_dims* dims, int32_t block, int32_t sparse)

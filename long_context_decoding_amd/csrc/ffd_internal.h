@@ -5,13 +5,14 @@
 #include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
+#include <hip/hip_vector_types.h>
 
 namespace ffd {
 
 constexpr int kHeadDim = 128;
-constexpr int kPartStride = kHeadDim + 4;  // per-split record: o[128], m (log2 units), l, pad
 constexpr int kWaves = 4;                  // waves per work-group of the decode kernels
 constexpr int kMaxBlocksPerSplit = 256;    // LDS sizing of the per-split block tables
+constexpr int kMaxSplits = 256;            // LDS sizing of the final split merge
 
 struct DecodeParams {
     const void* q;
@@ -22,7 +23,9 @@ struct DecodeParams {
     float* out;
     float* lse;
     uint8_t* keep_mask;
-    float* part;    // [B*Hq][S][kPartStride]
+    uint32_t* counters;  // [B*Hkv] finished splits of each (b, kv head); zero between calls
+    float2* part_ml;     // [B*Hkv][S][G] per-split (max in log2 units, sum of exp2)
+    float* part_o;       // [B*Hkv][S][G][d] per-split unnormalized output
     int B, Hq, Hkv, G;
     int L, cap, T;
     int n_full, n_blocks;
@@ -43,5 +46,6 @@ struct QuantParams {
 // Launchers (ffd_kernels.hip).  Return the hipError_t of the launch.
 hipError_t launch_decode(const DecodeParams& p, bool bf16, bool sparse, hipStream_t stream);
 hipError_t launch_quantize(const QuantParams& p, bool bf16, hipStream_t stream);
+hipError_t launch_zero_counters(uint32_t* counters, int n, hipStream_t stream);
 
 }  // namespace ffd

@@ -11,9 +11,10 @@
 //                               iff its estimated max >= pseudo-max - delta (Eq. 1)
 //                      exact    bf16/fp32 MFMA for the G x 16 score tile, online softmax with
 //                               fp32 probabilities, PV on the VALU in fp32 (Alg. 1 refinement)
-//                    then writes one partial (o, m, l) per query head (split-KV, FTF Sec. 2).
+//                      combine  one partial (o, m, l) per query head; the last work-group of the
+//                               (sequence, kv head) merges the splits' partials with the
+//                               log-sum-exp rule (split-KV decoding, FTF Sec. 2)
 //                    The dense baseline is the same kernel with every block kept and no scan.
-//   combine_kernel   log-sum-exp merge of the splits -> out, lse.
 //
 // Wave layout conventions (wave64):
 //   lane = 16 * kg + col, kg = lane >> 4 in 0..3, col = lane & 15.
@@ -237,17 +238,6 @@ __device__ __forceinline__ void tile_load(TileRegs<BF16>& r, const void* __restr
     }
 }
 
-template <bool BF16>
-struct QueryRegs;
-template <>
-struct QueryRegs<true> {
-    v8bf b[4];  // head col % G, channels 32*ks + 8*kg ..
-};
-template <>
-struct QueryRegs<false> {
-    float b[32];  // head col % G, channels 32*kg + i
-};
-
 template <int G>
 struct SoftState {
     float o[G][8];  // unnormalized output, channels 8*col.., summed over this lane's tokens
@@ -256,25 +246,31 @@ struct SoftState {
 };
 
 template <int G, bool BF16>
-__device__ __forceinline__ void tile_compute(const TileRegs<BF16>& r, const QueryRegs<BF16>& qr,
+__device__ __forceinline__ void tile_compute(const TileRegs<BF16>& r, const void* __restrict__ qrow,
                                              SoftState<G>& st, WaveScratch<G>& ws, int t0, int L,
                                              u32 kbits, float c_log2, int lane)
 {
     const int col = lane & 15, kg = lane >> 4;
     // scores S[token t0 + 4 kg + v][head col % G]
     v4f acc = {0.f, 0.f, 0.f, 0.f};
+    // B operand: query head col % G, read from LDS (channels 32 ks + 8 kg .. for bf16,
+    // 32 kg + 4 i .. for fp32), the same channel slice as the key row in the A operand
     if constexpr (BF16) {
+        const __bf16* qb = static_cast<const __bf16*>(qrow);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, r.k[ks]),
-                                                          qr.b[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(v8bf, r.k[ks]),
+                *reinterpret_cast<const v8bf*>(qb + ks * 32 + kg * 8), acc, 0, 0, 0);
     } else {
+        const float* qf = static_cast<const float*>(qrow);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r.k[i].x, qr.b[4 * i + 0], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r.k[i].y, qr.b[4 * i + 1], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r.k[i].z, qr.b[4 * i + 2], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r.k[i].w, qr.b[4 * i + 3], acc, 0, 0, 0);
+            const float4 qv = *reinterpret_cast<const float4*>(qf + kg * 32 + 4 * i);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r.k[i].x, qv.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r.k[i].y, qv.y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r.k[i].z, qv.z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r.k[i].w, qv.w, acc, 0, 0, 0);
         }
     }
     const bool head_keep = (kbits >> (col % G)) & 1u;
@@ -353,28 +349,89 @@ struct __attribute__((aligned(16))) DecodeShared {
     WaveScratch<G> wave[kWaves];
     union {
         float shat[G][kMaxBlocksPerSplit];                 // scan results of the split's blocks
-        struct {
+        struct {                                            // the waves' softmax states
             float o[kWaves][G][D];
             float m[kWaves][G];
             float l[kWaves][G];
         } merge;
+        struct {                                            // final merge of the splits
+            float wgt[G][kMaxSplits];                       // weight of each non-empty split
+            uint16_t idx[G][kMaxSplits];                    // its index
+            float M[G], Lsum[G];
+            int cnt[G];
+        } fin;
     } u;
+    float4 q[G * D / 4];                   // the group's query rows (bf16 or fp32 bytes)
     float pro[2][G];                       // estimates of the sink and local blocks
     uint8_t kbits[kMaxBlocksPerSplit];     // per-block head mask (bit h = query head h of group)
     uint16_t list[kMaxBlocksPerSplit];     // kept blocks (offsets in the split)
     int n_kept;
+    int is_last;
 };
 
+__device__ __forceinline__ float wave_max(float x)
+{
+    x = row16_max(x);
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// Device-scope (agent) relaxed atomic loads and stores: on gfx950 these are plain global loads
+// and stores with the device-scope cache policy (sc1), which write through to, and read from,
+// the point where all XCDs' accesses are coherent.  The split partials travel this way so that
+// the merging work-group needs no cache-wide writeback or invalidate (an agent-scope fence costs
+// a walk of the XCD's L2 per work-group).
+__device__ __forceinline__ void st_dev(float* p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev2(float2* p, float a, float b)
+{
+    const unsigned long long v = (unsigned long long)(u32)as_i(a) |
+                                 ((unsigned long long)(u32)as_i(b) << 32);
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), v, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_dev2(const float2* p)
+{
+    const unsigned long long v = __hip_atomic_load(
+        reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(as_f((int)(u32)v), as_f((int)(u32)(v >> 32)));
+}
+
+// One work-group per (sequence b, kv head g, split of the sequence).  Phases:
+//   1. scan (sparse only): every full block of the split that is neither the sink nor the local
+//      block, plus the sink and local blocks themselves for the pseudo-max; items are dealt
+//      round-robin to the waves and software-pipelined two deep with unconditional (clamped)
+//      loads, so that the next item's loads stay in flight while the current one is computed;
+//   2. select (sparse only): threshold against pseudo-max - delta, forced blocks, compaction of
+//      the kept blocks into an LDS list;
+//   3. exact attention over the kept blocks' 16-token tiles (pipelined the same way);
+//   4. merge of the waves' softmax states -> one (o, m, l) partial per query head;
+//   5. the last work-group of (b, g) to finish (atomic counter) merges the splits' partials
+//      with the log-sum-exp rule into out and lse, and resets the counter.
 template <int T, int G, bool BF16, bool SPARSE>
-__global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p)
+__global__ __launch_bounds__(kWaves * 64, (BF16 && G <= 4) ? 3 : 2) void decode_kernel(DecodeParams p)
 {
     __shared__ DecodeShared<G> sh;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int col = lane & 15, kg = lane >> 4;
 
-    // work-group -> (b, kv head, split); sparse: the splits holding the sink (0) and the local
-    // block (S-1) are dispatched first, they always carry exact work.
+    // work-group -> (b, kv head, split); all splits of one (b, g) share blockIdx.x mod (B*Hkv),
+    // which keeps them on one XCD when B*Hkv is a multiple of 8.  Sparse: the splits holding
+    // the sink (0) and the local block (S-1) are dispatched first, they always carry exact work.
     const int bh = p.B * p.Hkv;
     const int id = blockIdx.x;
     const int bg = id % bh;
@@ -391,32 +448,17 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p)
     const char* Vbg = static_cast<const char*>(p.V) + kv_off * esz;
     const int h0 = b * p.Hq + g * G;  // first query row of the group
 
-    // query registers for the exact stage (head col % G)
-    QueryRegs<BF16> qr;
-    {
-        const int hq = h0 + col % G;
-        if constexpr (BF16) {
-            const __bf16* qp = static_cast<const __bf16*>(p.q) + (size_t)hq * D;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                qr.b[ks] = __builtin_bit_cast(
-                    v8bf, *reinterpret_cast<const uint4*>(qp + ks * 32 + kg * 8));
-        } else {
-            const float* qp = static_cast<const float*>(p.q) + (size_t)hq * D;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float4 x = *reinterpret_cast<const float4*>(qp + kg * 32 + 4 * i);
-                qr.b[4 * i] = x.x;
-                qr.b[4 * i + 1] = x.y;
-                qr.b[4 * i + 2] = x.z;
-                qr.b[4 * i + 3] = x.w;
-            }
-        }
-    }
-
     WaveScratch<G>& ws = sh.wave[w];
-    const int NT = p.T / 16;
+    constexpr int NT = T / 16;
     int n_kept;
+
+    // copy the group's G query rows to LDS (16 bytes per thread)
+    {
+        const float4* qsrc = reinterpret_cast<const float4*>(
+            static_cast<const char*>(p.q) + (size_t)h0 * D * esz);
+        const int n16 = (int)(G * D * esz / 16);
+        for (int i = threadIdx.x; i < n16; i += kWaves * 64) sh.q[i] = qsrc[i];
+    }
 
     if constexpr (SPARSE) {
         constexpr int HPL = (G + 3) / 4;
@@ -433,53 +475,52 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p)
                 qw[k][4] = bf16_lo(x.z); qw[k][5] = bf16_hi(x.z);
                 qw[k][6] = bf16_lo(x.w); qw[k][7] = bf16_hi(x.w);
             } else {
-                const float* qp = static_cast<const float*>(p.q) + (size_t)hq * D + col * 8;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) qw[k][i] = qp[i];
+                const float4* qp = reinterpret_cast<const float4*>(
+                    static_cast<const float*>(p.q) + (size_t)hq * D + col * 8);
+                const float4 a = qp[0], c = qp[1];
+                qw[k][0] = a.x; qw[k][1] = a.y; qw[k][2] = a.z; qw[k][3] = a.w;
+                qw[k][4] = c.x; qw[k][5] = c.y; qw[k][6] = c.z; qw[k][7] = c.w;
             }
         }
 
         const uint8_t* kq_bg = p.Kq + (size_t)bg * p.cap * (D / 2);
-        const float* sc_bg = p.scales + (size_t)bg * (p.cap / p.T) * D;
+        const float* sc_bg = p.scales + (size_t)bg * (p.cap / T) * D;
         const int nf = p.n_full;
-        // scan items of this wave: [prologue block], then blocks j_lo + w + NW*i of the split
-        // that are neither forced nor beyond the full blocks
-        const bool has_pro = (w < 2) && nf >= 1;
-        const int j_pro = (w == 0) ? 0 : nf - 1;
+        // scan items of the split: [sink, local] (pseudo-max), then the full blocks j_lo..j_hi-1
+        // that are neither; item i goes to wave i % kWaves
+        const int n_pro = nf >= 1 ? 2 : 0;
         const int j_lo = max(jb, 1);
         const int j_hi = min(je, nf - 1);
-        const int n_range = (j_hi - j_lo - w > 0) ? (j_hi - j_lo - w + kWaves - 1) / kWaves : 0;
-        const int n_items = (has_pro ? 1 : 0) + n_range;
-        auto item_block = [&](int i) -> int {
-            if (has_pro) {
-                if (i == 0) return j_pro;
-                --i;
-            }
-            return j_lo + w + i * kWaves;
+        const int n_all = n_pro + max(j_hi - j_lo, 0);
+        const int n_items = n_all > w ? (n_all - w + kWaves - 1) / kWaves : 0;
+        auto block_of = [&](int i) -> int {
+            if (i < n_pro) return i == 0 ? 0 : nf - 1;
+            return j_lo + (i - n_pro);
         };
-        auto store = [&](int i, float shat) {
-            if (lane < G) {
-                if (has_pro && i == 0) sh.pro[w][lane] = shat;
-                else sh.u.shat[lane][item_block(i) - jb] = shat;
-            }
-        };
-        ScanRegs<T> ra, rb;
         if (n_items > 0) {
-            const int j = item_block(0);
-            scan_load<T>(ra, kq_bg + (size_t)j * T * (D / 2), sc_bg + (size_t)j * D, lane);
-        }
-        for (int i = 0; i < n_items; i += 2) {
-            if (i + 1 < n_items) {
-                const int j = item_block(i + 1);
-                scan_load<T>(rb, kq_bg + (size_t)j * T * (D / 2), sc_bg + (size_t)j * D, lane);
-            }
-            store(i, scan_compute<T, G>(ra, qw, p.kappa, ws, lane));
-            if (i + 1 < n_items) {
-                if (i + 2 < n_items) {
-                    const int j = item_block(i + 2);
-                    scan_load<T>(ra, kq_bg + (size_t)j * T * (D / 2), sc_bg + (size_t)j * D, lane);
+            ScanRegs<T> ra, rb;
+            auto load = [&](ScanRegs<T>& r, int k) {
+                const int j = block_of(w + min(k, n_items - 1) * kWaves);
+                scan_load<T>(r, kq_bg + (size_t)j * T * (D / 2), sc_bg + (size_t)j * D, lane);
+            };
+            auto store = [&](int k, float shat) {
+                const int i = w + k * kWaves;
+                if (lane < G) {
+                    if (i < n_pro) sh.pro[i][lane] = shat;
+                    else sh.u.shat[lane][block_of(i) - jb] = shat;
                 }
-                store(i + 1, scan_compute<T, G>(rb, qw, p.kappa, ws, lane));
+            };
+            // the scheduling barriers keep each prefetch issued before the computation that
+            // precedes it in program order (otherwise the scheduler hoists that computation's
+            // first use of the previous buffer above the loads, forcing a full wait)
+            load(ra, 0);
+            for (int k = 0; k < n_items; k += 2) {
+                load(rb, k + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                store(k, scan_compute<T, G>(ra, qw, p.kappa, ws, lane));
+                load(ra, k + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                if (k + 1 < n_items) store(k + 1, scan_compute<T, G>(rb, qw, p.kappa, ws, lane));
             }
         }
         __syncthreads();
@@ -518,8 +559,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p)
         __syncthreads();
         n_kept = sh.n_kept;
     } else {
-        n_kept = je - jb;
+        n_kept = max(je - jb, 0);
+        __syncthreads();  // query rows in LDS
     }
+
+    // the exact stage reads head col % G's query row from LDS
+    const void* qrow = reinterpret_cast<const char*>(sh.q) + (size_t)(col % G) * D * esz;
 
     // exact attention over the kept blocks, 16-token tiles dealt round-robin to the waves
     SoftState<G> st;
@@ -531,40 +576,36 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p)
     st.l = 0.0f;
     {
         const int n_tiles = n_kept * NT;
-        auto tile_of = [&](int it, int& t0, u32& kb) {
-            const int k = it / NT;
-            int off;
-            if constexpr (SPARSE) {
-                off = sh.list[k];
-                kb = sh.kbits[off];
-            } else {
-                off = k;
-                kb = 0xFFu;
-            }
-            t0 = (jb + off) * p.T + (it % NT) * 16;
-        };
-        TileRegs<BF16> ta, tb;
-        int t0a = 0, t0b = 0;
-        u32 kba = 0, kbb = 0;
-        int it = w;
-        if (it < n_tiles) {
-            tile_of(it, t0a, kba);
-            tile_load<BF16>(ta, Kbg, Vbg, t0a, lane);
-        }
-        for (; it < n_tiles; it += 2 * kWaves) {
-            const int it1 = it + kWaves;
-            if (it1 < n_tiles) {
-                tile_of(it1, t0b, kbb);
-                tile_load<BF16>(tb, Kbg, Vbg, t0b, lane);
-            }
-            tile_compute<G, BF16>(ta, qr, st, ws, t0a, p.L, kba, p.c_log2, lane);
-            if (it1 < n_tiles) {
-                const int it2 = it1 + kWaves;
-                if (it2 < n_tiles) {
-                    tile_of(it2, t0a, kba);
-                    tile_load<BF16>(ta, Kbg, Vbg, t0a, lane);
+        const int n_w = n_tiles > w ? (n_tiles - w + kWaves - 1) / kWaves : 0;
+        if (n_w > 0) {
+            auto tile_of = [&](int k, int& t0, u32& kb) {
+                const int it = w + min(k, n_w - 1) * kWaves;
+                const int kk = it / NT;
+                int off;
+                if constexpr (SPARSE) {
+                    off = sh.list[kk];
+                    kb = sh.kbits[off];
+                } else {
+                    off = kk;
+                    kb = 0xFFu;
                 }
-                tile_compute<G, BF16>(tb, qr, st, ws, t0b, p.L, kbb, p.c_log2, lane);
+                t0 = (jb + off) * T + (it % NT) * 16;
+            };
+            TileRegs<BF16> ta, tb;
+            int t0a, t0b;
+            u32 kba, kbb;
+            tile_of(0, t0a, kba);
+            tile_load<BF16>(ta, Kbg, Vbg, t0a, lane);
+            for (int k = 0; k < n_w; k += 2) {
+                tile_of(k + 1, t0b, kbb);
+                tile_load<BF16>(tb, Kbg, Vbg, t0b, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                tile_compute<G, BF16>(ta, qrow, st, ws, t0a, p.L, kba, p.c_log2, lane);
+                tile_of(k + 2, t0a, kba);
+                tile_load<BF16>(ta, Kbg, Vbg, t0a, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                if (k + 1 < n_w)
+                    tile_compute<G, BF16>(tb, qrow, st, ws, t0b, p.L, kbb, p.c_log2, lane);
             }
         }
     }
@@ -580,7 +621,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p)
             st.o[h][c] = x;
         }
 
-    // merge the waves' softmax states, write this split's partial
+    // merge the waves' softmax states into this split's partial
     __syncthreads();  // the shat table is reused as the merge buffer
     if (kg == 0) {
 #pragma unroll
@@ -595,50 +636,104 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p)
         }
     }
     __syncthreads();
+    const size_t rec0 = ((size_t)bg * p.S + split) * G;
+    if (n_kept > 0) {
+        for (int e = threadIdx.x; e < G * D; e += kWaves * 64) {
+            const int h = e / D, c = e % D;
+            float M = kNegInf;
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sh.u.merge.m[v][h]);
+            float o = 0.0f, l = 0.0f;
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v) {
+                const float mv = sh.u.merge.m[v][h];
+                const float sc = (mv == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
+                o = fmaf(sh.u.merge.o[v][h][c], sc, o);
+                l = fmaf(sh.u.merge.l[v][h], sc, l);
+            }
+            st_dev(&p.part_o[(rec0 + h) * D + c], o);
+            if (c == 0) st_dev2(&p.part_ml[rec0 + h], M, l);
+        }
+    } else if (threadIdx.x < G) {
+        st_dev2(&p.part_ml[rec0 + threadIdx.x], kNegInf, 0.0f);
+    }
+
+    // split-KV combine by the last work-group of (b, g) to finish.  Every thread waits until its
+    // device-scope partial stores have completed (s_waitcnt 0) before the barrier; only then does
+    // one thread count this split as done.  The work-group that brings the count to S reads the
+    // partials with device-scope loads, issued after its counter update has returned.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const u32 done = __hip_atomic_fetch_add(&p.counters[bg], 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+        sh.is_last = done == (u32)(p.S - 1);
+    }
+    __syncthreads();
+    if (!sh.is_last) return;
+    if (threadIdx.x == 0)  // ready for the next call
+        __hip_atomic_store(&p.counters[bg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    const size_t base = (size_t)bg * p.S * G;
+    for (int h = w; h < G; h += kWaves) {
+        float M = kNegInf;
+        for (int s = lane; s < p.S; s += 64) M = fmaxf(M, ld_dev2(&p.part_ml[base + (size_t)s * G + h]).x);
+        M = wave_max(M);
+        float Lsum = 0.0f;
+        int cnt = 0;
+        for (int s0 = 0; s0 < p.S; s0 += 64) {
+            const int s = s0 + lane;
+            float wgt = 0.0f, l = 0.0f;
+            if (s < p.S) {
+                const float2 ml = ld_dev2(&p.part_ml[base + (size_t)s * G + h]);
+                if (ml.x != kNegInf && ml.y > 0.0f) {
+                    wgt = __builtin_amdgcn_exp2f(ml.x - M);
+                    l = ml.y;
+                }
+            }
+            Lsum = fmaf(wgt, l, Lsum);
+            const unsigned long long ball = __ballot(wgt > 0.0f);
+            const int pos = __popcll(ball & ((1ull << lane) - 1ull));
+            if (wgt > 0.0f) {
+                sh.u.fin.wgt[h][cnt + pos] = wgt;
+                sh.u.fin.idx[h][cnt + pos] = (uint16_t)s;
+            }
+            cnt += __popcll(ball);
+        }
+        Lsum = wave_sum(Lsum);
+        if (lane == 0) {
+            sh.u.fin.M[h] = M;
+            sh.u.fin.Lsum[h] = Lsum;
+            sh.u.fin.cnt[h] = cnt;
+        }
+    }
+    __syncthreads();
     for (int e = threadIdx.x; e < G * D; e += kWaves * 64) {
         const int h = e / D, c = e % D;
-        float M = kNegInf;
+        const int n = sh.u.fin.cnt[h];
+        float acc = 0.0f;
+        for (int k0 = 0; k0 < n; k0 += 8) {
+            float v[8];
 #pragma unroll
-        for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sh.u.merge.m[v][h]);
-        float o = 0.0f, l = 0.0f;
+            for (int u = 0; u < 8; ++u) {
+                const int s = sh.u.fin.idx[h][min(k0 + u, n - 1)];
+                v[u] = ld_dev(&p.part_o[(base + (size_t)s * G + h) * D + c]);
+            }
 #pragma unroll
-        for (int v = 0; v < kWaves; ++v) {
-            const float mv = sh.u.merge.m[v][h];
-            const float sc = (mv == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
-            o = fmaf(sh.u.merge.o[v][h][c], sc, o);
-            l = fmaf(sh.u.merge.l[v][h], sc, l);
+            for (int u = 0; u < 8; ++u)
+                if (k0 + u < n) acc = fmaf(sh.u.fin.wgt[h][k0 + u], v[u], acc);
         }
-        float* rec = p.part + ((size_t)(h0 + h) * p.S + split) * kPartStride;
-        rec[c] = o;
-        if (c == 0) {
-            rec[D] = M;
-            rec[D + 1] = l;
-        }
+        const float L = sh.u.fin.Lsum[h];
+        p.out[(size_t)(h0 + h) * D + c] = acc / L;
+        if (p.lse && c == 0)
+            p.lse[h0 + h] = (sh.u.fin.M[h] + __log2f(L)) * 0.69314718055994530942f;
     }
 }
 
-// ------------------------------------------------------------------------------------------
-// Split-KV combine: one work-group of 128 threads (one per channel) per (b, query head).
-// ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ part,
-                                                      float* __restrict__ out,
-                                                      float* __restrict__ lse, int S)
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ p, int n)
 {
-    const int row = blockIdx.x;
-    const int c = threadIdx.x;
-    const float* rec = part + (size_t)row * S * kPartStride;
-    float M = kNegInf;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, rec[(size_t)s * kPartStride + D]);
-    float o = 0.0f, l = 0.0f;
-    for (int s = 0; s < S; ++s) {
-        const float* r = rec + (size_t)s * kPartStride;
-        const float ms = r[D];
-        const float sc = (ms == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-        o = fmaf(r[c], sc, o);
-        l = fmaf(r[D + 1], sc, l);
-    }
-    out[(size_t)row * D + c] = o / l;
-    if (lse && c == 0) lse[row] = (M + __log2f(l)) * 0.69314718055994530942f;
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -690,10 +785,6 @@ hipError_t launch_decode_t(const DecodeParams& p, bool sparse, hipStream_t strea
         hipLaunchKernelGGL((decode_kernel<T, G, BF16, true>), grid, block, 0, stream, p);
     else
         hipLaunchKernelGGL((decode_kernel<T, G, BF16, false>), grid, block, 0, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(combine_kernel, dim3(p.B * p.Hq), dim3(D), 0, stream, p.part, p.out, p.lse,
-                       p.S);
     return hipGetLastError();
 }
 
@@ -720,6 +811,13 @@ hipError_t launch_decode(const DecodeParams& p, bool bf16, bool sparse, hipStrea
         return bf16 ? launch_decode_g<128, true>(p, sparse, stream)
                     : launch_decode_g<128, false>(p, sparse, stream);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_zero_counters(uint32_t* counters, int n, hipStream_t stream)
+{
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, counters, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_quantize(const QuantParams& p, bool bf16, hipStream_t stream)

@@ -6,7 +6,7 @@ through ctypes, and raises on a non-OK status.  There is no fallback: if the lib
 or cannot be loaded, every call raises.
 
 Names follow the C ABI: ``quantize_k_append``, ``decode_sparse``, ``decode_dense``,
-``workspace_bytes``, ``num_splits``.
+``workspace_bytes``, ``workspace_init``, ``num_splits``.
 """
 from __future__ import annotations
 
@@ -52,6 +52,8 @@ def lib():
         L.ffd_status_string.restype = ctypes.c_char_p
         L.ffd_workspace_bytes.argtypes = [D, i32]
         L.ffd_workspace_bytes.restype = sz
+        L.ffd_workspace_init.argtypes = [D, i32, P, sz, P]
+        L.ffd_workspace_init.restype = i32
         L.ffd_num_splits.argtypes = [D, i32, i32]
         L.ffd_num_splits.restype = i32
         L.ffd_quantize_k_append.argtypes = [D, P, i32, i32, i32, P, P, P]
@@ -131,11 +133,21 @@ def num_splits(dims: Dims, block: int, sparse: bool = True) -> int:
     return int(lib().ffd_num_splits(ctypes.byref(dims), block, 1 if sparse else 0))
 
 
+def workspace_init(dims: Dims, block: int, workspace: torch.Tensor, stream=None) -> None:
+    """Prepare a workspace (zero its counters) on the current stream."""
+    _need(workspace, "workspace", torch.uint8)
+    _check(lib().ffd_workspace_init(ctypes.byref(dims), block, _ptr(workspace),
+                                    workspace.numel(), _stream(stream)))
+
+
 def alloc_workspace(dims: Dims, block: int, device) -> torch.Tensor:
+    """A prepared workspace for decode calls with these dims and block."""
     n = workspace_bytes(dims, block)
     if n == 0:
         raise FFDError(FFD_ERR_INVALID_ARG, "invalid dims for workspace")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    workspace_init(dims, block, ws)
+    return ws
 
 
 def alloc_kq(K: torch.Tensor, block: int):

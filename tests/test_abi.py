@@ -32,7 +32,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"ffd_quantize_k_append", "ffd_decode_sparse", "ffd_decode_dense",
-            "ffd_workspace_bytes", "ffd_status_string", "ffd_abi_version"} <= set(names)
+            "ffd_workspace_bytes", "ffd_workspace_init", "ffd_status_string",
+            "ffd_abi_version"} <= set(names)
     nm = subprocess.run(["nm", "-D", "--defined-only", str(ffd.LIB_PATH)], capture_output=True,
                         text=True, check=True).stdout
     exported = set(re.findall(r"\bT (ffd_\w+)", nm))
@@ -64,7 +65,9 @@ def test_workspace_and_splits(L):
     d = dims()
     S = ffd.num_splits(d, 64)
     assert S >= 1
-    assert ffd.workspace_bytes(d, 64) == 1 * 32 * S * (128 + 4) * 4
+    rec = 1 * 8 * S * 4                       # (b, kv head, split, query head of the group)
+    r256 = lambda x: -(-x // 256) * 256
+    assert ffd.workspace_bytes(d, 64) == r256(8 * 4) + r256(rec * 8) + rec * 128 * 4
     big = dims(B=8, seq_len=131072, seq_cap=131072)
     S = ffd.num_splits(big, 64)
     assert -(-2048 // S) <= 256
@@ -114,6 +117,22 @@ def test_quantize_validation(L):
     # ranges that complete no block launch nothing and succeed
     assert q(ctypes.byref(d), A, 0, 63, 64, A, A, None) == ffd.FFD_OK
     assert q(ctypes.byref(d), A, 64, 127, 64, A, A, None) == ffd.FFD_OK
+
+
+def test_workspace_init_validation(L):
+    d = dims()
+    n = ffd.workspace_bytes(d, 64)
+    wi = L.ffd_workspace_init
+    assert wi(ctypes.byref(d), 64, None, n, None) == ffd.FFD_ERR_WORKSPACE
+    assert wi(ctypes.byref(d), 64, MISALIGNED, n, None) == ffd.FFD_ERR_WORKSPACE
+    assert wi(ctypes.byref(d), 64, A, n - 1, None) == ffd.FFD_ERR_WORKSPACE
+    assert wi(ctypes.byref(d), 96, A, n, None) == ffd.FFD_ERR_UNSUPPORTED
+    assert wi(ctypes.byref(dims(B=0)), 64, None, 0, None) == ffd.FFD_OK
+
+
+def test_too_many_blocks_unsupported(L):
+    d = dims(seq_len=256 * 256 * 64 + 1, seq_cap=256 * 256 * 64 + 64)
+    assert sparse_call(L, d) == ffd.FFD_ERR_UNSUPPORTED
 
 
 def test_empty_batch_is_a_noop(L):

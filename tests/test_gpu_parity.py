@@ -201,3 +201,52 @@ def test_errors_launch_nothing(mid_case):
     with pytest.raises(ffd.FFDError) as e:
         ffd.decode_dense(qd, Kd, Vd, 96, w.L)
     assert e.value.status in (ffd.FFD_ERR_UNSUPPORTED, ffd.FFD_ERR_INVALID_ARG)
+
+
+def test_workspace_reuse_across_calls(mid_case):
+    """One workspace serves many calls: each call returns its counters to zero."""
+    w, _, (qd, Kd, Vd, Kq_d, sc_d) = mid_case
+    dims = ffd.dims_of(qd, Kd, w.L)
+    ws = ffd.alloc_workspace(dims, w.T, qd.device)
+    ref_s = ffd.decode_sparse(qd, Kd, Vd, Kq_d, sc_d, 5.0, w.T, w.L)
+    ref_d = ffd.decode_dense(qd, Kd, Vd, w.T, w.L)
+    for i in range(6):
+        if i % 2 == 0:
+            o, l = ffd.decode_sparse(qd, Kd, Vd, Kq_d, sc_d, 5.0, w.T, w.L, workspace=ws)
+            r = ref_s
+        else:
+            o, l = ffd.decode_dense(qd, Kd, Vd, w.T, w.L, workspace=ws)
+            r = ref_d
+        torch.cuda.synchronize()
+        assert torch.equal(o, r[0]) and torch.equal(l, r[1]), f"call {i} differs"
+
+
+def test_graph_replay_matches_eager(mid_case):
+    """The decode calls can be recorded into a HIP graph; every replay equals the eager result."""
+    w, _, (qd, Kd, Vd, Kq_d, sc_d) = mid_case
+    dims = ffd.dims_of(qd, Kd, w.L)
+    ws = ffd.alloc_workspace(dims, w.T, qd.device)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=DEV)
+    ref = ffd.decode_sparse(qd, Kd, Vd, Kq_d, sc_d, 5.0, w.T, w.L)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ffd.decode_sparse(qd, Kd, Vd, Kq_d, sc_d, 5.0, w.T, w.L, out=out, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ffd.decode_sparse(qd, Kd, Vd, Kq_d, sc_d, 5.0, w.T, w.L, out=out, lse=lse, workspace=ws)
+        ffd.decode_sparse(qd, Kd, Vd, Kq_d, sc_d, 5.0, w.T, w.L, out=out, lse=lse, workspace=ws)
+    for i in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), f"replay {i} differs"
+        # eager work between replays on the same workspace
+        ffd.decode_dense(qd, Kd, Vd, w.T, w.L, workspace=ws)
+        torch.cuda.synchronize()
