@@ -48,8 +48,9 @@ int splits_for(const ffd_dims* d, int32_t block)
         s = atoi(env);
         if (s > n_blocks) s = n_blocks;
     } else {
-        // enough work-groups to fill 256 CUs a few times over, at least two blocks per wave
-        const int64_t target_wgs = 768;  // 3 resident work-groups on each of 256 CUs
+        // one work-group per CU: fewer, longer streams measured faster than more resident
+        // work-groups at every occupancy tried
+        const int64_t target_wgs = 256;
         s = bh > 0 ? (target_wgs + bh - 1) / bh : 1;
         const int64_t max_s = n_blocks / (2 * kWaves) > 0 ? n_blocks / (2 * kWaves) : 1;
         if (s > max_s) s = max_s;
@@ -60,7 +61,7 @@ int splits_for(const ffd_dims* d, int32_t block)
     return (int)s;
 }
 
-// Workspace layout: counters [B*Hkv] u32 | ml [B*Hkv*S*G] float2 | o [B*Hkv*S*G*d] fp32,
+// Workspace layout: counters [B*Hkv] u64 | ml [B*Hkv*S*G] float2 | o [B*Hkv*S*G*d] fp32,
 // each region starting on a 256-byte boundary.
 struct WsLayout {
     size_t off_ml, off_o, total;
@@ -73,7 +74,7 @@ WsLayout ws_layout(const ffd_dims* d, int S)
     const size_t bh = (size_t)d->batch * d->n_kv_heads;
     const size_t rec = bh * (size_t)S * (size_t)(d->n_q_heads / d->n_kv_heads);
     WsLayout w;
-    w.off_ml = round256(bh * sizeof(uint32_t));
+    w.off_ml = round256(bh * sizeof(unsigned long long));
     w.off_o = w.off_ml + round256(rec * 2 * sizeof(float));
     w.total = w.off_o + rec * kHeadDim * sizeof(float);
     return w;
@@ -112,7 +113,7 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
     p.lse = lse;
     p.keep_mask = keep_mask;
     char* wsb = static_cast<char*>(workspace);
-    p.counters = reinterpret_cast<uint32_t*>(wsb);
+    p.counters = reinterpret_cast<unsigned long long*>(wsb);
     p.part_ml = reinterpret_cast<float2*>(wsb + lay.off_ml);
     p.part_o = reinterpret_cast<float*>(wsb + lay.off_o);
     p.B = dims->batch;
@@ -165,7 +166,7 @@ ffd_status ffd_workspace_init(const ffd_dims* dims, int32_t block, void* workspa
     if (!workspace || !aligned16(workspace)) return FFD_ERR_WORKSPACE;
     if (workspace_bytes < ws_layout(dims, splits_for(dims, block)).total) return FFD_ERR_WORKSPACE;
     return finish(ffd::launch_zero_counters(static_cast<uint32_t*>(workspace),
-                                            dims->batch * dims->n_kv_heads, stream));
+                                            2 * dims->batch * dims->n_kv_heads, stream));
 }
 
 int32_t ffd_num_splits(const ffd_dims* dims, int32_t block, int32_t sparse)

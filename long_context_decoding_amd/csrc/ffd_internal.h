@@ -23,7 +23,9 @@ struct DecodeParams {
     float* out;
     float* lse;
     uint8_t* keep_mask;
-    uint32_t* counters;  // [B*Hkv] finished splits of each (b, kv head); zero between calls
+    unsigned long long* counters;  // [B*Hkv] finished splits (high half) and, for S <= 32, a
+                                   // mask of the splits with a partial (low half); zero between
+                                   // calls
     float2* part_ml;     // [B*Hkv][S][G] per-split (max in log2 units, sum of exp2)
     float* part_o;       // [B*Hkv][S][G][d] per-split unnormalized output
     int B, Hq, Hkv, G;

@@ -348,7 +348,6 @@ template <int G>
 struct __attribute__((aligned(16))) DecodeShared {
     WaveScratch<G> wave[kWaves];
     union {
-        float shat[G][kMaxBlocksPerSplit];                 // scan results of the split's blocks
         struct {                                            // the waves' softmax states
             float o[kWaves][G][D];
             float m[kWaves][G];
@@ -362,11 +361,10 @@ struct __attribute__((aligned(16))) DecodeShared {
         } fin;
     } u;
     float4 q[G * D / 4];                   // the group's query rows (bf16 or fp32 bytes)
-    float pro[2][G];                       // estimates of the sink and local blocks
     uint8_t kbits[kMaxBlocksPerSplit];     // per-block head mask (bit h = query head h of group)
-    uint16_t list[kMaxBlocksPerSplit];     // kept blocks (offsets in the split)
-    int n_kept;
+    uint8_t list[kWaves][kMaxBlocksPerSplit];  // kept blocks (offsets in the split), per wave
     int is_last;
+    u32 mask;                              // non-empty splits (when S <= 32)
 };
 
 __device__ __forceinline__ float wave_max(float x)
@@ -422,7 +420,7 @@ __device__ __forceinline__ float2 ld_dev2(const float2* p)
 //   5. the last work-group of (b, g) to finish (atomic counter) merges the splits' partials
 //      with the log-sum-exp rule into out and lse, and resets the counter.
 template <int T, int G, bool BF16, bool SPARSE>
-__global__ __launch_bounds__(kWaves * 64, (BF16 && G <= 4) ? 3 : 2) void decode_kernel(DecodeParams p)
+__global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
 {
     __shared__ DecodeShared<G> sh;
     const int lane = threadIdx.x & 63;
@@ -452,13 +450,16 @@ __global__ __launch_bounds__(kWaves * 64, (BF16 && G <= 4) ? 3 : 2) void decode_
     constexpr int NT = T / 16;
     int n_kept;
 
-    // copy the group's G query rows to LDS (16 bytes per thread)
-    {
-        const float4* qsrc = reinterpret_cast<const float4*>(
-            static_cast<const char*>(p.q) + (size_t)h0 * D * esz);
-        const int n16 = (int)(G * D * esz / 16);
-        for (int i = threadIdx.x; i < n16; i += kWaves * 64) sh.q[i] = qsrc[i];
-    }
+    // the group's G query rows (at most 16 bytes per thread), copied to LDS once the first scan
+    // loads are in flight; the load is unconditional (clamped index) so that it is issued
+    // before them and the copy waits only for itself
+    constexpr int kQ16 = (int)(G * D * (BF16 ? 2 : 4) / 16);
+    static_assert(kQ16 <= kWaves * 64, "query rows exceed one 16-byte load per thread");
+    const float4 qcopy = reinterpret_cast<const float4*>(
+        static_cast<const char*>(p.q) + (size_t)h0 * D * esz)[min((int)threadIdx.x, kQ16 - 1)];
+    auto publish_q = [&]() {
+        if ((int)threadIdx.x < kQ16) sh.q[threadIdx.x] = qcopy;
+    };
 
     if constexpr (SPARSE) {
         constexpr int HPL = (G + 3) / 4;
@@ -486,87 +487,109 @@ __global__ __launch_bounds__(kWaves * 64, (BF16 && G <= 4) ? 3 : 2) void decode_
         const uint8_t* kq_bg = p.Kq + (size_t)bg * p.cap * (D / 2);
         const float* sc_bg = p.scales + (size_t)bg * (p.cap / T) * D;
         const int nf = p.n_full;
-        // scan items of the split: [sink, local] (pseudo-max), then the full blocks j_lo..j_hi-1
-        // that are neither; item i goes to wave i % kWaves
+        const u32 all_heads = (1u << G) - 1u;
+        // Forced blocks of the split (sink 0, the local block nf-1 and a partial tail) are kept
+        // for every head; every other block of the split is a scan item of exactly one wave.
+        if (w == 0) {
+            for (int t = lane; t < je - jb; t += 64) {
+                const int j = jb + t;
+                if (j == 0 || j >= nf - 1) {
+                    sh.kbits[t] = (uint8_t)all_heads;
+                    if (p.keep_mask)
+#pragma unroll
+                        for (int h = 0; h < G; ++h) p.keep_mask[(size_t)(h0 + h) * p.n_blocks + j] = 1;
+                }
+            }
+        }
+        // Scan items of this wave: the sink and local blocks (each wave forms the pseudo-max of
+        // Eq. 3 itself, so that it can apply Eq. 1 to its own blocks at once), then the split's
+        // non-forced full blocks j_lo + w, j_lo + w + kWaves, ...
         const int n_pro = nf >= 1 ? 2 : 0;
         const int j_lo = max(jb, 1);
         const int j_hi = min(je, nf - 1);
-        const int n_all = n_pro + max(j_hi - j_lo, 0);
-        const int n_items = n_all > w ? (n_all - w + kWaves - 1) / kWaves : 0;
-        auto block_of = [&](int i) -> int {
-            if (i < n_pro) return i == 0 ? 0 : nf - 1;
-            return j_lo + (i - n_pro);
+        const int n_main = max(j_hi - j_lo, 0);
+        const int n_items = n_pro + (n_main > w ? (n_main - w + kWaves - 1) / kWaves : 0);
+        auto block_of = [&](int k) -> int {
+            if (k < n_pro) return k == 0 ? 0 : nf - 1;
+            return j_lo + w + (k - n_pro) * kWaves;
         };
         if (n_items > 0) {
-            ScanRegs<T> ra, rb;
+            float pro0 = 0.0f, theta = 0.0f;  // lanes < G: head = lane
             auto load = [&](ScanRegs<T>& r, int k) {
-                const int j = block_of(w + min(k, n_items - 1) * kWaves);
+                const int j = block_of(k);
                 scan_load<T>(r, kq_bg + (size_t)j * T * (D / 2), sc_bg + (size_t)j * D, lane);
             };
-            auto store = [&](int k, float shat) {
-                const int i = w + k * kWaves;
-                if (lane < G) {
-                    if (i < n_pro) sh.pro[i][lane] = shat;
-                    else sh.u.shat[lane][block_of(i) - jb] = shat;
+            auto process = [&](const ScanRegs<T>& r, int k) {
+                const float shat = scan_compute<T, G>(r, qw, p.kappa, ws, lane);
+                if (k == 0) {
+                    pro0 = shat;
+                } else if (k == 1) {
+                    theta = __fsub_rn(fmaxf(pro0, shat), p.delta);
+                } else {
+                    // selection, Eq. 1 with the pseudo-max: shat >= mtilde - delta
+                    const int j = block_of(k);
+                    const bool keep = lane < G && shat >= theta;
+                    const u32 bits = (u32)__ballot(keep) & all_heads;
+                    if (lane == 0) sh.kbits[j - jb] = (uint8_t)bits;
+                    if (p.keep_mask && lane < G)
+                        p.keep_mask[(size_t)(h0 + lane) * p.n_blocks + j] = keep ? 1 : 0;
                 }
             };
-            // the scheduling barriers keep each prefetch issued before the computation that
-            // precedes it in program order (otherwise the scheduler hoists that computation's
-            // first use of the previous buffer above the loads, forcing a full wait)
+            // Two items in flight: item k + 1 is loaded while item k is computed.  The steady
+            // loop issues loads only for items that exist and the epilogue issues none past the
+            // end, so no load is left outstanding.  The scheduling barriers keep each prefetch
+            // issued before the computation that follows it in program order (otherwise the
+            // scheduler hoists that computation's first use of its buffer above the loads, and
+            // the in-order wait counter then waits for the prefetch too).
+            ScanRegs<T> ra, rb;
             load(ra, 0);
-            for (int k = 0; k < n_items; k += 2) {
+            __builtin_amdgcn_sched_barrier(0);
+            publish_q();
+            int k = 0;
+            for (; k + 2 < n_items; k += 2) {
                 load(rb, k + 1);
                 __builtin_amdgcn_sched_barrier(0);
-                store(k, scan_compute<T, G>(ra, qw, p.kappa, ws, lane));
+                process(ra, k);
                 load(ra, k + 2);
                 __builtin_amdgcn_sched_barrier(0);
-                if (k + 1 < n_items) store(k + 1, scan_compute<T, G>(rb, qw, p.kappa, ws, lane));
+                process(rb, k + 1);
             }
+            if (k + 1 < n_items) {
+                load(rb, k + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                process(ra, k);
+                process(rb, k + 1);
+            } else {
+                process(ra, k);
+            }
+        } else {
+            publish_q();
         }
-        __syncthreads();
+        __syncthreads();  // kbits complete, query rows in LDS
 
-        // selection (Eq. 1 with the Eq. 3 pseudo-max) and compaction of the kept blocks
-        if (w == 0) {
-            float theta[G];
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float mt = nf >= 1 ? fmaxf(sh.pro[0][h], sh.pro[1][h]) : 0.0f;
-                theta[h] = __fsub_rn(mt, p.delta);
-            }
-            int n = 0;
-            for (int base = 0; base < je - jb; base += 64) {
-                const int t = base + lane;
-                const int j = jb + t;
-                u32 bits = 0;
-                if (j < je) {
-                    const bool forced = (j == 0) || (j >= nf - 1);
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        const bool keep = forced || (sh.u.shat[h][t] >= theta[h]);
-                        bits |= (u32)keep << h;
-                        if (p.keep_mask)
-                            p.keep_mask[(size_t)(h0 + h) * p.n_blocks + j] = keep ? 1 : 0;
-                    }
-                    sh.kbits[t] = (uint8_t)bits;
-                }
-                const unsigned long long ball = __ballot(bits != 0);
-                const int pos = __popcll(ball & ((1ull << lane) - 1ull));
-                if (bits != 0) sh.list[n + pos] = (uint16_t)t;
-                n += __popcll(ball);
-            }
-            if (lane == 0) sh.n_kept = n;
+        // every wave compacts the kept blocks of the split, in increasing order, into its own
+        // list (identical in all waves)
+        int n = 0;
+        for (int base = 0; base < je - jb; base += 64) {
+            const int t = base + lane;
+            const u32 bits = t < je - jb ? sh.kbits[t] : 0u;
+            const unsigned long long ball = __ballot(bits != 0);
+            const int pos = __popcll(ball & ((1ull << lane) - 1ull));
+            if (bits != 0) sh.list[w][n + pos] = (uint8_t)t;
+            n += __popcll(ball);
         }
-        __syncthreads();
-        n_kept = sh.n_kept;
+        n_kept = n;
     } else {
         n_kept = max(je - jb, 0);
+        publish_q();
         __syncthreads();  // query rows in LDS
     }
 
     // the exact stage reads head col % G's query row from LDS
     const void* qrow = reinterpret_cast<const char*>(sh.q) + (size_t)(col % G) * D * esz;
 
-    // exact attention over the kept blocks, 16-token tiles dealt round-robin to the waves
+    // exact attention over the kept blocks, 16-token tiles dealt round-robin to the waves,
+    // pipelined like the scan (two tiles in flight, no load past the last tile)
     SoftState<G> st;
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -579,11 +602,11 @@ __global__ __launch_bounds__(kWaves * 64, (BF16 && G <= 4) ? 3 : 2) void decode_
         const int n_w = n_tiles > w ? (n_tiles - w + kWaves - 1) / kWaves : 0;
         if (n_w > 0) {
             auto tile_of = [&](int k, int& t0, u32& kb) {
-                const int it = w + min(k, n_w - 1) * kWaves;
+                const int it = w + k * kWaves;
                 const int kk = it / NT;
                 int off;
                 if constexpr (SPARSE) {
-                    off = sh.list[kk];
+                    off = sh.list[w][kk];
                     kb = sh.kbits[off];
                 } else {
                     off = kk;
@@ -596,7 +619,8 @@ __global__ __launch_bounds__(kWaves * 64, (BF16 && G <= 4) ? 3 : 2) void decode_
             u32 kba, kbb;
             tile_of(0, t0a, kba);
             tile_load<BF16>(ta, Kbg, Vbg, t0a, lane);
-            for (int k = 0; k < n_w; k += 2) {
+            int k = 0;
+            for (; k + 2 < n_w; k += 2) {
                 tile_of(k + 1, t0b, kbb);
                 tile_load<BF16>(tb, Kbg, Vbg, t0b, lane);
                 __builtin_amdgcn_sched_barrier(0);
@@ -604,8 +628,16 @@ __global__ __launch_bounds__(kWaves * 64, (BF16 && G <= 4) ? 3 : 2) void decode_
                 tile_of(k + 2, t0a, kba);
                 tile_load<BF16>(ta, Kbg, Vbg, t0a, lane);
                 __builtin_amdgcn_sched_barrier(0);
-                if (k + 1 < n_w)
-                    tile_compute<G, BF16>(tb, qrow, st, ws, t0b, p.L, kbb, p.c_log2, lane);
+                tile_compute<G, BF16>(tb, qrow, st, ws, t0b, p.L, kbb, p.c_log2, lane);
+            }
+            if (k + 1 < n_w) {
+                tile_of(k + 1, t0b, kbb);
+                tile_load<BF16>(tb, Kbg, Vbg, t0b, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                tile_compute<G, BF16>(ta, qrow, st, ws, t0a, p.L, kba, p.c_log2, lane);
+                tile_compute<G, BF16>(tb, qrow, st, ws, t0b, p.L, kbb, p.c_log2, lane);
+            } else {
+                tile_compute<G, BF16>(ta, qrow, st, ws, t0a, p.L, kba, p.c_log2, lane);
             }
         }
     }
@@ -637,6 +669,7 @@ __global__ __launch_bounds__(kWaves * 64, (BF16 && G <= 4) ? 3 : 2) void decode_
     }
     __syncthreads();
     const size_t rec0 = ((size_t)bg * p.S + split) * G;
+    const bool fast = p.S <= 32;  // the counter word can carry a mask of the non-empty splits
     if (n_kept > 0) {
         for (int e = threadIdx.x; e < G * D; e += kWaves * 64) {
             const int h = e / D, c = e % D;
@@ -654,30 +687,115 @@ __global__ __launch_bounds__(kWaves * 64, (BF16 && G <= 4) ? 3 : 2) void decode_
             st_dev(&p.part_o[(rec0 + h) * D + c], o);
             if (c == 0) st_dev2(&p.part_ml[rec0 + h], M, l);
         }
-    } else if (threadIdx.x < G) {
+    } else if (!fast && threadIdx.x < G) {
         st_dev2(&p.part_ml[rec0 + threadIdx.x], kNegInf, 0.0f);
     }
 
     // split-KV combine by the last work-group of (b, g) to finish.  Every thread waits until its
     // device-scope partial stores have completed (s_waitcnt 0) before the barrier; only then does
-    // one thread count this split as done.  The work-group that brings the count to S reads the
-    // partials with device-scope loads, issued after its counter update has returned.
+    // one thread count this split as done.  The counter word holds the number of finished
+    // splits in its high half and, when S <= 32, a bit per split that wrote a partial in its low
+    // half (each split adds its bit once, so no carry).  The work-group that brings the count to
+    // S reads the partials with device-scope loads, issued after its counter update returned.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
-        const u32 done = __hip_atomic_fetch_add(&p.counters[bg], 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-        sh.is_last = done == (u32)(p.S - 1);
+        const unsigned long long add =
+            (1ull << 32) | ((fast && n_kept > 0) ? (1ull << split) : 0ull);
+        const unsigned long long old = __hip_atomic_fetch_add(
+            &p.counters[bg], add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sh.is_last = (u32)(old >> 32) == (u32)(p.S - 1);
+        sh.mask = (u32)(old | add);
     }
     __syncthreads();
     if (!sh.is_last) return;
     if (threadIdx.x == 0)  // ready for the next call
-        __hip_atomic_store(&p.counters[bg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.counters[bg], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     const size_t base = (size_t)bg * p.S * G;
+    if (fast) {
+        // Non-empty splits in increasing order, read from the (wave-uniform) mask with scalar
+        // bit operations; their (m, l) and o in one round of loads for every output of this
+        // thread; then the log-sum-exp merge in split order: max, weights, weighted sums.
+        constexpr int NE = (G * D + kWaves * 64 - 1) / (kWaves * 64);
+        constexpr int kMB = NE >= 4 ? 8 : 16;
+        u32 mrest = __builtin_amdgcn_readfirstlane(sh.mask);
+        float M[NE], L[NE], acc[NE];
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            M[i] = kNegInf;
+            L[i] = 0.0f;
+            acc[i] = 0.0f;
+        }
+        while (mrest != 0u) {
+            int sidx[kMB];
+            int nb = 0;
+#pragma unroll
+            for (int u = 0; u < kMB; ++u) {
+                const int s = mrest ? __builtin_ctz(mrest) : -1;
+                if (mrest) {
+                    mrest &= mrest - 1u;
+                    ++nb;
+                }
+                sidx[u] = s < 0 ? (u > 0 ? sidx[u - 1] : 0) : s;
+            }
+            float2 ml[NE][kMB];
+            float v[NE][kMB];
+#pragma unroll
+            for (int i = 0; i < NE; ++i) {
+                const int e = min((int)threadIdx.x + i * kWaves * 64, G * D - 1);
+                const int h = e / D, c = e % D;
+#pragma unroll
+                for (int u = 0; u < kMB; ++u) {
+                    if (u < nb) {
+                        const size_t r = base + (size_t)sidx[u] * G + h;
+                        ml[i][u] = ld_dev2(&p.part_ml[r]);
+                        v[i][u] = ld_dev(&p.part_o[r * D + c]);
+                    } else {
+                        ml[i][u] = make_float2(kNegInf, 0.0f);
+                        v[i][u] = 0.0f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NE; ++i) {
+                // a head may have kept nothing in a split that another head used (m = -inf)
+                float Mb = M[i];
+#pragma unroll
+                for (int u = 0; u < kMB; ++u)
+                    if (ml[i][u].y > 0.0f) Mb = fmaxf(Mb, ml[i][u].x);
+                const float a = (M[i] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(M[i] - Mb);
+                float sa = acc[i] * a, sl = L[i] * a;
+#pragma unroll
+                for (int u = 0; u < kMB; ++u) {
+                    const float wgt =
+                        ml[i][u].y > 0.0f ? __builtin_amdgcn_exp2f(ml[i][u].x - Mb) : 0.0f;
+                    sa = fmaf(v[i][u], wgt, sa);
+                    sl = fmaf(ml[i][u].y, wgt, sl);
+                }
+                M[i] = Mb;
+                acc[i] = sa;
+                L[i] = sl;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const int e = (int)threadIdx.x + i * kWaves * 64;
+            if (e < G * D) {
+                const int h = e / D, c = e % D;
+                p.out[(size_t)(h0 + h) * D + c] = acc[i] / L[i];
+                if (p.lse && c == 0)
+                    p.lse[h0 + h] = (M[i] + __log2f(L[i])) * 0.69314718055994530942f;
+            }
+        }
+        return;
+    }
+
+    // general path: (m, l) of every split first, then o of the non-empty ones
     for (int h = w; h < G; h += kWaves) {
         float M = kNegInf;
-        for (int s = lane; s < p.S; s += 64) M = fmaxf(M, ld_dev2(&p.part_ml[base + (size_t)s * G + h]).x);
+        for (int s = lane; s < p.S; s += 64)
+            M = fmaxf(M, ld_dev2(&p.part_ml[base + (size_t)s * G + h]).x);
         M = wave_max(M);
         float Lsum = 0.0f;
         int cnt = 0;

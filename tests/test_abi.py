@@ -67,7 +67,7 @@ def test_workspace_and_splits(L):
     assert S >= 1
     rec = 1 * 8 * S * 4                       # (b, kv head, split, query head of the group)
     r256 = lambda x: -(-x // 256) * 256
-    assert ffd.workspace_bytes(d, 64) == r256(8 * 4) + r256(rec * 8) + rec * 128 * 4
+    assert ffd.workspace_bytes(d, 64) == r256(8 * 8) + r256(rec * 8) + rec * 128 * 4
     big = dims(B=8, seq_len=131072, seq_cap=131072)
     S = ffd.num_splits(big, 64)
     assert -(-2048 // S) <= 256
