@@ -250,3 +250,69 @@ def test_graph_replay_matches_eager(mid_case):
         # eager work between replays on the same workspace
         ffd.decode_dense(qd, Kd, Vd, w.T, w.L, workspace=ws)
         torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------------------------
+# Edge cases: no full block, spare cache capacity, the largest supported block count
+# --------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dt,T,L", [("bf16", 64, 17), ("bf16", 128, 127), ("f32", 64, 1)])
+def test_no_full_block_keeps_everything(dt, T, L):
+    w = W.small(f"short_{dt}_{T}_{L}", B=2, Hq=8, Hkv=2, L=L, T=T, dtype=dt, seed=L + T)
+    q, K, V, _ = W.make_inputs(w)
+    log(f"[gpu] {w.name}")
+    qd, Kd, Vd = upload(w, q, K, V)
+    Kq_d, sc_d = gpu_quantize(w, Kd)
+    Kq, sc = oracle.quantize_k(K, w.T, 0, w.L)
+    out, lse, keep = gpu_sparse(w, qd, Kd, Vd, Kq_d, sc_d, 0.0)
+    ref = oracle.decode(q, K, V, w.L, w.T, delta=0.0, Kq=Kq, scales=sc)
+    assert keep.all()
+    np.testing.assert_array_equal(keep, ref["keep"])
+    assert_close(out, ref["out"], TOL[dt], "out")
+    assert_close(lse, ref["lse"], TOL[dt], "lse")
+
+
+@pytest.mark.parametrize("T", [64, 128])
+def test_spare_capacity_rows_are_ignored(T):
+    """seq_cap well beyond L: the padding rows (NaN in the inputs) never reach the outputs."""
+    L = 9 * T + 5
+    w = W.small(f"cap_{T}", B=1, Hq=8, Hkv=2, L=L, T=T, seed=33, L_cap=16 * T)
+    q, K, V, _ = W.make_inputs(w)
+    log(f"[gpu] {w.name} cap={w.cap}")
+    qd, Kd, Vd = upload(w, q, K, V)
+    Kq_d, sc_d = gpu_quantize(w, Kd)
+    Kq, sc = oracle.quantize_k(K, w.T, 0, w.L)
+    np.testing.assert_array_equal(Kq_d.cpu().numpy()[:, :, :w.n_full * T], Kq[:, :, :w.n_full * T])
+    for delta in (2.0, INF):
+        out, lse, keep = gpu_sparse(w, qd, Kd, Vd, Kq_d, sc_d, delta)
+        ref = oracle.decode(q, K, V, w.L, w.T, delta=delta, Kq=Kq, scales=sc)
+        np.testing.assert_array_equal(keep, ref["keep"])
+        assert_close(out, ref["out"], 2e-3, f"out delta={delta}")
+        assert_close(lse, ref["lse"], 2e-3, f"lse delta={delta}")
+    out, lse = gpu_dense(w, qd, Kd, Vd)
+    ref = oracle.decode(q, K, V, w.L, w.T, sparse=False)
+    assert_close(out, ref["out"], 2e-3, "dense out")
+
+
+def test_largest_block_count():
+    """65536 blocks of 64 tokens (4M tokens, the most one call supports): 256 splits, so the
+    merge takes its general path; masks compared for the head, outputs against the oracle."""
+    w = W.Workload("max_blocks", B=1, Hq=2, Hkv=1, L=256 * 256 * 64, T=64, plant="needles",
+                   n_needles=40, needle_a=6.0, sink_a=10.0, seed=77)
+    log(f"[gpu] {w.name}: generating {w.L} tokens")
+    q, K, V, _ = W.make_inputs(w)
+    qd, Kd, Vd = upload(w, q, K, V)
+    Kq_d, sc_d = gpu_quantize(w, Kd)
+    dims = ffd.dims_of(qd, Kd, w.L)
+    assert ffd.num_splits(dims, w.T) == 256
+    log(f"[gpu] {w.name}: sparse")
+    out, lse, keep = gpu_sparse(w, qd, Kd, Vd, Kq_d, sc_d, 5.0)
+    Kq, sc = oracle.quantize_k(K, w.T, 0, w.L)
+    np.testing.assert_array_equal(Kq_d.cpu().numpy(), Kq)
+    ref_keep = oracle_masks(w, q, Kq, sc, 5.0)
+    np.testing.assert_array_equal(keep, ref_keep)
+    ref = oracle_attend(w, q, K, V, [(0, 0), (0, 1)], keep=ref_keep)
+    for h in range(2):
+        assert_close(out[0, h], ref[(0, h)][0], 2e-3, f"out h={h}")
+        assert_close(lse[0, h], ref[(0, h)][1], 2e-3, f"lse h={h}")
+    del qd, Kd, Vd, Kq_d, sc_d
+    torch.cuda.empty_cache()
