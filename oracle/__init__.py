@@ -71,6 +71,19 @@ def _load():
     lib.ffdo_decode.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, f32, i32,
                                 P, P, P, P, P, i32]
     lib.ffdo_decode.restype = i32
+    lib.ffdo_quantize_residual.argtypes = [P, i32, P, P]
+    lib.ffdo_quantize_residual.restype = None
+    lib.ffdo_quantize_k_res.argtypes = [P, i32, i32, i32, i32, i32, i32, i32, P, P, P, P]
+    lib.ffdo_quantize_k_res.restype = i32
+    lib.ffdo_dequant.argtypes = [P, P, P, P, i32, i32, i32, i32, i32]
+    lib.ffdo_dequant.restype = ctypes.c_double
+    lib.ffdo_scan_head_bits.argtypes = [P, P, P, i32, i32, i32, i32, P, P, P]
+    lib.ffdo_scan_head_bits.restype = None
+    lib.ffdo_attend_head_res.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P]
+    lib.ffdo_attend_head_res.restype = None
+    lib.ffdo_decode_res.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P,
+                                    f32, i32, P, P, P, P, P, i32]
+    lib.ffdo_decode_res.restype = i32
     _lib = lib
     return lib
 
@@ -221,6 +234,118 @@ def decode(q, K, V, L: int, T: int, delta: float = float("inf"), Kq=None, scales
                              n_threads or n_threads_default())
     if rc < 0:
         raise ValueError("oracle decode: bad sizes")
+    res = {"out": out, "lse": lse}
+    if sparse:
+        res["keep"] = keep[:, :, :n_blocks]
+        res["mtilde"] = mtilde
+        if want_shat:
+            res["shat"] = shat[:, :, :n_full]
+    return res
+
+
+# ------------------------------------------------------------------------------------------
+# Residual storage form: low-bit thumbnail + 8-bit residual (Sec. 3.1, Fig. 2, Alg. 1 Dequant)
+# ------------------------------------------------------------------------------------------
+def quantize_residual(r: np.ndarray):
+    """8-bit symmetric quantizer of one residual vector -> (codes int8[n], scale float)."""
+    r = np.ascontiguousarray(r, dtype=np.float32)
+    rq = np.empty(r.shape[0], dtype=np.int8)
+    s = np.empty(1, dtype=np.float32)
+    _load().ffdo_quantize_residual(_ptr(r), r.shape[0], _ptr(rq), _ptr(s))
+    return rq, float(s[0])
+
+
+def quantize_k_res(K: np.ndarray, T: int, bits: int, tok_begin: int = 0, tok_end: int | None = None,
+                   out=None):
+    """Thumbnail + residual of the completed blocks of K [B, Hkv, L_cap, d] ->
+    (Kc u8 [.., d*bits/8], sc f32 [.., L_cap/T, d], Kr i8 [.., d], sr f32 [.., L_cap/T, d])."""
+    B, Hkv, L_cap, d = K.shape
+    if tok_end is None:
+        tok_end = L_cap
+    K = np.ascontiguousarray(K)
+    if out is None:
+        out = (np.zeros((B, Hkv, L_cap, d * bits // 8), np.uint8),
+               np.zeros((B, Hkv, L_cap // T, d), np.float32),
+               np.zeros((B, Hkv, L_cap, d), np.int8),
+               np.zeros((B, Hkv, L_cap // T, d), np.float32))
+    Kc, sc, Kr, sr = out
+    lib = _load()
+    dt = _dtype_code(K)
+    for b in range(B):
+        for g in range(Hkv):
+            rc = lib.ffdo_quantize_k_res(_ptr(K[b, g]), dt, L_cap, d, T, bits, tok_begin, tok_end,
+                                         _ptr(Kc[b, g]), _ptr(sc[b, g]), _ptr(Kr[b, g]),
+                                         _ptr(sr[b, g]))
+            if rc < 0:
+                raise ValueError("oracle quantize_k_res: bad sizes")
+    return Kc, sc, Kr, sr
+
+
+def dequant(Kc, sc, Kr, sr, T: int, bits: int, t: int, c: int) -> float:
+    """Alg. 1 Dequant of key element (t, c) of one slice (double)."""
+    d = Kr.shape[-1]
+    return float(_load().ffdo_dequant(_ptr(np.ascontiguousarray(Kc)), _ptr(np.ascontiguousarray(sc)),
+                                      _ptr(np.ascontiguousarray(Kr)), _ptr(np.ascontiguousarray(sr)),
+                                      d, T, bits, t, c))
+
+
+def scan_head_bits(qh, Kc_slice, sc_slice, n_full: int, T: int, bits: int, per_token=False):
+    """Scan of one head over a thumbnail slice (bits = 2 or 4)."""
+    qh = np.ascontiguousarray(to_f32(qh))
+    d = qh.shape[0]
+    Kc_slice = np.ascontiguousarray(Kc_slice)
+    sc_slice = np.ascontiguousarray(sc_slice)
+    sb = np.empty(max(n_full, 1), dtype=np.float32)
+    st = np.empty(max(n_full * T, 1), dtype=np.float32) if per_token else None
+    Et = np.empty(max(n_full * T, 1), dtype=np.int32) if per_token else None
+    _load().ffdo_scan_head_bits(_ptr(qh), _ptr(Kc_slice), _ptr(sc_slice), n_full, T, d, bits,
+                                _ptr(sb), _ptr(st), _ptr(Et))
+    if per_token:
+        return sb[:n_full], st[: n_full * T], Et[: n_full * T]
+    return sb[:n_full]
+
+
+def attend_head_res(qh, Kc, sc, Kr, sr, Ktail, V, L: int, T: int, bits: int, keep=None):
+    """Exact fp64 attention of one head over Dequant keys (full blocks) + 16-bit tail keys."""
+    qv = np.ascontiguousarray(to_f32(qh))
+    d = qv.shape[0]
+    out = np.empty(d, dtype=np.float64)
+    lse = np.empty(1, dtype=np.float64)
+    kp = None if keep is None else np.ascontiguousarray(keep, dtype=np.uint8)
+    V = np.ascontiguousarray(V)
+    _load().ffdo_attend_head_res(_ptr(qv), _ptr(np.ascontiguousarray(Kc)),
+                                 _ptr(np.ascontiguousarray(sc)), _ptr(np.ascontiguousarray(Kr)),
+                                 _ptr(np.ascontiguousarray(sr)),
+                                 None if Ktail is None else _ptr(np.ascontiguousarray(Ktail)),
+                                 _ptr(V), _dtype_code(V), L, d, T, bits, _ptr(kp), _ptr(out),
+                                 _ptr(lse))
+    return out, float(lse[0])
+
+
+def decode_res(q, Ktail, V, Kc, sc, Kr, sr, L: int, T: int, bits: int, delta: float = float("inf"),
+               sparse: bool = True, n_threads: int | None = None, want_shat: bool = False):
+    """Whole decode step in the residual storage form (q, Ktail, V bf16 bits)."""
+    B, Hq, d = q.shape
+    _, Hkv, L_cap, _ = V.shape
+    for a in (q, V) + (() if Ktail is None else (Ktail,)):
+        if _dtype_code(a) != DTYPE_BF16:
+            raise TypeError("the residual form takes bf16 q, tail keys and values")
+    n_blocks = (L + T - 1) // T
+    n_full = L // T
+    out = np.empty((B, Hq, d), dtype=np.float64)
+    lse = np.empty((B, Hq), dtype=np.float64)
+    keep = np.empty((B, Hq, max(n_blocks, 1)), dtype=np.uint8) if sparse else None
+    mtilde = np.empty((B, Hq), dtype=np.float32) if sparse else None
+    shat = np.empty((B, Hq, max(n_full, 1)), dtype=np.float32) if (sparse and want_shat) else None
+    arrs = [np.ascontiguousarray(a) for a in (q, V, Kc, sc, Kr, sr)]
+    Kt = None if Ktail is None else np.ascontiguousarray(Ktail)
+    rc = _load().ffdo_decode_res(B, Hq, Hkv, d, L, L_cap, T, bits, _ptr(arrs[0]), _ptr(Kt),
+                                 _ptr(arrs[1]), _ptr(arrs[2]), _ptr(arrs[3]), _ptr(arrs[4]),
+                                 _ptr(arrs[5]), float(delta), 1 if sparse else 0, _ptr(out),
+                                 _ptr(lse), _ptr(keep), _ptr(shat), _ptr(mtilde),
+                                 n_threads or n_threads_default())
+    if rc < 0:
+        raise ValueError("oracle decode_res: bad sizes")
     res = {"out": out, "lse": lse}
     if sparse:
         res["keep"] = keep[:, :, :n_blocks]

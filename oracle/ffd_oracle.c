@@ -21,6 +21,10 @@
  *   O8  attention    Alg. 1, refinement stage: exact softmax(q K^T / sqrt(d)) V over the tokens of
  *                    the kept blocks, in double precision.
  *   O9  dense        the same over every token (FlashAttention-style exact decode, FTF Sec. 2).
+ *   R1-R4 residual storage form (Sec. 3.1, Fig. 2, Alg. 1 Dequant, Eq. 4): a 2- or 4-bit
+ *                    thumbnail plus an 8-bit residual replaces the 16-bit keys of full blocks;
+ *                    the scan reads the thumbnail, the refinement attends over Dequant keys
+ *                    (see the section at the end of this file for its readings).
  *
  * Readings of points the paper leaves open (each is also listed in the design notes):
  *   - Quantizer levels: value of code u is (u - (2^bits-1)/2) * s, s = amax / ((2^bits-1)/2).
@@ -312,6 +316,233 @@ int ffdo_decode(int B, int Hq, int Hkv, int d, int L, int L_cap, int T, int dtyp
             free(sb);
         }
         ffdo_attend_head(qh, Kbg, Vbg, dtype, L, d, T, kp, out + (size_t)r * d, lse + r);
+        free(kp);
+        free(qh);
+    }
+    return rows;
+}
+
+/* ========================================================================================== */
+/* Storage form of FTF Sec. 3.1 / Fig. 2: the key cache split into a low-bit thumbnail and an  */
+/* 8-bit residual; Alg. 1's Dequant rebuilds the key for the refinement stage (Eq. 4 is the    */
+/* same quantity written as two dot products).                                                 */
+/*                                                                                             */
+/* Readings (the paper fixes the thumbnail quantizer, App. A, but not the residual's):         */
+/*   - thumbnail: the App. A quantizer with 2^bits levels, bits = 2 (App. A exactly) or 4;     */
+/*     codes packed little-endian in bytes, channel c at bit (c % (8/bits)) * bits of byte     */
+/*     c / (8/bits) of its token row;                                                          */
+/*   - residual of a key element: r = RN(x - RN((u - half) * s)) in fp32;                      */
+/*   - residual quantizer: symmetric 8-bit per (block, channel): s_r = RN(max|r| / 127),       */
+/*     r_q = clamp(rint(RN(r * RN(127 / max|r|))), -127, 127); max|r| = 0 gives s_r = 0, r_q=0;*/
+/*   - Dequant: k = (u - half) * s + r_q * s_r (evaluated in double here);                     */
+/*   - a partial tail block (tokens after the last full block) has no low-bit copy: its keys   */
+/*     are read from a 16-bit key buffer.                                                      */
+/* ========================================================================================== */
+
+static int code_at(const uint8_t* row, int c, int bits)
+{
+    const int per = 8 / bits;
+    return (row[c / per] >> ((c % per) * bits)) & ((1 << bits) - 1);
+}
+
+/* Residual quantizer for one channel vector r[0..n) (stride 1). */
+void ffdo_quantize_residual(const float* r, int n, int8_t* rq, float* scale_out)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        const float a = fabsf(r[i]);
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+        *scale_out = 0.0f;
+        for (int i = 0; i < n; ++i) rq[i] = 0;
+        return;
+    }
+    *scale_out = amax / 127.0f;
+    const float inv = 127.0f / amax;
+    for (int i = 0; i < n; ++i) {
+        float v = rintf(r[i] * inv);
+        if (v > 127.0f) v = 127.0f;
+        if (v < -127.0f) v = -127.0f;
+        rq[i] = (int8_t)v;
+    }
+}
+
+/*
+ * Thumbnail + residual of the completed blocks of one (batch, kv-head) slice K [L_cap][d]
+ * (fp32 or bf16 bits); blocks whose last token lies in [tok_begin, tok_end) are written:
+ *   Kc [L_cap][d*bits/8] packed codes, sc [L_cap/T][d] thumbnail scales,
+ *   Kr [L_cap][d] int8 residual codes, sr [L_cap/T][d] residual scales.
+ * Returns the number of blocks written (or -1 for bad sizes).
+ */
+int ffdo_quantize_k_res(const void* K, int dtype, int L_cap, int d, int T, int bits,
+                        int tok_begin, int tok_end, uint8_t* Kc, float* sc, int8_t* Kr,
+                        float* sr)
+{
+    if ((bits != 2 && bits != 4) || d % (8 / bits) || T <= 0 || L_cap % T) return -1;
+    const int per = 8 / bits;
+    const int row_bytes = d / per;
+    const float half = (float)((1 << bits) - 1) * 0.5f;
+    float* x = (float*)malloc(sizeof(float) * (size_t)T);
+    float* r = (float*)malloc(sizeof(float) * (size_t)T);
+    uint8_t* codes = (uint8_t*)malloc((size_t)T);
+    int8_t* rq = (int8_t*)malloc((size_t)T);
+    int written = 0;
+    for (int j = 0; j < L_cap / T; ++j) {
+        const int last = (j + 1) * T - 1;
+        if (last < tok_begin || last >= tok_end) continue;
+        for (int t = 0; t < T; ++t) memset(Kc + (size_t)(j * T + t) * row_bytes, 0, (size_t)row_bytes);
+        for (int c = 0; c < d; ++c) {
+            for (int t = 0; t < T; ++t) x[t] = load_elem(K, dtype, (size_t)(j * T + t) * d + c);
+            float s;
+            ffdo_quantize_channel(x, T, 1, bits, codes, &s);
+            for (int t = 0; t < T; ++t) {
+                const float xh = ((float)codes[t] - half) * s;
+                r[t] = x[t] - xh;
+            }
+            float s_r;
+            ffdo_quantize_residual(r, T, rq, &s_r);
+            sc[(size_t)j * d + c] = s;
+            sr[(size_t)j * d + c] = s_r;
+            for (int t = 0; t < T; ++t) {
+                uint8_t* row = Kc + (size_t)(j * T + t) * row_bytes;
+                row[c / per] |= (uint8_t)(codes[t] << ((c % per) * bits));
+                Kr[(size_t)(j * T + t) * d + c] = rq[t];
+            }
+        }
+        ++written;
+    }
+    free(x);
+    free(r);
+    free(codes);
+    free(rq);
+    return written;
+}
+
+/* Alg. 1 Dequant of key element (t, c) of a slice, in double. */
+double ffdo_dequant(const uint8_t* Kc, const float* sc, const int8_t* Kr, const float* sr,
+                    int d, int T, int bits, int t, int c)
+{
+    const int row_bytes = d * bits / 8;
+    const int u = code_at(Kc + (size_t)t * row_bytes, c, bits);
+    const double half = (double)((1 << bits) - 1) * 0.5;
+    const size_t sidx = (size_t)(t / T) * d + c;
+    return ((double)u - half) * (double)sc[sidx] + (double)Kr[(size_t)t * d + c] * (double)sr[sidx];
+}
+
+/*
+ * Integer-exact scan of one query head over the thumbnail codes (bits = 2 or 4); the same
+ * arithmetic as ffdo_scan_head with E_t = sum_c wi_c * (2 u_tc - (2^bits - 1)).
+ */
+void ffdo_scan_head_bits(const float* qh, const uint8_t* Kc, const float* scales, int n_full,
+                         int T, int d, int bits, float* shat_block, float* shat_tok,
+                         int32_t* E_tok)
+{
+    const int row_bytes = d * bits / 8;
+    const int top = (1 << bits) - 1;
+    int32_t* wi = (int32_t*)malloc(sizeof(int32_t) * (size_t)d);
+    for (int j = 0; j < n_full; ++j) {
+        const float f = ffdo_requant(qh, scales + (size_t)j * d, d, wi);
+        float best = -INFINITY;
+        for (int t = 0; t < T; ++t) {
+            const uint8_t* row = Kc + (size_t)(j * T + t) * row_bytes;
+            int64_t E = 0;
+            for (int c = 0; c < d; ++c)
+                E += (int64_t)wi[c] * (int64_t)(2 * code_at(row, c, bits) - top);
+            const float sh = (float)E * f;
+            if (shat_tok) shat_tok[(size_t)j * T + t] = sh;
+            if (E_tok) E_tok[(size_t)j * T + t] = (int32_t)E;
+            if (sh > best) best = sh;
+        }
+        shat_block[j] = best;
+    }
+    free(wi);
+}
+
+/*
+ * Exact attention of one head over the kept blocks with Dequant keys (full blocks) and the
+ * 16-bit tail keys Ktail [L_cap][d] (bf16 bits; rows n_full*T .. L-1 are read, may be NULL when
+ * L % T == 0).  V [L_cap][d] in `dtype`.  keep = NULL for all blocks.
+ */
+void ffdo_attend_head_res(const float* qh, const uint8_t* Kc, const float* sc, const int8_t* Kr,
+                          const float* sr, const void* Ktail, const void* V, int dtype, int L,
+                          int d, int T, int bits, const uint8_t* keep, double* out, double* lse)
+{
+    const int n_full = L / T;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    double m = -INFINITY;
+    for (int t = 0; t < L; ++t) {
+        if (keep && !keep[t / T]) { s[t] = -INFINITY; continue; }
+        double acc = 0.0;
+        for (int c = 0; c < d; ++c) {
+            const double k = t < n_full * T
+                                 ? ffdo_dequant(Kc, sc, Kr, sr, d, T, bits, t, c)
+                                 : (double)load_elem(Ktail, FFDO_DTYPE_BF16, (size_t)t * d + c);
+            acc += (double)qh[c] * k;
+        }
+        s[t] = acc * inv_sqrt_d;
+        if (s[t] > m) m = s[t];
+    }
+    double l = 0.0;
+    for (int c = 0; c < d; ++c) out[c] = 0.0;
+    for (int t = 0; t < L; ++t) {
+        if (s[t] == -INFINITY) continue;
+        const double p = exp(s[t] - m);
+        l += p;
+        for (int c = 0; c < d; ++c) out[c] += p * (double)load_elem(V, dtype, (size_t)t * d + c);
+    }
+    for (int c = 0; c < d; ++c) out[c] /= l;
+    *lse = m + log(l);
+    free(s);
+}
+
+/*
+ * Whole decode step in the residual storage form (q, Ktail, V bf16 bits; thumbnail + residual of
+ * the full blocks), OpenMP over (batch, query head).  sparse = 0 attends over every token with
+ * the same Dequant keys.  Outputs as ffdo_decode.
+ */
+int ffdo_decode_res(int B, int Hq, int Hkv, int d, int L, int L_cap, int T, int bits,
+                    const void* q, const void* Ktail, const void* V, const uint8_t* Kc,
+                    const float* sc, const int8_t* Kr, const float* sr, float delta, int sparse,
+                    double* out, double* lse, uint8_t* keep, float* shat, float* mtilde,
+                    int n_threads)
+{
+    if (Hkv <= 0 || Hq % Hkv || (bits != 2 && bits != 4) || d % (8 / bits) || T <= 0 || L < 0 ||
+        L > L_cap || L_cap % T)
+        return -1;
+    if (L % T && !Ktail) return -1;
+    const int G = Hq / Hkv;
+    const int n_full = L / T;
+    const int n_blocks = (L + T - 1) / T;
+    const int row_bytes = d * bits / 8;
+    const int rows = B * Hq;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads > 0 ? n_threads : 1)
+    for (int r = 0; r < rows; ++r) {
+        const int b = r / Hq, h = r % Hq, g = h / G;
+        const size_t bg = (size_t)b * Hkv + g;
+        float* qh = (float*)malloc(sizeof(float) * (size_t)d);
+        for (int c = 0; c < d; ++c) qh[c] = load_elem(q, FFDO_DTYPE_BF16, (size_t)r * d + c);
+        const uint8_t* Kc_bg = Kc + bg * (size_t)L_cap * row_bytes;
+        const float* sc_bg = sc + bg * (size_t)(L_cap / T) * d;
+        const int8_t* Kr_bg = Kr + bg * (size_t)L_cap * d;
+        const float* sr_bg = sr + bg * (size_t)(L_cap / T) * d;
+        const char* Kt_bg = Ktail ? (const char*)Ktail + bg * (size_t)L_cap * d * 2 : NULL;
+        const char* V_bg = (const char*)V + bg * (size_t)L_cap * d * 2;
+        uint8_t* kp = NULL;
+        if (sparse) {
+            float* sb = (float*)malloc(sizeof(float) * (size_t)(n_full > 0 ? n_full : 1));
+            kp = (uint8_t*)malloc((size_t)(n_blocks > 0 ? n_blocks : 1));
+            ffdo_scan_head_bits(qh, Kc_bg, sc_bg, n_full, T, d, bits, sb, NULL, NULL);
+            float mt;
+            ffdo_select_head(sb, n_full, n_blocks, delta, kp, &mt, NULL);
+            if (keep) memcpy(keep + (size_t)r * n_blocks, kp, (size_t)n_blocks);
+            if (shat) memcpy(shat + (size_t)r * n_full, sb, sizeof(float) * (size_t)n_full);
+            if (mtilde) mtilde[r] = mt;
+            free(sb);
+        }
+        ffdo_attend_head_res(qh, Kc_bg, sc_bg, Kr_bg, sr_bg, Kt_bg, V_bg, FFDO_DTYPE_BF16, L, d,
+                             T, bits, kp, out + (size_t)r * d, lse + r);
         free(kp);
         free(qh);
     }

@@ -1,0 +1,221 @@
+"""Pins for the oracle's residual storage form of the key cache.
+
+"Faster Than Flash" Sec. 3.1 and Fig. 2 split each key into a low-bit thumbnail (the App. A
+quantizer; 2 bits in the paper) and an 8-bit residual; Alg. 1's Dequant rebuilds the key for the
+refinement stage, and Eq. 4 writes the same score as q.k_quant + q.k_res.  The paper does not fix
+the residual's quantizer; the oracle's reading is a symmetric 8-bit code per (block, channel).
+Pins (none re-types the oracle's formulas):
+
+* the thumbnail at 2 bits is App. A by brute force over its 4-level codebook, and the 4-bit
+  thumbnail is byte-identical to the already-pinned 4-bit key copy;
+* the residual quantizer against brute-force nearest-integer search, with closed forms;
+* every Dequant key lies within half a residual step of the original key;
+* keys exactly on the thumbnail grid have a zero residual, and attention over their Dequant keys
+  equals PyTorch's scaled_dot_product_attention over the original keys (fp64);
+* on general keys, lse over Dequant keys is within the bound implied by the per-key error;
+* the 2-bit scan: exact on a representable grid, one-hot query closed form, int64 recomputation.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_decoding_amd import workloads as W
+
+
+def unpack_bits(Kc, bits, d):
+    """[..., d*bits/8] packed bytes -> [..., d] codes, channel c at bit (c % per)*bits of byte c/per."""
+    per = 8 // bits
+    out = np.empty(Kc.shape[:-1] + (d,), dtype=np.int64)
+    for i in range(per):
+        out[..., i::per] = (Kc.astype(np.int64) >> (i * bits)) & ((1 << bits) - 1)
+    return out
+
+
+def vals(a):
+    return oracle.to_f32(a).astype(np.float64)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_residual_quantizer_is_nearest_integer(seed):
+    rng = np.random.default_rng(seed)
+    n = 300
+    r = (rng.standard_normal(n) * 10.0 ** rng.uniform(-3, 1)).astype(np.float32)
+    # adversarial: values whose r/s lands near a half-integer
+    r[:40] = ((rng.integers(-126, 126, 40) + 0.5) * (np.abs(r).max() / 127)).astype(np.float32)
+    rq, s = oracle.quantize_residual(r)
+    amax = float(np.abs(r).max())
+    assert s == np.float32(np.float32(amax) / np.float32(127.0))
+    assert np.abs(rq).max() == 127
+    assert rq[np.argmax(np.abs(r))] == 127 * np.sign(r[np.argmax(np.abs(r))])
+    y = r.astype(np.float64) / s
+    ks = np.arange(-127, 128, dtype=np.float64)
+    dist = np.abs(y[:, None] - ks[None, :])
+    best = dist.min(axis=1)
+    ok = dist[np.arange(n), rq.astype(np.int64) + 127] <= best + 1e-4
+    assert ok.all(), np.nonzero(~ok)
+    assert (np.abs(r - rq.astype(np.float64) * s) <= s * (0.5 + 1e-4)).all()
+
+
+def test_residual_zero_vector():
+    rq, s = oracle.quantize_residual(np.zeros(64, np.float32))
+    assert s == 0.0 and (rq == 0).all()
+
+
+@pytest.mark.parametrize("T", [64, 128])
+def test_two_bit_thumbnail_is_app_a(T):
+    rng = np.random.default_rng(T)
+    d, n = 128, 3
+    K = W.f32_to_bf16_bits(rng.standard_normal((1, 1, n * T, d)).astype(np.float32))
+    Kc, sc, Kr, sr = oracle.quantize_k_res(K, T, 2)
+    codes = unpack_bits(Kc[0, 0], 2, d)
+    x = vals(K[0, 0])
+    cb = np.array([-1.5, -0.5, 0.5, 1.5])
+    for j in range(n):
+        blk = x[j * T:(j + 1) * T]
+        s = (np.abs(blk).max(axis=0).astype(np.float32) / np.float32(1.5)).astype(np.float32)
+        np.testing.assert_array_equal(sc[0, 0, j], s)
+        dist = np.abs((blk / s.astype(np.float64))[:, :, None] - cb[None, None, :])
+        near = dist <= dist.min(axis=2, keepdims=True) + 1e-6
+        got = codes[j * T:(j + 1) * T]
+        assert near[np.arange(T)[:, None], np.arange(d)[None, :], got].all()
+
+
+def test_four_bit_thumbnail_equals_key_copy():
+    rng = np.random.default_rng(3)
+    K = W.f32_to_bf16_bits(rng.standard_normal((2, 2, 5 * 64, 128)).astype(np.float32))
+    Kc, sc, _, _ = oracle.quantize_k_res(K, 64, 4)
+    Kq, sq = oracle.quantize_k(K, 64)
+    np.testing.assert_array_equal(Kc, Kq)
+    np.testing.assert_array_equal(sc, sq)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_dequant_within_half_residual_step(bits):
+    rng = np.random.default_rng(bits)
+    T, d, n = 64, 128, 4
+    K = W.f32_to_bf16_bits(rng.standard_normal((1, 1, n * T, d)).astype(np.float32) * 3)
+    Kc, sc, Kr, sr = oracle.quantize_k_res(K, T, bits)
+    x = vals(K[0, 0])
+    idx = rng.integers(0, n * T, 1500), rng.integers(0, d, 1500)
+    for t, c in zip(*idx):
+        k = oracle.dequant(Kc[0, 0], sc[0, 0], Kr[0, 0], sr[0, 0], T, bits, int(t), int(c))
+        s_r = float(sr[0, 0, t // T, c])
+        assert abs(k - x[t, c]) <= s_r * (0.5 + 1e-4) + 2.0 ** -22 * abs(x[t, c]), (t, c)
+
+
+@pytest.mark.parametrize("bits,tail", [(2, 0), (4, 0), (2, 13), (4, 63)])
+def test_zero_residual_reduces_to_sdpa_on_original_keys(bits, tail):
+    """Full blocks on the thumbnail grid (zero residual) plus an off-grid partial tail read from
+    the 16-bit keys: attention over the Dequant keys equals SDPA over the original keys."""
+    rng = np.random.default_rng(10 + bits + tail)
+    T, d, n, Hq = 64, 128, 4, 4
+    half = (2 ** bits - 1) / 2
+    u = rng.integers(0, 2 ** bits, size=(n, T, d))
+    u[:, 0, :] = np.where(rng.random((n, d)) < 0.5, 0, 2 ** bits - 1)  # amax reached
+    s = 2.0 ** rng.integers(-3, 2, size=(n, 1, d))
+    x = np.zeros(((n + 1) * T, d), np.float32)
+    x[:n * T] = ((u - half) * s).reshape(n * T, d)
+    x[n * T:] = rng.standard_normal((T, d)).astype(np.float32) * 2   # tail (and padding)
+    L = n * T + tail
+    K = W.f32_to_bf16_bits(x)[None, None]
+    xk = oracle.to_f32(K[0, 0]).astype(np.float64)
+    assert (xk[:n * T] == x[:n * T]).all()
+    q = W.f32_to_bf16_bits(rng.standard_normal((1, Hq, d)).astype(np.float32))
+    V = W.f32_to_bf16_bits(rng.standard_normal((1, 1, (n + 1) * T, d)).astype(np.float32))
+    Kc, sc, Kr, sr = oracle.quantize_k_res(K, T, bits, 0, L)
+    assert (Kr[0, 0, :n * T] == 0).all() and (sr[0, 0, :n] == 0).all()
+    res = oracle.decode_res(q, K, V, Kc, sc, Kr, sr, L, T, bits, sparse=False)
+    qt = torch.from_numpy(vals(q)[0])[:, None, :]
+    kt = torch.from_numpy(xk[:L])[None].expand(Hq, -1, -1)
+    vt = torch.from_numpy(vals(V[0, 0])[:L])[None].expand(Hq, -1, -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[:, 0].numpy()
+    np.testing.assert_allclose(res["out"][0], ref, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_lse_within_dequant_error_bound(bits):
+    """Every score moves by at most sum_c |q_c| * err_c / sqrt(d), so lse moves at most that."""
+    w = W.small("r", B=1, Hq=4, Hkv=1, L=6 * 64, T=64, seed=bits)
+    q, K, V, _ = W.make_inputs(w)
+    Kc, sc, Kr, sr = oracle.quantize_k_res(K, w.T, bits)
+    res = oracle.decode_res(q, None, V, Kc, sc, Kr, sr, w.L, w.T, bits, sparse=False)
+    dense = oracle.decode(q, K, V, w.L, w.T, sparse=False)
+    qa = np.abs(vals(q[0]))                                       # [Hq, d]
+    x = vals(K[0, 0])
+    err = np.repeat(sr[0, 0].astype(np.float64), w.T, axis=0) * (0.5 + 1e-4) + \
+        2.0 ** -22 * np.abs(x)                                     # [L, d] per-key bound
+    bound = (qa @ err.T).max(axis=1) / math.sqrt(w.d)               # [Hq]
+    assert (np.abs(res["lse"][0] - dense["lse"][0]) <= bound + 1e-12).all()
+    assert (bound > 0).all() and (bound < 0.2).all()
+
+
+def grid2(rng, n, T, d, exps):
+    u = rng.integers(0, 4, size=(n, T, d))
+    u[:, 0, :] = np.where(rng.random((n, d)) < 0.5, 0, 3)
+    s = np.asarray([2.0 ** e for e in exps])[:, None, None]
+    return ((u - 1.5) * s).reshape(n * T, d).astype(np.float32), u.reshape(n * T, d)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_two_bit_scan_exact_on_grid(seed):
+    rng = np.random.default_rng(seed)
+    T, d, n = 64, 128, 5
+    exps = rng.integers(-4, 3, size=n)
+    x, u = grid2(rng, n, T, d, exps)
+    Kc, sc, _, _ = oracle.quantize_k_res(x[None, None], T, 2)
+    assert (unpack_bits(Kc[0, 0], 2, d) == u).all()
+    q = rng.integers(-127, 128, size=d).astype(np.float32)
+    q[rng.integers(d)] = 127.0
+    sb, st, _ = oracle.scan_head_bits(q, Kc[0, 0], sc[0, 0], n, T, 2, per_token=True)
+    exact = (x.astype(np.float64) @ q.astype(np.float64)) / math.sqrt(d)
+    assert (np.abs(st - exact) <= 4 * 2.0 ** -24 * np.abs(exact) + 1e-30).all()
+    np.testing.assert_array_equal(sb, st.reshape(n, T).max(axis=1))
+
+
+@pytest.mark.parametrize("c", [0, 3, 77])
+def test_two_bit_scan_one_hot_query(c):
+    rng = np.random.default_rng(c)
+    T, d, n = 64, 128, 3
+    K = W.f32_to_bf16_bits(rng.standard_normal((1, 1, n * T, d)).astype(np.float32))
+    Kc, sc, _, _ = oracle.quantize_k_res(K, T, 2)
+    q = np.zeros(d, np.float32)
+    q[c] = 2.5
+    _, st, _ = oracle.scan_head_bits(q, Kc[0, 0], sc[0, 0], n, T, 2, per_token=True)
+    codes = unpack_bits(Kc[0, 0], 2, d)[:, c]
+    expect = (codes - 1.5) * np.repeat(sc[0, 0, :, c], T).astype(np.float64) * 2.5 / math.sqrt(d)
+    np.testing.assert_allclose(st, expect, rtol=4 * 2.0 ** -24, atol=0)
+
+
+def test_two_bit_scan_integer_sums():
+    rng = np.random.default_rng(8)
+    T, d, n = 128, 128, 3
+    K = W.f32_to_bf16_bits(rng.standard_normal((1, 1, n * T, d)).astype(np.float32))
+    Kc, sc, _, _ = oracle.quantize_k_res(K, T, 2)
+    q = W.bf16_bits_to_f32(W.f32_to_bf16_bits(rng.standard_normal(d).astype(np.float32)))
+    _, st, Et = oracle.scan_head_bits(q, Kc[0, 0], sc[0, 0], n, T, 2, per_token=True)
+    codes = unpack_bits(Kc[0, 0], 2, d)
+    for j in range(n):
+        wi, f = oracle.requant(q, sc[0, 0, j])
+        E = (codes[j * T:(j + 1) * T] * 2 - 3) @ wi.astype(np.int64)
+        np.testing.assert_array_equal(Et[j * T:(j + 1) * T], E)
+
+
+def test_residual_decode_mask_rules():
+    """Forced blocks, delta = inf keeps all, masks nested in delta, partial tail from 16-bit keys."""
+    w = W.small("m", B=2, Hq=8, Hkv=2, L=11 * 64 + 21, T=64, seed=4)
+    q, K, V, _ = W.make_inputs(w)
+    Kc, sc, Kr, sr = oracle.quantize_k_res(K, w.T, 2, 0, w.L)
+    prev = None
+    for delta in (0.0, 1.0, 3.0, 6.0, float("inf")):
+        r = oracle.decode_res(q, K, V, Kc, sc, Kr, sr, w.L, w.T, 2, delta=delta)
+        keep = r["keep"]
+        assert keep[:, :, 0].all() and keep[:, :, w.n_full - 1:].all()
+        if prev is not None:
+            assert (keep >= prev).all()
+        prev = keep
+    assert prev.all()
+    dense = oracle.decode_res(q, K, V, Kc, sc, Kr, sr, w.L, w.T, 2, sparse=False)
+    np.testing.assert_allclose(r["out"], dense["out"], atol=1e-12)
