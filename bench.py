@@ -63,6 +63,21 @@ def bytes_sparse(w, keep: np.ndarray) -> dict:
             "union_keep": float(union.mean()), "head_keep": float(keep.mean())}
 
 
+def bytes_residual(w, keep: np.ndarray, bits: int) -> dict:
+    """Algorithmic bytes of one sparse step in the residual storage form: thumbnail codes and
+    scales of every full block; for every union-kept block its codes, 8-bit residual codes, both
+    scale rows and bf16 values; q."""
+    d, T = w.d, w.T
+    code_b = T * d * bits // 8
+    scan = w.B * w.Hkv * w.n_full * (code_b + 4 * d)
+    union = keep.reshape(w.B, w.Hkv, w.G, w.n_blocks).max(axis=2)
+    U = int(union.sum())
+    exact = U * (code_b + T * d + 2 * 4 * d + 2 * T * d)
+    qb = w.B * w.Hq * d * 2
+    return {"scan": scan, "exact": exact, "q": qb, "total": scan + exact + qb,
+            "union_keep": float(union.mean())}
+
+
 def bytes_dense(w) -> int:
     return 2 * w.B * w.Hkv * w.L * w.d * w.elem_bytes + w.B * w.Hq * w.d * w.elem_bytes
 
@@ -71,7 +86,7 @@ def bytes_dense(w) -> int:
 # GPU measurement
 # ------------------------------------------------------------------------------------------
 def run_workload(w, delta: float, steps: int, warmup: int, min_rotation_mib: int = 1024,
-                 graphs: bool = True):
+                 graphs: bool = True, residual_bits: int = 0):
     """Time one decode step of workload w on cuda:0.
 
     Steps run back to back over R copies of the KV cache (like R layers of a model, each with
@@ -187,6 +202,54 @@ def run_workload(w, delta: float, steps: int, warmup: int, min_rotation_mib: int
     us_s_warm = timed(sparse, steps, rotate=False)
     us_d_warm = timed(dense, steps, rotate=False)
 
+    res_form = None
+    if residual_bits:
+        # the residual storage form (thumbnail + 8-bit residual replace the keys of full blocks)
+        bits = residual_bits
+        del reps
+        torch.cuda.empty_cache()
+        kres = ffd.alloc_kres(Kd, w.T, bits)
+        ev0.record(stream)
+        ffd.quantize_k_residual_append(Kd, 0, w.L, w.T, bits, kres, seq_len=w.L)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        rq_us = ev0.elapsed_time(ev1) * 1e3
+        keep_r = torch.zeros_like(keep)
+        out_r = torch.empty_like(out_s)
+        lse_r = torch.empty_like(lse_s)
+        Kt = Kd if w.L % w.T else None
+        ffd.decode_sparse_residual(qd, Kt, Vd, kres, bits, delta, w.T, w.L, out=out_r, lse=lse_r,
+                                   keep_mask=keep_r, workspace=ws)
+        torch.cuda.synchronize()
+        br = bytes_residual(w, keep_r.cpu().numpy(), bits)
+        o_r = out_r.double().cpu().numpy()
+        cos_r = (o_r * o_d).sum(-1) / (np.linalg.norm(o_r, axis=-1) * np.linalg.norm(o_d, axis=-1))
+        Rr = max(2, math.ceil(min_rotation_mib * 2**20 / br["total"]) + 1)
+        reps_r = [(Vd, kres)] + [(Vd.clone(), tuple(t.clone() for t in kres))
+                                 for _ in range(Rr - 1)]
+        torch.cuda.synchronize()
+
+        def sparse_res(r):
+            Vr, kr = reps_r[r % Rr]
+            ffd.decode_sparse_residual(qd, Kt, Vr, kr, bits, delta, w.T, w.L, out=out_r,
+                                       lse=lse_r, workspace=ws)
+
+        timed_eager(sparse_res, warmup)
+        us_r = timed(sparse_res, steps)
+        us_r_warm = timed(sparse_res, steps, rotate=False)
+        res_form = {
+            "storage": f"{bits}-bit thumbnail + 8-bit residual keys, bf16 values",
+            "sparse_us": us_r, "sparse_us_warm_cache": us_r_warm,
+            "speedup_vs_dense_bf16": us_d / us_r,
+            "bytes_read": br["total"], "bytes_scan": br["scan"], "bytes_exact": br["exact"],
+            "GBps": br["total"] / us_r * 1e-3, "hbm_frac": br["total"] / us_r * 1e-3 / HBM_PEAK_GBPS,
+            "union_keep": br["union_keep"], "recall_cos_min_vs_dense": float(cos_r.min()),
+            "masks_equal_4bit_path": bool(torch.equal(keep_r, keep)) if bits == 4 else None,
+            "quantize_us": rq_us, "cache_copies": Rr,
+        }
+        del reps_r, kres
+        torch.cuda.empty_cache()
+
     res = {
         "workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "L": w.L,
         "block": w.T, "delta": delta, "kv_dtype": w.dtype, "scan_bits": 4,
@@ -204,8 +267,11 @@ def run_workload(w, delta: float, steps: int, warmup: int, min_rotation_mib: int
         "recall_cos_min": float(cos.min()), "recall_cos_mean": float(cos.mean()),
         "lse_err_vs_dense": lse_err,
         "quantize_us": quant_us,
+        "residual_form": res_form,
     }
-    del reps, qd, Kd, Vd, Kq, sc, ws
+    if not residual_bits:
+        del reps
+    del qd, Kd, Vd, Kq, sc, ws
     torch.cuda.empty_cache()
     return res, (q, K, V)
 
@@ -259,6 +325,8 @@ def main() -> int:
                     help="second workload reported alongside ('' for none)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--residual-bits", type=int, default=2, choices=(0, 2, 4),
+                    help="also time the residual storage form on the primary workload (0: no)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (no graph capture), e.g. under counter tools")
     ap.add_argument("--rotation-mib", type=int, default=1024,
@@ -285,9 +353,13 @@ def main() -> int:
     delta = args.delta if args.delta is not None else w.deltas[0]
     t_wall = time.time()
     prim, host = run_workload(w, delta, args.steps, args.warmup, args.rotation_mib,
-                              graphs=not args.eager)
+                              graphs=not args.eager, residual_bits=args.residual_bits)
     log(f"{w.name}: sparse {prim['sparse_us']:.1f} us, dense {prim['dense_us']:.1f} us, "
         f"{prim['sparse_GBps']:.0f} GB/s, keep {prim['union_keep']:.4f}")
+    if prim["residual_form"]:
+        rf = prim["residual_form"]
+        log(f"{w.name} residual form: sparse {rf['sparse_us']:.1f} us, {rf['GBps']:.0f} GB/s, "
+            f"{rf['speedup_vs_dense_bf16']:.2f}x vs dense")
     sec = None
     if args.secondary and not args.no_secondary and args.secondary != args.workload:
         w2 = W.WORKLOADS[args.secondary]

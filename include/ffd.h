@@ -124,6 +124,40 @@ ffd_status ffd_decode_dense(const ffd_dims* dims, const void* q, const void* K, 
                             int32_t block, float* out, float* lse, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Residual storage form of the keys (Sec. 3.1 and Fig. 2: a low-bit "thumbnail" plus an 8-bit
+ * residual replace the 16-bit keys of full blocks; Alg. 1 rebuilds each kept key with Dequant,
+ * Eq. 4 being the same score written as q.k_quant + q.k_res).
+ * Writes, for every block completed by tokens [tok_begin, tok_end) (as in ffd_quantize_k_append):
+ *   Kc         [B, Hkv, seq_cap, d*bits/8] uint8: thumbnail codes, channel c at bit
+ *              (c % (8/bits)) * bits of byte c / (8/bits) of the token row (App. A quantizer
+ *              with 2^bits levels: value (u - (2^bits-1)/2) * s; bits = 2 is App. A exactly)
+ *   scales     [B, Hkv, seq_cap/T, d] fp32: thumbnail scale s = RN(max|x| / ((2^bits-1)/2))
+ *   Kr         [B, Hkv, seq_cap, d] int8: residual code of r = RN(x - RN((u - half) s)),
+ *              clamp(rint(RN(r * RN(127 / max|r|))), -127, 127), max over the block's T tokens
+ *   res_scales [B, Hkv, seq_cap/T, d] fp32: s_r = RN(max|r| / 127) (0 when max|r| = 0)
+ * K must be bf16 (dims.dtype == FFD_BF16); bits must be 2 or 4 (else FFD_ERR_UNSUPPORTED).
+ * Rebuilt key (Dequant): (u - half) * s + r_q * s_r, within s_r / 2 of the stored key.
+ */
+ffd_status ffd_quantize_k_residual_append(const ffd_dims* dims, const void* K, int32_t tok_begin,
+                                          int32_t tok_end, int32_t block, int32_t bits,
+                                          uint8_t* Kc, float* scales, int8_t* Kr,
+                                          float* res_scales, hipStream_t stream);
+
+/*
+ * Sparse decode step in the residual storage form: the scan reads the bits-wide thumbnail; the
+ * refinement attends over the kept blocks with Dequant keys (fp32, fed to the bf16 MFMA as a
+ * high/low bf16 pair) and bf16 values.  K_tail [B, Hkv, seq_cap, d] bf16 supplies the keys of
+ * the partial tail block (rows floor(L/T)*T .. L-1 only; NULL is allowed when L % T == 0).
+ * Same outputs, workspace and errors as ffd_decode_sparse; q and V bf16 only.
+ */
+ffd_status ffd_decode_sparse_residual(const ffd_dims* dims, const void* q, const void* K_tail,
+                                      const void* V, const uint8_t* Kc, const float* scales,
+                                      const int8_t* Kr, const float* res_scales, int32_t bits,
+                                      float delta, int32_t block, float* out, float* lse,
+                                      uint8_t* keep_mask, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
 /* Workspace bytes needed by ffd_decode_sparse / ffd_decode_dense for these dims and block
  * (the maximum of the two); 0 for invalid dims.  The size depends on the split count, which the
  * environment variable FFD_NUM_SPLITS (a positive integer) overrides. */

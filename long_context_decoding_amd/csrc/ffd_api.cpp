@@ -85,19 +85,27 @@ ffd_status finish(hipError_t e) { return e == hipSuccess ? FFD_OK : FFD_ERR_HIP;
 ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, const void* V,
                          const uint8_t* Kq, const float* scales, float delta, int32_t block,
                          float* out, float* lse, uint8_t* keep_mask, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream, bool sparse)
+                         size_t workspace_bytes, hipStream_t stream, bool sparse,
+                         const int8_t* Kr = nullptr, const float* res_scales = nullptr,
+                         int bits = 0)
 {
+    const bool res = bits != 0;
     ffd_status st = check_dims(dims, block);
     if (st != FFD_OK) return st;
+    if (res && (dims->dtype != FFD_BF16 || (bits != 2 && bits != 4))) return FFD_ERR_UNSUPPORTED;
     if (dims->batch == 0) return FFD_OK;
-    if (!q || !K || !V || !out) return FFD_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(out) ||
+    // the residual form reads 16-bit keys only for a partial tail block
+    const bool need_K = !res || dims->seq_len % block != 0;
+    if (!q || (need_K && !K) || !V || !out) return FFD_ERR_INVALID_ARG;
+    if (!aligned16(q) || (K && !aligned16(K)) || !aligned16(V) || !aligned16(out) ||
         (lse && !aligned16(lse)) || (keep_mask && !aligned16(keep_mask)))
         return FFD_ERR_INVALID_ARG;
     if (sparse) {
         if (!Kq || !scales || !aligned16(Kq) || !aligned16(scales)) return FFD_ERR_INVALID_ARG;
         if (isnan(delta) || delta < 0.0f) return FFD_ERR_INVALID_ARG;
     }
+    if (res && (!Kr || !res_scales || !aligned16(Kr) || !aligned16(res_scales)))
+        return FFD_ERR_INVALID_ARG;
     const int S = splits_for(dims, block);
     const WsLayout lay = ws_layout(dims, S);
     if (!workspace || !aligned16(workspace)) return FFD_ERR_WORKSPACE;
@@ -109,6 +117,8 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
     p.V = V;
     p.Kq = Kq;
     p.scales = scales;
+    p.Kr = Kr;
+    p.res_scales = res_scales;
     p.out = out;
     p.lse = lse;
     p.keep_mask = keep_mask;
@@ -130,7 +140,21 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
     p.delta = delta;
     p.kappa = (float)(0.5 / (127.0 * sqrt((double)kHeadDim)));
     p.c_log2 = (float)(1.4426950408889634 / sqrt((double)kHeadDim));
+    if (res) return finish(ffd::launch_decode_res(p, bits, stream));
     return finish(ffd::launch_decode(p, dims->dtype == FFD_BF16, sparse, stream));
+}
+
+// Blocks j with tok_begin <= (j+1)*block - 1 < tok_end, as [j_first, j_last]; validation shared
+// by both append calls.
+ffd_status append_range(const ffd_dims* dims, int32_t tok_begin, int32_t tok_end, int32_t block,
+                        int* j_first, int* j_last)
+{
+    ffd_status st = check_dims(dims, block);
+    if (st != FFD_OK) return st;
+    if (tok_begin < 0 || tok_end < tok_begin || tok_end > dims->seq_len) return FFD_ERR_INVALID_ARG;
+    *j_first = (tok_begin + 1 + block - 1) / block - 1;
+    *j_last = tok_end / block - 1;
+    return FFD_OK;
 }
 
 }  // namespace
@@ -210,6 +234,47 @@ ffd_status ffd_decode_sparse(const ffd_dims* dims, const void* q, const void* K,
 {
     return decode_common(dims, q, K, V, Kq, scales, delta, block, out, lse, keep_mask, workspace,
                          workspace_bytes, stream, true);
+}
+
+ffd_status ffd_quantize_k_residual_append(const ffd_dims* dims, const void* K, int32_t tok_begin,
+                                          int32_t tok_end, int32_t block, int32_t bits,
+                                          uint8_t* Kc, float* scales, int8_t* Kr,
+                                          float* res_scales, hipStream_t stream)
+{
+    int j_first, j_last;
+    ffd_status st = append_range(dims, tok_begin, tok_end, block, &j_first, &j_last);
+    if (st != FFD_OK) return st;
+    if (dims->dtype != FFD_BF16 || (bits != 2 && bits != 4)) return FFD_ERR_UNSUPPORTED;
+    if (dims->batch == 0) return FFD_OK;
+    if (!K || !Kc || !scales || !Kr || !res_scales || !aligned16(K) || !aligned16(Kc) ||
+        !aligned16(scales) || !aligned16(Kr) || !aligned16(res_scales))
+        return FFD_ERR_INVALID_ARG;
+    if (j_last < j_first) return FFD_OK;
+    ffd::QuantParams p{};
+    p.K = K;
+    p.Kq = Kc;
+    p.scales = scales;
+    p.Kr = Kr;
+    p.res_scales = res_scales;
+    p.B = dims->batch;
+    p.Hkv = dims->n_kv_heads;
+    p.cap = dims->seq_cap;
+    p.T = block;
+    p.j_first = j_first;
+    p.n_blocks = j_last - j_first + 1;
+    return finish(ffd::launch_quantize_res(p, bits, stream));
+}
+
+ffd_status ffd_decode_sparse_residual(const ffd_dims* dims, const void* q, const void* K_tail,
+                                      const void* V, const uint8_t* Kc, const float* scales,
+                                      const int8_t* Kr, const float* res_scales, int32_t bits,
+                                      float delta, int32_t block, float* out, float* lse,
+                                      uint8_t* keep_mask, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream)
+{
+    if (bits == 0) return FFD_ERR_UNSUPPORTED;
+    return decode_common(dims, q, K_tail, V, Kc, scales, delta, block, out, lse, keep_mask,
+                         workspace, workspace_bytes, stream, true, Kr, res_scales, bits);
 }
 
 ffd_status ffd_decode_dense(const ffd_dims* dims, const void* q, const void* K, const void* V,

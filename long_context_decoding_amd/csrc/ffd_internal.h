@@ -18,8 +18,10 @@ struct DecodeParams {
     const void* q;
     const void* K;
     const void* V;
-    const uint8_t* Kq;
+    const uint8_t* Kq;      // scanned codes (4 bits; 2 or 4 bits in the residual form)
     const float* scales;
+    const int8_t* Kr;       // residual form: 8-bit residual codes [B*Hkv][cap][d]
+    const float* res_scales;  // residual form: residual scales [B*Hkv][cap/T][d]
     float* out;
     float* lse;
     uint8_t* keep_mask;
@@ -41,6 +43,8 @@ struct QuantParams {
     const void* K;
     uint8_t* Kq;
     float* scales;
+    int8_t* Kr;         // residual form only
+    float* res_scales;  // residual form only
     int B, Hkv, cap, T;
     int j_first, n_blocks;  // blocks j_first .. j_first + n_blocks - 1
 };
@@ -48,6 +52,8 @@ struct QuantParams {
 // Launchers (ffd_kernels.hip).  Return the hipError_t of the launch.
 hipError_t launch_decode(const DecodeParams& p, bool bf16, bool sparse, hipStream_t stream);
 hipError_t launch_quantize(const QuantParams& p, bool bf16, hipStream_t stream);
+hipError_t launch_decode_res(const DecodeParams& p, int bits, hipStream_t stream);
+hipError_t launch_quantize_res(const QuantParams& p, int bits, hipStream_t stream);
 hipError_t launch_zero_counters(uint32_t* counters, int n, hipStream_t stream);
 
 }  // namespace ffd

@@ -5,6 +5,10 @@
 //
 //   quantize_kernel  App. A quantizer (16 levels) of each completed key block -> packed int4 codes
 //                    and one fp32 scale per (block, channel).
+//   quantize_res_kernel
+//                    the residual storage form (Sec. 3.1, Fig. 2): App. A thumbnail at 2 or 4 bits
+//                    plus a symmetric 8-bit code of the residual x - (u - half) s, both with one
+//                    fp32 scale per (block, channel).
 //   decode_kernel    one work-group per (sequence, kv head, split of the sequence):
 //                      scan     int4 codes x int8-requantized (q . s) on the int8 MFMA (Alg. 1 scan)
 //                      select   pseudo-max over the sink and local blocks (Eq. 3), keep a block
@@ -15,6 +19,10 @@
 //                               (sequence, kv head) merges the splits' partials with the
 //                               log-sum-exp rule (split-KV decoding, FTF Sec. 2)
 //                    The dense baseline is the same kernel with every block kept and no scan.
+//                    In the residual storage form the scan reads the 2- or 4-bit thumbnail and the
+//                    exact stage rebuilds each kept key (Alg. 1 Dequant) from thumbnail and
+//                    residual, as a bf16 high/low pair, so that q.k_quant + q.k_res (Eq. 4) is
+//                    accumulated on the bf16 MFMA.
 //
 // Wave layout conventions (wave64):
 //   lane = 16 * kg + col, kg = lane >> 4 in 0..3, col = lane & 15.
@@ -75,6 +83,15 @@ __device__ __forceinline__ void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+template <bool C, class A, class B>
+struct pick {
+    typedef A type;
+};
+template <class A, class B>
+struct pick<false, A, B> {
+    typedef B type;
+};
+
 __device__ __forceinline__ float bf16_lo(u32 x) { return as_f((int)(x << 16)); }
 __device__ __forceinline__ float bf16_hi(u32 x) { return as_f((int)(x & 0xFFFF0000u)); }
 
@@ -88,26 +105,39 @@ struct __attribute__((aligned(16))) WaveScratch {
     float f[G];              // per-head scan factor RN(W * kappa)
     int wsum[G];             // per-head sum of the requantized weights
     float alpha[16];         // per-head rescale factor of the current tile
+    float4 rsc[64];          // residual form: the current block's s (lanes 0-31), s_r (32-63)
 };
 
 // ------------------------------------------------------------------------------------------
 // Scan of one full block (FTF Alg. 1, scan stage; App. B Eq. 8 for what it approximates).
 // ------------------------------------------------------------------------------------------
-template <int T>
-struct ScanRegs {
-    uint4 kq[T / 16];  // 16 packed bytes of token row (16*i + col), bytes kg*16 .. kg*16+15
-    float4 s0, s1;     // scales of channels 8*col .. 8*col+7
+template <int BITS>
+struct CodeSlice;  // the packed codes of 32 channels of one token row
+template <>
+struct CodeSlice<4> {
+    typedef uint4 type;
+};
+template <>
+struct CodeSlice<2> {
+    typedef uint2 type;
 };
 
-template <int T>
-__device__ __forceinline__ void scan_load(ScanRegs<T>& r, const uint8_t* __restrict__ kq_blk,
+template <int T, int BITS>
+struct ScanRegs {
+    typename CodeSlice<BITS>::type kq[T / 16];  // token row (16*i + col), channels 32*kg .. +31
+    float4 s0, s1;                              // scales of channels 8*col .. 8*col+7
+};
+
+template <int T, int BITS>
+__device__ __forceinline__ void scan_load(ScanRegs<T, BITS>& r, const uint8_t* __restrict__ kq_blk,
                                           const float* __restrict__ sc_blk, int lane)
 {
     const int col = lane & 15, kg = lane >> 4;
+    constexpr int RB = D * BITS / 8, CB = 32 * BITS / 8;  // bytes per row, per 32 channels
 #pragma unroll
     for (int i = 0; i < T / 16; ++i)
-        r.kq[i] = *reinterpret_cast<const uint4*>(kq_blk + (size_t)(i * 16 + col) * (D / 2) +
-                                                  kg * 16);
+        r.kq[i] = *reinterpret_cast<const typename CodeSlice<BITS>::type*>(
+            kq_blk + (size_t)(i * 16 + col) * RB + kg * CB);
     const float4* sp = reinterpret_cast<const float4*>(sc_blk + col * 8);
     r.s0 = sp[0];
     r.s1 = sp[1];
@@ -117,14 +147,17 @@ __device__ __forceinline__ void scan_load(ScanRegs<T>& r, const uint8_t* __restr
 // handles head kg (+4 for G = 8), 8 channels 8*col..8*col+7.  Result valid in lanes with
 // col < G (head col), identical across kg.
 //
-// The A operand unpacks each packed dword d (channels c..c+7, two per byte) into
-// lo = d & 0x0F0F0F0F (channels c, c+2, c+4, c+6) and hi = (d >> 4) & 0x0F0F0F0F (c+1, c+3,
-// c+5, c+7); the B operand stores the requantized weights in that same channel order.
-// Codes enter as u in 0..15 (positive int8), so D_t = sum_c wi_c u_tc and
-// E_t = sum_c wi_c (2 u_tc - 15) = 2 D_t - 15 sum_c wi_c, all exact in int32.
-template <int T, int G>
-__device__ __forceinline__ float scan_compute(const ScanRegs<T>& r, const float (&qw)[(G + 3) / 4][8],
-                                              float kappa, WaveScratch<G>& ws, int lane)
+// The A operand holds 16 channels c0..c0+15 per 16 bytes.  At 4 bits each packed dword
+// (channels c..c+7, two per byte) unpacks into lo = d & 0x0F0F0F0F (channels c, c+2, c+4, c+6)
+// and hi = (d >> 4) & 0x0F0F0F0F (c+1, c+3, c+5, c+7); at 2 bits a dword (channels c..c+15,
+// four per byte) unpacks into (d >> 2m) & 0x03030303 (channels c+m, c+m+4, c+m+8, c+m+12),
+// m = 0..3.  The B operand stores the requantized weights in the same channel order.
+// Codes enter as u in 0..2^BITS-1 (positive int8), so D_t = sum_c wi_c u_tc and
+// E_t = sum_c wi_c (2 u_tc - (2^BITS - 1)) = 2 D_t - (2^BITS - 1) sum_c wi_c, exact in int32.
+template <int T, int G, int BITS>
+__device__ __forceinline__ float scan_compute(const ScanRegs<T, BITS>& r,
+                                              const float (&qw)[(G + 3) / 4][8], float kappa,
+                                              WaveScratch<G>& ws, int lane)
 {
     constexpr int HPL = (G + 3) / 4;
     const int col = lane & 15, kg = lane >> 4;
@@ -155,14 +188,24 @@ __device__ __forceinline__ float scan_compute(const ScanRegs<T>& r, const float 
         }
         const int wsum =
             row16_sum(wi[0] + wi[1] + wi[2] + wi[3] + wi[4] + wi[5] + wi[6] + wi[7]);
-        const u32 d0 = (u32)(wi[0] & 255) | ((u32)(wi[2] & 255) << 8) |
-                       ((u32)(wi[4] & 255) << 16) | ((u32)(wi[6] & 255) << 24);
-        const u32 d1 = (u32)(wi[1] & 255) | ((u32)(wi[3] & 255) << 8) |
-                       ((u32)(wi[5] & 255) << 16) | ((u32)(wi[7] & 255) << 24);
         if (G >= 4 || h < G) {
-            // channel c = 8*col: kg' = c / 32, k-step = (c % 32) / 16, byte offset (c % 16)
+            // channel 8*col + i: kg' = col / 4, k-step (col % 4) / 2, offset 8 * (col % 2) + i
+            // within the k-step's 16 channels
             const int kgw = col >> 2, ks = (col & 3) >> 1;
-            *reinterpret_cast<uint2*>(&ws.wB[ks][h][kgw][(col & 1) * 8]) = make_uint2(d0, d1);
+            int8_t* dst = &ws.wB[ks][h][kgw][0];
+            if constexpr (BITS == 4) {
+                const u32 d0 = (u32)(wi[0] & 255) | ((u32)(wi[2] & 255) << 8) |
+                               ((u32)(wi[4] & 255) << 16) | ((u32)(wi[6] & 255) << 24);
+                const u32 d1 = (u32)(wi[1] & 255) | ((u32)(wi[3] & 255) << 8) |
+                               ((u32)(wi[5] & 255) << 16) | ((u32)(wi[7] & 255) << 24);
+                *reinterpret_cast<uint2*>(dst + (col & 1) * 8) = make_uint2(d0, d1);
+            } else {
+                // offset o = 8 * (col % 2) + i sits at byte 4 * (o % 4) + o / 4
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<uint16_t*>(dst + 4 * i + 2 * (col & 1)) =
+                        (uint16_t)((wi[i] & 255) | ((wi[i + 4] & 255) << 8));
+            }
             if (col == 0) {
                 ws.f[h] = __fmul_rn(W, kappa);
                 ws.wsum[h] = wsum;
@@ -173,15 +216,23 @@ __device__ __forceinline__ float scan_compute(const ScanRegs<T>& r, const float 
     const int hB = col % G;
     const v4i B0 = *reinterpret_cast<const v4i*>(&ws.wB[0][hB][kg][0]);
     const v4i B1 = *reinterpret_cast<const v4i*>(&ws.wB[1][hB][kg][0]);
-    constexpr u32 M = 0x0F0F0F0Fu;
     int dmax = -2147483647 - 1;
 #pragma unroll
     for (int i = 0; i < T / 16; ++i) {
-        const uint4 p = r.kq[i];
-        const v4i A0 = {(int)(p.x & M), (int)((p.x >> 4) & M), (int)(p.y & M),
-                        (int)((p.y >> 4) & M)};
-        const v4i A1 = {(int)(p.z & M), (int)((p.z >> 4) & M), (int)(p.w & M),
-                        (int)((p.w >> 4) & M)};
+        v4i A0, A1;
+        if constexpr (BITS == 4) {
+            constexpr u32 M = 0x0F0F0F0Fu;
+            const uint4 p = r.kq[i];
+            A0 = v4i{(int)(p.x & M), (int)((p.x >> 4) & M), (int)(p.y & M), (int)((p.y >> 4) & M)};
+            A1 = v4i{(int)(p.z & M), (int)((p.z >> 4) & M), (int)(p.w & M), (int)((p.w >> 4) & M)};
+        } else {
+            constexpr u32 M = 0x03030303u;
+            const uint2 p = r.kq[i];
+            A0 = v4i{(int)(p.x & M), (int)((p.x >> 2) & M), (int)((p.x >> 4) & M),
+                     (int)((p.x >> 6) & M)};
+            A1 = v4i{(int)(p.y & M), (int)((p.y >> 2) & M), (int)((p.y >> 4) & M),
+                     (int)((p.y >> 6) & M)};
+        }
         v4i acc = {0, 0, 0, 0};
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, B0, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, B1, acc, 0, 0, 0);
@@ -189,7 +240,7 @@ __device__ __forceinline__ float scan_compute(const ScanRegs<T>& r, const float 
     }
     dmax = max(dmax, __shfl_xor(dmax, 16));
     dmax = max(dmax, __shfl_xor(dmax, 32));
-    const int E = 2 * dmax - 15 * ws.wsum[hB];
+    const int E = 2 * dmax - ((1 << BITS) - 1) * ws.wsum[hB];
     const float shat = __fmul_rn((float)E, ws.f[hB]);
     wave_sync();
     return shat;
@@ -245,13 +296,12 @@ struct SoftState {
     float l;        // running sum of exp2(s - m) of head col % G
 };
 
-template <int G, bool BF16>
-__device__ __forceinline__ void tile_compute(const TileRegs<BF16>& r, const void* __restrict__ qrow,
-                                             SoftState<G>& st, WaveScratch<G>& ws, int t0, int L,
-                                             u32 kbits, float c_log2, int lane)
+// Scores S[token t0 + 4 kg + v][head col % G] of a 16-token tile with stored keys.
+template <bool BF16>
+__device__ __forceinline__ v4f tile_scores(const TileRegs<BF16>& r, const void* __restrict__ qrow,
+                                           int lane)
 {
-    const int col = lane & 15, kg = lane >> 4;
-    // scores S[token t0 + 4 kg + v][head col % G]
+    const int kg = lane >> 4;
     v4f acc = {0.f, 0.f, 0.f, 0.f};
     // B operand: query head col % G, read from LDS (channels 32 ks + 8 kg .. for bf16,
     // 32 kg + 4 i .. for fp32), the same channel slice as the key row in the A operand
@@ -273,6 +323,17 @@ __device__ __forceinline__ void tile_compute(const TileRegs<BF16>& r, const void
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r.k[i].w, qv.w, acc, 0, 0, 0);
         }
     }
+    return acc;
+}
+
+// Online softmax (base 2) of a tile's scores and P.V into the lane's running state.  r.v holds
+// the tile's values: 4 x uint4 of bf16 (token 4*kg + i, channels 8*col ..) or 8 x float4.
+template <int G, bool VBF16, typename TR>
+__device__ __forceinline__ void softmax_pv(v4f acc, const TR& r, SoftState<G>& st,
+                                           WaveScratch<G>& ws, int t0, int L, u32 kbits,
+                                           float c_log2, int lane)
+{
+    const int col = lane & 15, kg = lane >> 4;
     const bool head_keep = (kbits >> (col % G)) & 1u;
     float s2[4];
     float tmax = kNegInf;
@@ -319,7 +380,7 @@ __device__ __forceinline__ void tile_compute(const TileRegs<BF16>& r, const void
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         float vv[8];
-        if constexpr (BF16) {
+        if constexpr (VBF16) {
             const uint4 x = r.v[v];
             vv[0] = bf16_lo(x.x); vv[1] = bf16_hi(x.x);
             vv[2] = bf16_lo(x.y); vv[3] = bf16_hi(x.y);
@@ -339,6 +400,138 @@ __device__ __forceinline__ void tile_compute(const TileRegs<BF16>& r, const void
 #pragma unroll
             for (int c = 0; c < 8; ++c) st.o[h][c] = fmaf(pp[h][v], vv[c], st.o[h][c]);
     }
+}
+
+template <int G, bool BF16>
+__device__ __forceinline__ void tile_compute(const TileRegs<BF16>& r, const void* __restrict__ qrow,
+                                             SoftState<G>& st, WaveScratch<G>& ws, int t0, int L,
+                                             u32 kbits, float c_log2, int lane)
+{
+    softmax_pv<G, BF16>(tile_scores<BF16>(r, qrow, lane), r, st, ws, t0, L, kbits, c_log2, lane);
+}
+
+// ------------------------------------------------------------------------------------------
+// Exact attention on one 16-token tile in the residual storage form.  Lane (kg, col) holds
+// token row col, channels 32*kg .. 32*kg+31 (the A operand of k-step ks takes channels
+// 32*kg + 8*ks ..; the query side reads the same channels).
+// ------------------------------------------------------------------------------------------
+struct TileRes {
+    // full block: a[0] = the 32 channels' codes (16 B at 4 bits, 8 B + 8 unused at 2 bits),
+    // a[1..2] = their 8-bit residual codes, a[3] = 16 B of the block's scales (lanes 0-31: s of
+    // channels 4*lane .., lanes 32-63: s_r of channels 4*(lane-32) ..).  Tail block (no low-bit
+    // copy): a[0..3] = the 32 channels' 16-bit keys.
+    uint4 a[4];
+    uint4 v[4];  // as TileRegs<true>::v
+};
+
+template <int BITS>
+__device__ __forceinline__ void tile_load_res(TileRes& r, const uint8_t* __restrict__ kc_bg,
+                                              const float* __restrict__ sc_bg,
+                                              const int8_t* __restrict__ kr_bg,
+                                              const float* __restrict__ sr_bg,
+                                              const __bf16* __restrict__ kt_bg,
+                                              const __bf16* __restrict__ V_bg, int t0, int T,
+                                              bool tail, int lane)
+{
+    const int col = lane & 15, kg = lane >> 4;
+    constexpr int RB = D * BITS / 8, CB = 32 * BITS / 8;
+    const size_t row = (size_t)(t0 + col);
+    const size_t blk = (size_t)(t0 / T);
+    // the same four loads into the same registers whichever the source, so that the wait
+    // counter tracks them alike on both paths
+    const char* a0;
+    const char* a1;
+    const char* a2;
+    const char* a3;
+    if (tail) {
+        const __bf16* kt = kt_bg + row * D + kg * 32;
+        a0 = reinterpret_cast<const char*>(kt);
+        a1 = reinterpret_cast<const char*>(kt + 8);
+        a2 = reinterpret_cast<const char*>(kt + 16);
+        a3 = reinterpret_cast<const char*>(kt + 24);
+    } else {
+        a0 = reinterpret_cast<const char*>(kc_bg + row * RB + kg * CB);
+        a1 = reinterpret_cast<const char*>(kr_bg + row * D + kg * 32);
+        a2 = a1 + 16;
+        a3 = reinterpret_cast<const char*>(lane < 32 ? sc_bg + blk * D + lane * 4
+                                                     : sr_bg + blk * D + (lane - 32) * 4);
+    }
+    if constexpr (BITS == 4) {
+        r.a[0] = *reinterpret_cast<const uint4*>(a0);
+    } else {
+        const uint2 lo = *reinterpret_cast<const uint2*>(a0);
+        const uint2 hi = *reinterpret_cast<const uint2*>(tail ? a0 + 8 : a0);
+        r.a[0] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+    r.a[1] = *reinterpret_cast<const uint4*>(a1);
+    r.a[2] = *reinterpret_cast<const uint4*>(a2);
+    r.a[3] = *reinterpret_cast<const uint4*>(a3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r.v[i] = *reinterpret_cast<const uint4*>(V_bg + (size_t)(t0 + 4 * kg + i) * D + col * 8);
+}
+
+__device__ __forceinline__ u32 byte_of(const uint4& x, int b)
+{
+    const u32 w = (b >> 2) == 0 ? x.x : (b >> 2) == 1 ? x.y : (b >> 2) == 2 ? x.z : x.w;
+    return (w >> ((b & 3) * 8)) & 255u;
+}
+
+// Scores of a residual-form tile: Dequant k = RN(RN((u - half) s) + RN(r_q s_r)) in fp32 (Alg. 1),
+// split into bf16 k_hi = RN_bf16(k) and k_lo = RN_bf16(k - k_hi) (|k - k_hi - k_lo| <= 2^-16 |k|),
+// so that q.k_quant + q.k_res accumulates on the bf16 MFMA with fp32 sums (Eq. 4).
+template <int BITS, int G>
+__device__ __forceinline__ v4f tile_scores_res(const TileRes& r, const void* __restrict__ qrow,
+                                               WaveScratch<G>& ws, bool tail, int lane)
+{
+    const int kg = lane >> 4;
+    const __bf16* qb = static_cast<const __bf16*>(qrow) + kg * 32;
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    if (tail) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(v8bf, r.a[ks]), *reinterpret_cast<const v8bf*>(qb + ks * 8),
+                acc, 0, 0, 0);
+        return acc;
+    }
+    ws.rsc[lane] = __builtin_bit_cast(float4, r.a[3]);
+    wave_sync();
+    const float* sq = reinterpret_cast<const float*>(ws.rsc) + kg * 32;  // s of my channels
+    const float* sr = sq + 128;                                           // s_r of my channels
+    constexpr float half = (float)((1 << BITS) - 1) * 0.5f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        v8bf hi, lo;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = 8 * ks + i;  // channel 32*kg + c
+            u32 u;
+            if constexpr (BITS == 4) u = (byte_of(r.a[0], c >> 1) >> ((c & 1) * 4)) & 15u;
+            else u = (byte_of(r.a[0], c >> 2) >> ((c & 3) * 2)) & 3u;
+            const int rq = (int)(int8_t)byte_of(c < 16 ? r.a[1] : r.a[2], c & 15);
+            const float k = __fadd_rn(__fmul_rn((float)u - half, sq[c]),
+                                      __fmul_rn((float)rq, sr[c]));
+            const __bf16 kh = (__bf16)k;
+            hi[i] = kh;
+            lo[i] = (__bf16)__fsub_rn(k, (float)kh);
+        }
+        const v8bf qv = *reinterpret_cast<const v8bf*>(qb + ks * 8);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, qv, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, qv, acc, 0, 0, 0);
+    }
+    wave_sync();
+    return acc;
+}
+
+template <int G, int BITS>
+__device__ __forceinline__ void tile_compute_res(const TileRes& r, const void* __restrict__ qrow,
+                                                 SoftState<G>& st, WaveScratch<G>& ws, int t0,
+                                                 int L, u32 kbits, float c_log2, bool tail,
+                                                 int lane)
+{
+    softmax_pv<G, true>(tile_scores_res<BITS, G>(r, qrow, ws, tail, lane), r, st, ws, t0, L, kbits,
+                        c_log2, lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -409,17 +602,17 @@ __device__ __forceinline__ float2 ld_dev2(const float2* p)
 }
 
 // One work-group per (sequence b, kv head g, split of the sequence).  Phases:
-//   1. scan (sparse only): every full block of the split that is neither the sink nor the local
-//      block, plus the sink and local blocks themselves for the pseudo-max; items are dealt
-//      round-robin to the waves and software-pipelined two deep with unconditional (clamped)
-//      loads, so that the next item's loads stay in flight while the current one is computed;
-//   2. select (sparse only): threshold against pseudo-max - delta, forced blocks, compaction of
-//      the kept blocks into an LDS list;
+//   1. scan and select (sparse only): every wave scans the sink and local blocks (its own
+//      pseudo-max), then its share of the split's other full blocks, two items in flight, and
+//      applies the top-delta test to each block as soon as it is scanned;
+//   2. compaction of the kept blocks into a per-wave LDS list, in increasing order;
 //   3. exact attention over the kept blocks' 16-token tiles (pipelined the same way);
 //   4. merge of the waves' softmax states -> one (o, m, l) partial per query head;
 //   5. the last work-group of (b, g) to finish (atomic counter) merges the splits' partials
 //      with the log-sum-exp rule into out and lse, and resets the counter.
-template <int T, int G, bool BF16, bool SPARSE>
+// BITS is the width of the scanned codes; RES selects the residual storage form (thumbnail +
+// 8-bit residual instead of stored keys; bf16 values; sparse only).
+template <int T, int G, bool BF16, bool SPARSE, int BITS, bool RES>
 __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
 {
     __shared__ DecodeShared<G> sh;
@@ -442,7 +635,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
 
     const size_t esz = BF16 ? 2 : 4;
     const size_t kv_off = (size_t)bg * p.cap * D;
-    const char* Kbg = static_cast<const char*>(p.K) + kv_off * esz;
+    const char* Kbg = p.K ? static_cast<const char*>(p.K) + kv_off * esz : nullptr;
     const char* Vbg = static_cast<const char*>(p.V) + kv_off * esz;
     const int h0 = b * p.Hq + g * G;  // first query row of the group
 
@@ -484,7 +677,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
             }
         }
 
-        const uint8_t* kq_bg = p.Kq + (size_t)bg * p.cap * (D / 2);
+        const uint8_t* kq_bg = p.Kq + (size_t)bg * p.cap * (D * BITS / 8);
         const float* sc_bg = p.scales + (size_t)bg * (p.cap / T) * D;
         const int nf = p.n_full;
         const u32 all_heads = (1u << G) - 1u;
@@ -515,12 +708,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
         };
         if (n_items > 0) {
             float pro0 = 0.0f, theta = 0.0f;  // lanes < G: head = lane
-            auto load = [&](ScanRegs<T>& r, int k) {
+            auto load = [&](ScanRegs<T, BITS>& r, int k) {
                 const int j = block_of(k);
-                scan_load<T>(r, kq_bg + (size_t)j * T * (D / 2), sc_bg + (size_t)j * D, lane);
+                scan_load<T, BITS>(r, kq_bg + (size_t)j * T * (D * BITS / 8), sc_bg + (size_t)j * D,
+                                   lane);
             };
-            auto process = [&](const ScanRegs<T>& r, int k) {
-                const float shat = scan_compute<T, G>(r, qw, p.kappa, ws, lane);
+            auto process = [&](const ScanRegs<T, BITS>& r, int k) {
+                const float shat = scan_compute<T, G, BITS>(r, qw, p.kappa, ws, lane);
                 if (k == 0) {
                     pro0 = shat;
                 } else if (k == 1) {
@@ -541,7 +735,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
             // issued before the computation that follows it in program order (otherwise the
             // scheduler hoists that computation's first use of its buffer above the loads, and
             // the in-order wait counter then waits for the prefetch too).
-            ScanRegs<T> ra, rb;
+            ScanRegs<T, BITS> ra, rb;
             load(ra, 0);
             __builtin_amdgcn_sched_barrier(0);
             publish_q();
@@ -614,30 +808,52 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
                 }
                 t0 = (jb + off) * T + (it % NT) * 16;
             };
-            TileRegs<BF16> ta, tb;
+            typedef typename pick<RES, TileRes, TileRegs<BF16>>::type TR;
+            // residual form: tiles of full blocks are rebuilt from thumbnail + residual, the tiles
+            // of a partial tail block (no low-bit copy) read the 16-bit keys
+            const int full_end = p.n_full * T;
+            auto load_tile = [&](TR& r, int t0) {
+                if constexpr (RES)
+                    tile_load_res<BITS>(
+                        r, p.Kq + (size_t)bg * p.cap * (D * BITS / 8),
+                        p.scales + (size_t)bg * (p.cap / T) * D, p.Kr + (size_t)bg * p.cap * D,
+                        p.res_scales + (size_t)bg * (p.cap / T) * D,
+                        reinterpret_cast<const __bf16*>(Kbg), reinterpret_cast<const __bf16*>(Vbg),
+                        t0, T, t0 >= full_end, lane);
+                else
+                    tile_load<BF16>(r, Kbg, Vbg, t0, lane);
+            };
+            auto compute_tile = [&](const TR& r, int t0, u32 kb) {
+                if constexpr (RES)
+                    tile_compute_res<G, BITS>(r, qrow, st, ws, t0, p.L, kb, p.c_log2,
+                                              t0 >= full_end, lane);
+                else
+                    tile_compute<G, BF16>(r, qrow, st, ws, t0, p.L, kb, p.c_log2, lane);
+            };
+            TR ta, tb;
             int t0a, t0b;
             u32 kba, kbb;
             tile_of(0, t0a, kba);
-            tile_load<BF16>(ta, Kbg, Vbg, t0a, lane);
+            load_tile(ta, t0a);
             int k = 0;
             for (; k + 2 < n_w; k += 2) {
                 tile_of(k + 1, t0b, kbb);
-                tile_load<BF16>(tb, Kbg, Vbg, t0b, lane);
+                load_tile(tb, t0b);
                 __builtin_amdgcn_sched_barrier(0);
-                tile_compute<G, BF16>(ta, qrow, st, ws, t0a, p.L, kba, p.c_log2, lane);
+                compute_tile(ta, t0a, kba);
                 tile_of(k + 2, t0a, kba);
-                tile_load<BF16>(ta, Kbg, Vbg, t0a, lane);
+                load_tile(ta, t0a);
                 __builtin_amdgcn_sched_barrier(0);
-                tile_compute<G, BF16>(tb, qrow, st, ws, t0b, p.L, kbb, p.c_log2, lane);
+                compute_tile(tb, t0b, kbb);
             }
             if (k + 1 < n_w) {
                 tile_of(k + 1, t0b, kbb);
-                tile_load<BF16>(tb, Kbg, Vbg, t0b, lane);
+                load_tile(tb, t0b);
                 __builtin_amdgcn_sched_barrier(0);
-                tile_compute<G, BF16>(ta, qrow, st, ws, t0a, p.L, kba, p.c_log2, lane);
-                tile_compute<G, BF16>(tb, qrow, st, ws, t0b, p.L, kbb, p.c_log2, lane);
+                compute_tile(ta, t0a, kba);
+                compute_tile(tb, t0b, kbb);
             } else {
-                tile_compute<G, BF16>(ta, qrow, st, ws, t0a, p.L, kba, p.c_log2, lane);
+                compute_tile(ta, t0a, kba);
             }
         }
     }
@@ -895,14 +1111,75 @@ __global__ __launch_bounds__(128) void quantize_kernel(QuantParams p)
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// Residual storage form of the keys (Sec. 3.1, Fig. 2): App. A thumbnail at BITS bits and the
+// symmetric 8-bit code of the residual, per (block, channel); one thread per channel, the same
+// fp32 operations as the oracle: xh = RN((u - half) s), r = RN(x - xh), s_r = RN(max|r| / 127),
+// r_q = clamp(rint(RN(r * RN(127 / max|r|))), -127, 127).
+// ------------------------------------------------------------------------------------------
+template <int T, int BITS>
+__global__ __launch_bounds__(128) void quantize_res_kernel(QuantParams p)
+{
+    constexpr float half = (float)((1 << BITS) - 1) * 0.5f;
+    constexpr int top = (1 << BITS) - 1;
+    const int j = p.j_first + blockIdx.x;
+    const int bg = blockIdx.y;
+    const int c = threadIdx.x;
+    const size_t row0 = (size_t)bg * p.cap + (size_t)j * T;
+    const unsigned short* Kb = static_cast<const unsigned short*>(p.K);
+    float x[T];
+    float amax = 0.0f;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        x[t] = as_f((int)((u32)Kb[(row0 + t) * D + c] << 16));
+        amax = fmaxf(amax, fabsf(x[t]));
+    }
+    float s = 0.0f, inv = 0.0f;
+    if (amax > 0.0f) {
+        s = __fdiv_rn(amax, half);
+        inv = __fdiv_rn(half, amax);
+    }
+    // codes, and the residual in place of x
+    int u[T];
+    float ramax = 0.0f;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        int v = 1 << (BITS - 1);
+        if (amax > 0.0f) v = min(max((int)floorf(__fmul_rn(x[t], inv)) + (1 << (BITS - 1)), 0), top);
+        u[t] = v;
+        x[t] = __fsub_rn(x[t], __fmul_rn((float)v - half, s));
+        ramax = fmaxf(ramax, fabsf(x[t]));
+    }
+    float s_r = 0.0f, inv_r = 0.0f;
+    if (ramax > 0.0f) {
+        s_r = __fdiv_rn(ramax, 127.0f);
+        inv_r = __fdiv_rn(127.0f, ramax);
+    }
+    const size_t srow = ((size_t)bg * (p.cap / T) + j) * D + c;
+    p.scales[srow] = s;
+    p.res_scales[srow] = s_r;
+    constexpr int per = 8 / BITS;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        float rq = 0.0f;
+        if (ramax > 0.0f) rq = fminf(fmaxf(rintf(__fmul_rn(x[t], inv_r)), -127.0f), 127.0f);
+        p.Kr[(row0 + t) * D + c] = (int8_t)(int)rq;
+        // channel c's code sits at bit (c % per) * BITS of byte c / per
+        int byte = u[t];
+#pragma unroll
+        for (int i = 1; i < per; ++i) byte |= __shfl_down(u[t], i, per) << (i * BITS);
+        if (c % per == 0) p.Kq[(row0 + t) * (D * BITS / 8) + c / per] = (uint8_t)byte;
+    }
+}
+
 template <int T, int G, bool BF16>
 hipError_t launch_decode_t(const DecodeParams& p, bool sparse, hipStream_t stream)
 {
     const dim3 grid(p.B * p.Hkv * p.S), block(kWaves * 64);
     if (sparse)
-        hipLaunchKernelGGL((decode_kernel<T, G, BF16, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((decode_kernel<T, G, BF16, true, 4, false>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((decode_kernel<T, G, BF16, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((decode_kernel<T, G, BF16, false, 4, false>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
@@ -918,6 +1195,20 @@ hipError_t launch_decode_g(const DecodeParams& p, bool sparse, hipStream_t strea
     }
 }
 
+template <int T, int BITS>
+hipError_t launch_res_g(const DecodeParams& p, hipStream_t stream)
+{
+    const dim3 grid(p.B * p.Hkv * p.S), block(kWaves * 64);
+    switch (p.G) {
+    case 1: hipLaunchKernelGGL((decode_kernel<T, 1, true, true, BITS, true>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<T, 2, true, true, BITS, true>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<T, 4, true, true, BITS, true>), grid, block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<T, 8, true, true, BITS, true>), grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, bool bf16, bool sparse, hipStream_t stream)
@@ -929,6 +1220,30 @@ hipError_t launch_decode(const DecodeParams& p, bool bf16, bool sparse, hipStrea
         return bf16 ? launch_decode_g<128, true>(p, sparse, stream)
                     : launch_decode_g<128, false>(p, sparse, stream);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_res(const DecodeParams& p, int bits, hipStream_t stream)
+{
+    if (p.T == 64) return bits == 2 ? launch_res_g<64, 2>(p, stream) : launch_res_g<64, 4>(p, stream);
+    if (p.T == 128)
+        return bits == 2 ? launch_res_g<128, 2>(p, stream) : launch_res_g<128, 4>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_quantize_res(const QuantParams& p, int bits, hipStream_t stream)
+{
+    if (p.n_blocks <= 0) return hipSuccess;
+    const dim3 grid(p.n_blocks, p.B * p.Hkv), block(D);
+    if (p.T == 64) {
+        if (bits == 2) hipLaunchKernelGGL((quantize_res_kernel<64, 2>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((quantize_res_kernel<64, 4>), grid, block, 0, stream, p);
+    } else if (p.T == 128) {
+        if (bits == 2) hipLaunchKernelGGL((quantize_res_kernel<128, 2>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((quantize_res_kernel<128, 4>), grid, block, 0, stream, p);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_zero_counters(uint32_t* counters, int n, hipStream_t stream)

@@ -6,7 +6,8 @@ through ctypes, and raises on a non-OK status.  There is no fallback: if the lib
 or cannot be loaded, every call raises.
 
 Names follow the C ABI: ``quantize_k_append``, ``decode_sparse``, ``decode_dense``,
-``workspace_bytes``, ``workspace_init``, ``num_splits``.
+``quantize_k_residual_append``, ``decode_sparse_residual``, ``workspace_bytes``,
+``workspace_init``, ``num_splits``.
 """
 from __future__ import annotations
 
@@ -62,6 +63,11 @@ def lib():
         L.ffd_decode_sparse.restype = i32
         L.ffd_decode_dense.argtypes = [D, P, P, P, i32, P, P, P, sz, P]
         L.ffd_decode_dense.restype = i32
+        L.ffd_quantize_k_residual_append.argtypes = [D, P, i32, i32, i32, i32, P, P, P, P, P]
+        L.ffd_quantize_k_residual_append.restype = i32
+        L.ffd_decode_sparse_residual.argtypes = [D, P, P, P, P, P, P, P, i32, f32, i32, P, P, P, P,
+                                                 sz, P]
+        L.ffd_decode_sparse_residual.restype = i32
         _lib = L
     return _lib
 
@@ -227,4 +233,69 @@ def decode_dense(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, block: int, 
     _check(lib().ffd_decode_dense(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V), block,
                                   _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                   _stream(stream)))
+    return out, lse
+
+
+# ------------------------------------------------------------------------------------------
+# Residual storage form: low-bit thumbnail + 8-bit residual instead of 16-bit keys
+# ------------------------------------------------------------------------------------------
+def alloc_kres(K: torch.Tensor, block: int, bits: int):
+    """Zero-filled (Kc u8 [B,Hkv,cap,d*bits/8], scales f32 [B,Hkv,cap/block,d],
+    Kr int8 [B,Hkv,cap,d], res_scales f32 [B,Hkv,cap/block,d])."""
+    B, Hkv, cap, d = K.shape
+    dev = K.device
+    return (torch.zeros((B, Hkv, cap, d * bits // 8), dtype=torch.uint8, device=dev),
+            torch.zeros((B, Hkv, cap // block, d), dtype=torch.float32, device=dev),
+            torch.zeros((B, Hkv, cap, d), dtype=torch.int8, device=dev),
+            torch.zeros((B, Hkv, cap // block, d), dtype=torch.float32, device=dev))
+
+
+def _need_kres(K_shape, block, bits, Kc, sc, Kr, sr, device):
+    B, Hkv, cap, d = K_shape
+    _need(Kc, "Kc", torch.uint8, (B, Hkv, cap, d * bits // 8), device)
+    _need(sc, "scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d), device)
+    _need(Kr, "Kr", torch.int8, (B, Hkv, cap, d), device)
+    _need(sr, "res_scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d), device)
+
+
+def quantize_k_residual_append(K: torch.Tensor, tok_begin: int, tok_end: int, block: int,
+                               bits: int, kres, seq_len: int | None = None, stream=None) -> None:
+    """Thumbnail + residual of the blocks of K (bf16) completed by tokens [tok_begin, tok_end)."""
+    B, Hkv, cap, d = K.shape
+    _need(K, "K")
+    Kc, sc, Kr, sr = kres
+    _need_kres(K.shape, block, bits, Kc, sc, Kr, sr, K.device)
+    dims = make_dims(B, Hkv, Hkv, seq_len if seq_len is not None else cap, cap, _dtype_code(K), d)
+    _check(lib().ffd_quantize_k_residual_append(ctypes.byref(dims), _ptr(K), tok_begin, tok_end,
+                                                block, bits, _ptr(Kc), _ptr(sc), _ptr(Kr),
+                                                _ptr(sr), _stream(stream)))
+
+
+def decode_sparse_residual(q: torch.Tensor, K_tail: torch.Tensor | None, V: torch.Tensor, kres,
+                           bits: int, delta: float, block: int, seq_len: int,
+                           out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                           keep_mask: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None, want_lse: bool = True,
+                           stream=None):
+    """Sparse decode step in the residual storage form.  K_tail (bf16 [B,Hkv,cap,d]) supplies
+    the keys of a partial tail block and may be None when seq_len % block == 0."""
+    dims = dims_of(q, V, seq_len)
+    _need(V, "V", torch.bfloat16, None, V.device)
+    _need(q, "q", torch.bfloat16, None, V.device)
+    if K_tail is not None:
+        _need(K_tail, "K_tail", torch.bfloat16, V.shape, V.device)
+    Kc, sc, Kr, sr = kres
+    _need_kres(V.shape, block, bits, Kc, sc, Kr, sr, V.device)
+    out, lse = _decode_outputs(q, out, lse, want_lse)
+    if keep_mask is not None:
+        _need(keep_mask, "keep_mask", torch.uint8,
+              (q.shape[0], q.shape[1], math.ceil(seq_len / block)), q.device)
+    if workspace is None:
+        workspace = alloc_workspace(dims, block, q.device)
+    _need(workspace, "workspace", torch.uint8, None, q.device)
+    _check(lib().ffd_decode_sparse_residual(ctypes.byref(dims), _ptr(q), _ptr(K_tail), _ptr(V),
+                                            _ptr(Kc), _ptr(sc), _ptr(Kr), _ptr(sr), bits,
+                                            float(delta), block, _ptr(out), _ptr(lse),
+                                            _ptr(keep_mask), _ptr(workspace), workspace.numel(),
+                                            _stream(stream)))
     return out, lse

@@ -149,3 +149,27 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ffd, "_lib", None)
     with pytest.raises(FileNotFoundError):
         ffd.lib()
+
+
+def test_residual_validation(L):
+    d = dims()
+    n = ffd.workspace_bytes(d, 64)
+    dec = L.ffd_decode_sparse_residual
+    qa = L.ffd_quantize_k_residual_append
+
+    def call(dd=d, bits=2, Kt=None, Kr=A, delta=5.0, block=64):
+        return dec(ctypes.byref(dd), A, Kt, A, A, A, Kr, A, bits, delta, block, A, A, None, A, n,
+                   None)
+
+    assert call(bits=3) == ffd.FFD_ERR_UNSUPPORTED
+    assert call(bits=0) == ffd.FFD_ERR_UNSUPPORTED
+    assert call(dd=dims(dtype=ffd.FFD_F32)) == ffd.FFD_ERR_UNSUPPORTED
+    assert call(Kr=None) == ffd.FFD_ERR_INVALID_ARG
+    assert call(delta=float("nan")) == ffd.FFD_ERR_INVALID_ARG
+    # a partial tail block needs the 16-bit tail keys
+    assert call(dd=dims(seq_len=4000, seq_cap=4096)) == ffd.FFD_ERR_INVALID_ARG
+    assert qa(ctypes.byref(d), A, 0, 64, 64, 3, A, A, A, A, None) == ffd.FFD_ERR_UNSUPPORTED
+    assert qa(ctypes.byref(dims(dtype=ffd.FFD_F32)), A, 0, 64, 64, 2, A, A, A, A, None) == \
+        ffd.FFD_ERR_UNSUPPORTED
+    assert qa(ctypes.byref(d), A, 0, 64, 64, 2, A, A, None, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert qa(ctypes.byref(d), A, 0, 63, 64, 2, A, A, A, A, None) == ffd.FFD_OK  # no block
