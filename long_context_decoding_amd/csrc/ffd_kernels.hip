@@ -74,6 +74,74 @@ __device__ __forceinline__ int row16_sum(int x)
     return x;
 }
 
+// Exchanges across the 16-lane rows on the VALU (gfx950 permlane swaps, no LDS round trip).
+// The two results of permlane16_swap(x, x) hold, in every lane l, the values of lanes l & ~16 and
+// l | 16, so an operation on them forms op(x_l, x_{l^16}) with the same operand order in both
+// lanes of a pair; permlane32_swap does the same for l ^ 32.
+__device__ __forceinline__ void pair16(int x, int& a, int& b)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap((u32)x, (u32)x, false, false);
+    a = (int)r[0];
+    b = (int)r[1];
+}
+__device__ __forceinline__ void pair32(int x, int& a, int& b)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap((u32)x, (u32)x, false, false);
+    a = (int)r[0];
+    b = (int)r[1];
+}
+__device__ __forceinline__ float fmax16(float x)
+{
+    int a, b;
+    pair16(as_i(x), a, b);
+    return fmaxf(as_f(a), as_f(b));
+}
+__device__ __forceinline__ float fmax32(float x)
+{
+    int a, b;
+    pair32(as_i(x), a, b);
+    return fmaxf(as_f(a), as_f(b));
+}
+__device__ __forceinline__ float fsum16(float x)
+{
+    int a, b;
+    pair16(as_i(x), a, b);
+    return as_f(a) + as_f(b);
+}
+__device__ __forceinline__ float fsum32(float x)
+{
+    int a, b;
+    pair32(as_i(x), a, b);
+    return as_f(a) + as_f(b);
+}
+__device__ __forceinline__ int imax16(int x)
+{
+    int a, b;
+    pair16(x, a, b);
+    return max(a, b);
+}
+__device__ __forceinline__ int imax32(int x)
+{
+    int a, b;
+    pair32(x, a, b);
+    return max(a, b);
+}
+
+// Value of lane h of this lane's 16-lane row (DPP row_newbcast), h < 8 known after unrolling.
+__device__ __forceinline__ float row_bcast(float x, int h)
+{
+    switch (h) {
+    case 0: return as_f(dpp<0x150>(as_i(x)));
+    case 1: return as_f(dpp<0x151>(as_i(x)));
+    case 2: return as_f(dpp<0x152>(as_i(x)));
+    case 3: return as_f(dpp<0x153>(as_i(x)));
+    case 4: return as_f(dpp<0x154>(as_i(x)));
+    case 5: return as_f(dpp<0x155>(as_i(x)));
+    case 6: return as_f(dpp<0x156>(as_i(x)));
+    default: return as_f(dpp<0x157>(as_i(x)));
+    }
+}
+
 // Orders this wave's LDS accesses (LDS executes one wave's instructions in order; this only
 // stops the compiler from moving accesses across the point).
 __device__ __forceinline__ void wave_sync()
@@ -101,10 +169,8 @@ __device__ __forceinline__ float bf16_hi(u32 x) { return as_f((int)(x & 0xFFFF00
 template <int G>
 struct __attribute__((aligned(16))) WaveScratch {
     int8_t wB[2][G][4][16];  // scan MFMA B operand: [k-step][head][kg][16 int8]
-    v4f P[4][16];            // probabilities exchanged from the score layout: [kg][col]
     float f[G];              // per-head scan factor RN(W * kappa)
     int wsum[G];             // per-head sum of the requantized weights
-    float alpha[16];         // per-head rescale factor of the current tile
     float4 rsc[64];          // residual form: the current block's s (lanes 0-31), s_r (32-63)
 };
 
@@ -238,8 +304,7 @@ __device__ __forceinline__ float scan_compute(const ScanRegs<T, BITS>& r,
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, B1, acc, 0, 0, 0);
         dmax = max(dmax, max(max(acc[0], acc[1]), max(acc[2], acc[3])));
     }
-    dmax = max(dmax, __shfl_xor(dmax, 16));
-    dmax = max(dmax, __shfl_xor(dmax, 32));
+    dmax = imax32(imax16(dmax));
     const int E = 2 * dmax - ((1 << BITS) - 1) * ws.wsum[hB];
     const float shat = __fmul_rn((float)E, ws.f[hB]);
     wave_sync();
@@ -296,22 +361,21 @@ struct SoftState {
     float l;        // running sum of exp2(s - m) of head col % G
 };
 
-// Scores S[token t0 + 4 kg + v][head col % G] of a 16-token tile with stored keys.
+// Scores S[token t0 + 4 kg + v][head col % G] of a 16-token tile with stored keys.  B operand:
+// query head col % G, the same channel slice as the key row in the A operand: for bf16 the four
+// k-steps' 8 channels 32 ks + 8 kg .. held in registers (qv), for fp32 channels 32 kg + 4 i ..
+// read from the query row in LDS.
 template <bool BF16>
 __device__ __forceinline__ v4f tile_scores(const TileRegs<BF16>& r, const void* __restrict__ qrow,
-                                           int lane)
+                                           const v8bf* qv, int lane)
 {
     const int kg = lane >> 4;
     v4f acc = {0.f, 0.f, 0.f, 0.f};
-    // B operand: query head col % G, read from LDS (channels 32 ks + 8 kg .. for bf16,
-    // 32 kg + 4 i .. for fp32), the same channel slice as the key row in the A operand
     if constexpr (BF16) {
-        const __bf16* qb = static_cast<const __bf16*>(qrow);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(v8bf, r.k[ks]),
-                *reinterpret_cast<const v8bf*>(qb + ks * 32 + kg * 8), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, r.k[ks]), qv[ks],
+                                                          acc, 0, 0, 0);
     } else {
         const float* qf = static_cast<const float*>(qrow);
 #pragma unroll
@@ -329,9 +393,8 @@ __device__ __forceinline__ v4f tile_scores(const TileRegs<BF16>& r, const void* 
 // Online softmax (base 2) of a tile's scores and P.V into the lane's running state.  r.v holds
 // the tile's values: 4 x uint4 of bf16 (token 4*kg + i, channels 8*col ..) or 8 x float4.
 template <int G, bool VBF16, typename TR>
-__device__ __forceinline__ void softmax_pv(v4f acc, const TR& r, SoftState<G>& st,
-                                           WaveScratch<G>& ws, int t0, int L, u32 kbits,
-                                           float c_log2, int lane)
+__device__ __forceinline__ void softmax_pv(v4f acc, const TR& r, SoftState<G>& st, int t0, int L,
+                                           u32 kbits, float c_log2, int lane)
 {
     const int col = lane & 15, kg = lane >> 4;
     const bool head_keep = (kbits >> (col % G)) & 1u;
@@ -343,8 +406,7 @@ __device__ __forceinline__ void softmax_pv(v4f acc, const TR& r, SoftState<G>& s
         s2[v] = valid ? acc[v] * c_log2 : kNegInf;
         tmax = fmaxf(tmax, s2[v]);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = fmax32(fmax16(tmax));
     const float m_new = fmaxf(st.m, tmax);
     const float alpha = (m_new == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(st.m - m_new);
     v4f p;
@@ -354,23 +416,20 @@ __device__ __forceinline__ void softmax_pv(v4f acc, const TR& r, SoftState<G>& s
         p[v] = (s2[v] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(s2[v] - m_new);
         psum += p[v];
     }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
+    psum = fsum32(fsum16(psum));
     st.l = st.l * alpha + psum;
     st.m = m_new;
 
-    // move probabilities to the PV layout: lane needs p[h][4 kg + v] for every head h
-    ws.P[kg][col] = p;
-    if (kg == 0) ws.alpha[col] = alpha;
-    wave_sync();
-    v4f pp[G];
+    // move probabilities to the PV layout: lane (kg, col) needs p[4 kg + v] of every head h of
+    // the group, and its rescale factor, from lane h of its own row (column h of the score tile)
+    float pp[G][4];
     float al[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        pp[h] = ws.P[kg][h];
-        al[h] = ws.alpha[h];
+        al[h] = row_bcast(alpha, h);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) pp[h][v] = row_bcast(p[v], h);
     }
-    wave_sync();
 
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -404,10 +463,10 @@ __device__ __forceinline__ void softmax_pv(v4f acc, const TR& r, SoftState<G>& s
 
 template <int G, bool BF16>
 __device__ __forceinline__ void tile_compute(const TileRegs<BF16>& r, const void* __restrict__ qrow,
-                                             SoftState<G>& st, WaveScratch<G>& ws, int t0, int L,
+                                             const v8bf* qv, SoftState<G>& st, int t0, int L,
                                              u32 kbits, float c_log2, int lane)
 {
-    softmax_pv<G, BF16>(tile_scores<BF16>(r, qrow, lane), r, st, ws, t0, L, kbits, c_log2, lane);
+    softmax_pv<G, BF16>(tile_scores<BF16>(r, qrow, qv, lane), r, st, t0, L, kbits, c_log2, lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -480,19 +539,18 @@ __device__ __forceinline__ u32 byte_of(const uint4& x, int b)
 // Scores of a residual-form tile: Dequant k = RN(RN((u - half) s) + RN(r_q s_r)) in fp32 (Alg. 1),
 // split into bf16 k_hi = RN_bf16(k) and k_lo = RN_bf16(k - k_hi) (|k - k_hi - k_lo| <= 2^-16 |k|),
 // so that q.k_quant + q.k_res accumulates on the bf16 MFMA with fp32 sums (Eq. 4).
+// qv: the query operand of k-step ks, channels 32 kg + 8 ks .., in registers.
 template <int BITS, int G>
-__device__ __forceinline__ v4f tile_scores_res(const TileRes& r, const void* __restrict__ qrow,
+__device__ __forceinline__ v4f tile_scores_res(const TileRes& r, const v8bf* qv,
                                                WaveScratch<G>& ws, bool tail, int lane)
 {
     const int kg = lane >> 4;
-    const __bf16* qb = static_cast<const __bf16*>(qrow) + kg * 32;
     v4f acc = {0.f, 0.f, 0.f, 0.f};
     if (tail) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(v8bf, r.a[ks]), *reinterpret_cast<const v8bf*>(qb + ks * 8),
-                acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, r.a[ks]), qv[ks],
+                                                          acc, 0, 0, 0);
         return acc;
     }
     ws.rsc[lane] = __builtin_bit_cast(float4, r.a[3]);
@@ -516,21 +574,20 @@ __device__ __forceinline__ v4f tile_scores_res(const TileRes& r, const void* __r
             hi[i] = kh;
             lo[i] = (__bf16)__fsub_rn(k, (float)kh);
         }
-        const v8bf qv = *reinterpret_cast<const v8bf*>(qb + ks * 8);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, qv, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, qv, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, qv[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, qv[ks], acc, 0, 0, 0);
     }
     wave_sync();
     return acc;
 }
 
 template <int G, int BITS>
-__device__ __forceinline__ void tile_compute_res(const TileRes& r, const void* __restrict__ qrow,
+__device__ __forceinline__ void tile_compute_res(const TileRes& r, const v8bf* qv,
                                                  SoftState<G>& st, WaveScratch<G>& ws, int t0,
                                                  int L, u32 kbits, float c_log2, bool tail,
                                                  int lane)
 {
-    softmax_pv<G, true>(tile_scores_res<BITS, G>(r, qrow, ws, tail, lane), r, st, ws, t0, L, kbits,
+    softmax_pv<G, true>(tile_scores_res<BITS, G>(r, qv, ws, tail, lane), r, st, t0, L, kbits,
                         c_log2, lane);
 }
 
@@ -562,16 +619,16 @@ struct __attribute__((aligned(16))) DecodeShared {
 
 __device__ __forceinline__ float wave_max(float x)
 {
-    x = row16_max(x);
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+    return fmax32(fmax16(row16_max(x)));
 }
 
 __device__ __forceinline__ float wave_sum(float x)
 {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
-    return x;
+    x += as_f(dpp<0xB1>(as_i(x)));
+    x += as_f(dpp<0x4E>(as_i(x)));
+    x += as_f(dpp<0x141>(as_i(x)));
+    x += as_f(dpp<0x140>(as_i(x)));
+    return fsum32(fsum16(x));
 }
 
 // Device-scope (agent) relaxed atomic loads and stores: on gfx950 these are plain global loads
@@ -779,8 +836,17 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
         __syncthreads();  // query rows in LDS
     }
 
-    // the exact stage reads head col % G's query row from LDS
+    // the exact stage reads head col % G's query row from LDS: for 16-bit inputs once, into
+    // the MFMA operand registers of the four k-steps (channels 32 ks + 8 kg .. for stored keys,
+    // 32 kg + 8 ks .. in the residual form), for fp32 at every tile
     const void* qrow = reinterpret_cast<const char*>(sh.q) + (size_t)(col % G) * D * esz;
+    v8bf qv[4];
+    if constexpr (BF16) {
+        const __bf16* qb = static_cast<const __bf16*>(qrow);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            qv[ks] = *reinterpret_cast<const v8bf*>(qb + (RES ? kg * 32 + ks * 8 : ks * 32 + kg * 8));
+    }
 
     // exact attention over the kept blocks, 16-token tiles dealt round-robin to the waves,
     // pipelined like the scan (two tiles in flight, no load past the last tile)
@@ -825,10 +891,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
             };
             auto compute_tile = [&](const TR& r, int t0, u32 kb) {
                 if constexpr (RES)
-                    tile_compute_res<G, BITS>(r, qrow, st, ws, t0, p.L, kb, p.c_log2,
+                    tile_compute_res<G, BITS>(r, qv, st, ws, t0, p.L, kb, p.c_log2,
                                               t0 >= full_end, lane);
                 else
-                    tile_compute<G, BF16>(r, qrow, st, ws, t0, p.L, kb, p.c_log2, lane);
+                    tile_compute<G, BF16>(r, qrow, qv, st, t0, p.L, kb, p.c_log2, lane);
             };
             TR ta, tb;
             int t0a, t0b;
@@ -864,8 +930,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             float x = st.o[h][c];
-            x += __shfl_xor(x, 16);
-            x += __shfl_xor(x, 32);
+            x = fsum32(fsum16(x));
             st.o[h][c] = x;
         }
 
