@@ -86,7 +86,7 @@ def bytes_dense(w) -> int:
 # GPU measurement
 # ------------------------------------------------------------------------------------------
 def run_workload(w, delta: float, steps: int, warmup: int, min_rotation_mib: int = 1024,
-                 graphs: bool = True, residual_bits: int = 0):
+                 graphs: bool = True, residual_bits: int = 0, decode_loop: bool = False):
     """Time one decode step of workload w on cuda:0.
 
     Steps run back to back over R copies of the KV cache (like R layers of a model, each with
@@ -202,6 +202,44 @@ def run_workload(w, delta: float, steps: int, warmup: int, min_rotation_mib: int
     us_s_warm = timed(sparse, steps, rotate=False)
     us_d_warm = timed(dense, steps, rotate=False)
 
+    loop = None
+    if decode_loop and R >= 2:
+        # Decode loop: one step appends the new token's key and value on the device (quantizing
+        # the key block it completes) and runs the sparse decode with device-side lengths, as a
+        # generation loop replays it.  It runs on the cache copies other than the first (which
+        # it modifies), each sequence starting a few tokens below the capacity so that no
+        # replay reaches it.
+        loop_reps = reps[1:]
+        RL = len(loop_reps)
+        cap = Kd.shape[2]
+        start = max(0, cap - (2 * math.ceil(steps / RL) + 2 * math.ceil(warmup / RL) + 8))
+        lens_l = [torch.full((w.B,), start, dtype=torch.int32, device=dev) for _ in range(RL)]
+        gen = torch.Generator().manual_seed(20261202)
+        k_new = torch.randn((w.B, w.Hkv, w.d), generator=gen).to(dev, Kd.dtype)
+        v_new = torch.randn((w.B, w.Hkv, w.d), generator=gen).to(dev, Kd.dtype)
+
+        def loop_step(r):
+            Kr, Vr, Kqr, scr = loop_reps[r % RL]
+            ln = lens_l[r % RL]
+            ffd.append_token(k_new, v_new, Kr, Vr, ln, w.T, Kqr, scr)
+            ffd.decode_sparse_varlen(qd, Kr, Vr, Kqr, scr, ln, delta, w.T, max_len=w.L,
+                                     out=out_s, lse=lse_s, workspace=ws)
+
+        def varlen_only(r):
+            Kr, Vr, Kqr, scr = loop_reps[r % RL]
+            ffd.decode_sparse_varlen(qd, Kr, Vr, Kqr, scr, lens_l[r % RL], delta, w.T,
+                                     max_len=w.L, out=out_s, lse=lse_s, workspace=ws)
+
+        timed_eager(loop_step, min(warmup, RL))
+        us_loop = timed(loop_step, steps)
+        us_varlen = timed(varlen_only, steps)
+        torch.cuda.synchronize()
+        loop = {"step": "append_token + decode_sparse_varlen", "us_per_token": us_loop,
+                "tokens_per_s": w.B * 1e6 / us_loop, "decode_varlen_us": us_varlen,
+                "append_us": us_loop - us_varlen, "start_len": start,
+                "end_len": int(max(int(x.max()) for x in lens_l)), "cache_copies": RL}
+        del loop_reps, lens_l
+
     res_form = None
     if residual_bits:
         # the residual storage form (thumbnail + 8-bit residual replace the keys of full blocks)
@@ -268,6 +306,7 @@ def run_workload(w, delta: float, steps: int, warmup: int, min_rotation_mib: int
         "lse_err_vs_dense": lse_err,
         "quantize_us": quant_us,
         "residual_form": res_form,
+        "decode_loop": loop,
     }
     if not residual_bits:
         del reps
@@ -327,6 +366,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--residual-bits", type=int, default=2, choices=(0, 2, 4),
                     help="also time the residual storage form on the primary workload (0: no)")
+    ap.add_argument("--no-loop", action="store_true",
+                    help="skip the decode-loop leg (append + decode with device-side lengths)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (no graph capture), e.g. under counter tools")
     ap.add_argument("--rotation-mib", type=int, default=1024,
@@ -353,9 +394,14 @@ def main() -> int:
     delta = args.delta if args.delta is not None else w.deltas[0]
     t_wall = time.time()
     prim, host = run_workload(w, delta, args.steps, args.warmup, args.rotation_mib,
-                              graphs=not args.eager, residual_bits=args.residual_bits)
+                              graphs=not args.eager, residual_bits=args.residual_bits,
+                              decode_loop=not args.no_loop)
     log(f"{w.name}: sparse {prim['sparse_us']:.1f} us, dense {prim['dense_us']:.1f} us, "
         f"{prim['sparse_GBps']:.0f} GB/s, keep {prim['union_keep']:.4f}")
+    if prim["decode_loop"]:
+        lp = prim["decode_loop"]
+        log(f"{w.name} decode loop: {lp['us_per_token']:.1f} us/token "
+            f"(append {lp['append_us']:.1f} us + varlen decode {lp['decode_varlen_us']:.1f} us)")
     if prim["residual_form"]:
         rf = prim["residual_form"]
         log(f"{w.name} residual form: sparse {rf['sparse_us']:.1f} us, {rf['GBps']:.0f} GB/s, "

@@ -158,6 +158,44 @@ ffd_status ffd_decode_sparse_residual(const ffd_dims* dims, const void* q, const
                                       uint8_t* keep_mask, void* workspace, size_t workspace_bytes,
                                       hipStream_t stream);
 
+/*
+ * Decode loop (Sec. 3.3: the fused step runs once per generated token; Fig. 2: the low-bit key
+ * copy is maintained as blocks complete; App. G / Table 9: the step is replayed as a graph).
+ * Everything a step needs lives in device memory, so one captured step (append + decode) can be
+ * replayed for every token, across block boundaries, with no re-capture.
+ *
+ * ffd_append_token: for every sequence b (and every kv head), writes the new token's key and value
+ * rows k_new[b, g, :] and v_new[b, g, :] at position seq_lens[b] of K and V; if that token
+ * completes key block j = seq_lens[b] / block, quantizes block j into Kq/scales exactly as
+ * ffd_quantize_k_append does; then increments seq_lens[b].
+ *   k_new, v_new  [B, Hkv, d] in dims->dtype
+ *   K, V, Kq, scales  the caches (layouts of ffd_decode_sparse), updated in place
+ *   seq_lens   device int32 [B], the current lengths; a sequence already at dims->seq_cap (or
+ *              with a negative length) is left unchanged and nothing of it is written
+ * dims->seq_len is not used (it must still be valid). Two kernel launches, no host synchronisation.
+ */
+ffd_status ffd_append_token(const ffd_dims* dims, const void* k_new, const void* v_new, void* K,
+                            void* V, int32_t* seq_lens, int32_t block, uint8_t* Kq,
+                            float* scales, hipStream_t stream);
+
+/*
+ * Sparse (and dense) decode step with per-sequence lengths read from device memory: sequence b
+ * attends over its first seq_lens[b] tokens, clamped to [0, dims->seq_len]; dims->seq_len is the
+ * bound the splits cover (normally dims->seq_cap) and sizes the workspace.  Everything else is as
+ * in ffd_decode_sparse / ffd_decode_dense; keep_mask rows are ceil(dims->seq_len / block) long,
+ * and entries past a sequence's own blocks are not written.  A sequence of length 0 gets out = 0
+ * and lse = -inf.
+ */
+ffd_status ffd_decode_sparse_varlen(const ffd_dims* dims, const void* q, const void* K,
+                                    const void* V, const uint8_t* Kq, const float* scales,
+                                    const int32_t* seq_lens, float delta, int32_t block,
+                                    float* out, float* lse, uint8_t* keep_mask, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+ffd_status ffd_decode_dense_varlen(const ffd_dims* dims, const void* q, const void* K,
+                                   const void* V, const int32_t* seq_lens, int32_t block,
+                                   float* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes needed by ffd_decode_sparse / ffd_decode_dense for these dims and block
  * (the maximum of the two); 0 for invalid dims.  The size depends on the split count, which the
  * environment variable FFD_NUM_SPLITS (a positive integer) overrides. */

@@ -87,7 +87,7 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
                          float* out, float* lse, uint8_t* keep_mask, void* workspace,
                          size_t workspace_bytes, hipStream_t stream, bool sparse,
                          const int8_t* Kr = nullptr, const float* res_scales = nullptr,
-                         int bits = 0)
+                         int bits = 0, const int32_t* seq_lens = nullptr)
 {
     const bool res = bits != 0;
     ffd_status st = check_dims(dims, block);
@@ -97,6 +97,7 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
     // the residual form reads 16-bit keys only for a partial tail block
     const bool need_K = !res || dims->seq_len % block != 0;
     if (!q || (need_K && !K) || !V || !out) return FFD_ERR_INVALID_ARG;
+    if (seq_lens && (reinterpret_cast<uintptr_t>(seq_lens) & 3u)) return FFD_ERR_INVALID_ARG;
     if (!aligned16(q) || (K && !aligned16(K)) || !aligned16(V) || !aligned16(out) ||
         (lse && !aligned16(lse)) || (keep_mask && !aligned16(keep_mask)))
         return FFD_ERR_INVALID_ARG;
@@ -137,6 +138,8 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
     p.n_blocks = (dims->seq_len + block - 1) / block;
     p.S = S;
     p.R = (p.n_blocks + S - 1) / S;
+    p.seq_lens = seq_lens;
+    p.mask_stride = p.n_blocks;
     p.delta = delta;
     p.kappa = (float)(0.5 / (127.0 * sqrt((double)kHeadDim)));
     p.c_log2 = (float)(1.4426950408889634 / sqrt((double)kHeadDim));
@@ -283,6 +286,54 @@ ffd_status ffd_decode_dense(const ffd_dims* dims, const void* q, const void* K, 
 {
     return decode_common(dims, q, K, V, nullptr, nullptr, 0.0f, block, out, lse, nullptr,
                          workspace, workspace_bytes, stream, false);
+}
+
+ffd_status ffd_decode_sparse_varlen(const ffd_dims* dims, const void* q, const void* K,
+                                    const void* V, const uint8_t* Kq, const float* scales,
+                                    const int32_t* seq_lens, float delta, int32_t block,
+                                    float* out, float* lse, uint8_t* keep_mask, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream)
+{
+    if (!seq_lens) return FFD_ERR_INVALID_ARG;
+    return decode_common(dims, q, K, V, Kq, scales, delta, block, out, lse, keep_mask, workspace,
+                         workspace_bytes, stream, true, nullptr, nullptr, 0, seq_lens);
+}
+
+ffd_status ffd_decode_dense_varlen(const ffd_dims* dims, const void* q, const void* K,
+                                   const void* V, const int32_t* seq_lens, int32_t block,
+                                   float* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream)
+{
+    if (!seq_lens) return FFD_ERR_INVALID_ARG;
+    return decode_common(dims, q, K, V, nullptr, nullptr, 0.0f, block, out, lse, nullptr,
+                         workspace, workspace_bytes, stream, false, nullptr, nullptr, 0,
+                         seq_lens);
+}
+
+ffd_status ffd_append_token(const ffd_dims* dims, const void* k_new, const void* v_new, void* K,
+                            void* V, int32_t* seq_lens, int32_t block, uint8_t* Kq,
+                            float* scales, hipStream_t stream)
+{
+    ffd_status st = check_dims(dims, block);
+    if (st != FFD_OK) return st;
+    if (dims->batch == 0) return FFD_OK;
+    if (!k_new || !v_new || !K || !V || !seq_lens || !Kq || !scales) return FFD_ERR_INVALID_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(K) || !aligned16(V) ||
+        !aligned16(Kq) || !aligned16(scales) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+        return FFD_ERR_INVALID_ARG;
+    ffd::AppendParams a{};
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.K = K;
+    a.V = V;
+    a.seq_lens = seq_lens;
+    a.Kq = Kq;
+    a.scales = scales;
+    a.B = dims->batch;
+    a.Hkv = dims->n_kv_heads;
+    a.cap = dims->seq_cap;
+    a.T = block;
+    return finish(ffd::launch_append(a, dims->dtype == FFD_BF16, stream));
 }
 
 }  // extern "C"

@@ -37,6 +37,10 @@ struct DecodeParams {
     float delta;    // top-delta threshold (logit units)
     float kappa;    // (float)(0.5 / (127 sqrt(d)))
     float c_log2;   // (float)(log2(e) / sqrt(d))
+    const int32_t* seq_lens;  // optional [B] per-sequence lengths in device memory, each clamped
+                              // to [0, L]; L, n_full and n_blocks are then the bounds the splits
+                              // cover and each work-group derives its sequence's own
+    int mask_stride;          // keep_mask row length in blocks
 };
 
 struct QuantParams {
@@ -49,7 +53,21 @@ struct QuantParams {
     int j_first, n_blocks;  // blocks j_first .. j_first + n_blocks - 1
 };
 
+// One decode-loop step of the cache: the new token's key and value rows go to position
+// seq_lens[b] of every (b, kv head), and the key block they complete (if any) is quantized.
+struct AppendParams {
+    const void* k_new;  // [B][Hkv][d]
+    const void* v_new;  // [B][Hkv][d]
+    void* K;            // [B][Hkv][cap][d]
+    void* V;
+    int32_t* seq_lens;  // [B], device
+    uint8_t* Kq;
+    float* scales;
+    int B, Hkv, cap, T;
+};
+
 // Launchers (ffd_kernels.hip).  Return the hipError_t of the launch.
+hipError_t launch_append(const AppendParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, bool bf16, bool sparse, hipStream_t stream);
 hipError_t launch_quantize(const QuantParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_decode_res(const DecodeParams& p, int bits, hipStream_t stream);

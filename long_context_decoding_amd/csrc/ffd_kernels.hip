@@ -687,8 +687,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
     int split = rank;
     if (SPARSE && p.S > 1) split = rank == 0 ? 0 : (rank == 1 ? p.S - 1 : rank - 1);
     const int b = bg / p.Hkv, g = bg % p.Hkv;
+    // this sequence's length: the common one, or (decode loops) its own from device memory
+    int L_b = p.L;
+    if (p.seq_lens) L_b = min(max(p.seq_lens[b], 0), p.L);
+    const int nf_b = L_b / T;            // full blocks
+    const int nb_b = (L_b + T - 1) / T;  // blocks, the last one possibly partial
     const int jb = split * p.R;
-    const int je = min(p.n_blocks, jb + p.R);
+    const int je = min(nb_b, jb + p.R);
 
     const size_t esz = BF16 ? 2 : 4;
     const size_t kv_off = (size_t)bg * p.cap * D;
@@ -736,7 +741,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
 
         const uint8_t* kq_bg = p.Kq + (size_t)bg * p.cap * (D * BITS / 8);
         const float* sc_bg = p.scales + (size_t)bg * (p.cap / T) * D;
-        const int nf = p.n_full;
+        const int nf = nf_b;
         const u32 all_heads = (1u << G) - 1u;
         // Forced blocks of the split (sink 0, the local block nf-1 and a partial tail) are kept
         // for every head; every other block of the split is a scan item of exactly one wave.
@@ -747,7 +752,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
                     sh.kbits[t] = (uint8_t)all_heads;
                     if (p.keep_mask)
 #pragma unroll
-                        for (int h = 0; h < G; ++h) p.keep_mask[(size_t)(h0 + h) * p.n_blocks + j] = 1;
+                        for (int h = 0; h < G; ++h) p.keep_mask[(size_t)(h0 + h) * p.mask_stride + j] = 1;
                 }
             }
         }
@@ -783,7 +788,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
                     const u32 bits = (u32)__ballot(keep) & all_heads;
                     if (lane == 0) sh.kbits[j - jb] = (uint8_t)bits;
                     if (p.keep_mask && lane < G)
-                        p.keep_mask[(size_t)(h0 + lane) * p.n_blocks + j] = keep ? 1 : 0;
+                        p.keep_mask[(size_t)(h0 + lane) * p.mask_stride + j] = keep ? 1 : 0;
                 }
             };
             // Two items in flight: item k + 1 is loaded while item k is computed.  The steady
@@ -877,7 +882,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
             typedef typename pick<RES, TileRes, TileRegs<BF16>>::type TR;
             // residual form: tiles of full blocks are rebuilt from thumbnail + residual, the tiles
             // of a partial tail block (no low-bit copy) read the 16-bit keys
-            const int full_end = p.n_full * T;
+            const int full_end = nf_b * T;
             auto load_tile = [&](TR& r, int t0) {
                 if constexpr (RES)
                     tile_load_res<BITS>(
@@ -891,10 +896,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
             };
             auto compute_tile = [&](const TR& r, int t0, u32 kb) {
                 if constexpr (RES)
-                    tile_compute_res<G, BITS>(r, qv, st, ws, t0, p.L, kb, p.c_log2,
+                    tile_compute_res<G, BITS>(r, qv, st, ws, t0, L_b, kb, p.c_log2,
                                               t0 >= full_end, lane);
                 else
-                    tile_compute<G, BF16>(r, qrow, qv, st, t0, p.L, kb, p.c_log2, lane);
+                    tile_compute<G, BF16>(r, qrow, qv, st, t0, L_b, kb, p.c_log2, lane);
             };
             TR ta, tb;
             int t0a, t0b;
@@ -1064,9 +1069,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
             const int e = (int)threadIdx.x + i * kWaves * 64;
             if (e < G * D) {
                 const int h = e / D, c = e % D;
-                p.out[(size_t)(h0 + h) * D + c] = acc[i] / L[i];
+                // an empty sequence (length 0) has no softmax: out = 0, lse = -inf
+                p.out[(size_t)(h0 + h) * D + c] = L[i] > 0.0f ? acc[i] / L[i] : 0.0f;
                 if (p.lse && c == 0)
-                    p.lse[h0 + h] = (M[i] + __log2f(L[i])) * 0.69314718055994530942f;
+                    p.lse[h0 + h] =
+                        L[i] > 0.0f ? (M[i] + __log2f(L[i])) * 0.69314718055994530942f : kNegInf;
             }
         }
         return;
@@ -1123,9 +1130,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
                 if (k0 + u < n) acc = fmaf(sh.u.fin.wgt[h][k0 + u], v[u], acc);
         }
         const float L = sh.u.fin.Lsum[h];
-        p.out[(size_t)(h0 + h) * D + c] = acc / L;
+        p.out[(size_t)(h0 + h) * D + c] = L > 0.0f ? acc / L : 0.0f;
         if (p.lse && c == 0)
-            p.lse[h0 + h] = (sh.u.fin.M[h] + __log2f(L)) * 0.69314718055994530942f;
+            p.lse[h0 + h] =
+                L > 0.0f ? (sh.u.fin.M[h] + __log2f(L)) * 0.69314718055994530942f : kNegInf;
     }
 }
 
@@ -1136,14 +1144,12 @@ __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ p,
 }
 
 // ------------------------------------------------------------------------------------------
-// App. A quantizer, 16 levels: one work-group of 128 threads (one per channel) per block.
+// App. A quantizer, 16 levels, of key block j of slice bg: one thread per channel c (a
+// work-group of 128 threads; neighbouring channels share a byte).
 // ------------------------------------------------------------------------------------------
 template <int T, bool BF16>
-__global__ __launch_bounds__(128) void quantize_kernel(QuantParams p)
+__device__ __forceinline__ void quantize_block(QuantParams p, int bg, int j, int c)
 {
-    const int j = p.j_first + blockIdx.x;
-    const int bg = blockIdx.y;
-    const int c = threadIdx.x;
     const size_t row0 = (size_t)bg * p.cap + (size_t)j * T;
     float x[T];
     float amax = 0.0f;
@@ -1173,6 +1179,58 @@ __global__ __launch_bounds__(128) void quantize_kernel(QuantParams p)
         }
         const int partner = __shfl_xor(u, 1);
         if ((c & 1) == 0) p.Kq[(row0 + t) * (D / 2) + c / 2] = (uint8_t)(u | (partner << 4));
+    }
+}
+
+template <int T, bool BF16>
+__global__ __launch_bounds__(128) void quantize_kernel(QuantParams p)
+{
+    quantize_block<T, BF16>(p, blockIdx.y, p.j_first + blockIdx.x, threadIdx.x);
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode-loop cache update, one work-group of 128 threads (one per channel) per (b, kv head):
+// the new token's key and value go to position seq_lens[b]; when that token completes a key
+// block, the block is quantized right away (the key copy is maintained at block boundaries,
+// Fig. 2).  A sequence already at the capacity is left as it is.  The lengths advance in a
+// separate launch, after every (b, kv head) of the step has read them.
+// ------------------------------------------------------------------------------------------
+template <int T, bool BF16>
+__global__ __launch_bounds__(128) void append_kernel(AppendParams a)
+{
+    const int bg = blockIdx.x;
+    const int b = bg / a.Hkv;
+    const int c = threadIdx.x;
+    const int pos = a.seq_lens[b];
+    if (pos < 0 || pos >= a.cap) return;  // uniform over the work-group
+    const size_t src = (size_t)bg * D + c;
+    const size_t dst = ((size_t)bg * a.cap + pos) * D + c;
+    if constexpr (BF16) {
+        static_cast<unsigned short*>(a.K)[dst] = static_cast<const unsigned short*>(a.k_new)[src];
+        static_cast<unsigned short*>(a.V)[dst] = static_cast<const unsigned short*>(a.v_new)[src];
+    } else {
+        static_cast<float*>(a.K)[dst] = static_cast<const float*>(a.k_new)[src];
+        static_cast<float*>(a.V)[dst] = static_cast<const float*>(a.v_new)[src];
+    }
+    if ((pos + 1) % T == 0) {
+        // this thread wrote the block's last key of its channel; the other rows are older
+        QuantParams q{};
+        q.K = a.K;
+        q.Kq = a.Kq;
+        q.scales = a.scales;
+        q.cap = a.cap;
+        q.T = T;
+        quantize_block<T, BF16>(q, bg, pos / T, c);
+    }
+}
+
+__global__ __launch_bounds__(256) void advance_kernel(int32_t* __restrict__ seq_lens, int B,
+                                                      int cap)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B) {
+        const int L = seq_lens[b];
+        if (L >= 0 && L < cap) seq_lens[b] = L + 1;
     }
 }
 
@@ -1315,6 +1373,26 @@ hipError_t launch_zero_counters(uint32_t* counters, int n, hipStream_t stream)
 {
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(zero_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, counters, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendParams& p, bool bf16, hipStream_t stream)
+{
+    if (p.B <= 0) return hipSuccess;
+    const dim3 grid(p.B * p.Hkv), block(D);
+    if (p.T == 64) {
+        if (bf16) hipLaunchKernelGGL((append_kernel<64, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((append_kernel<64, false>), grid, block, 0, stream, p);
+    } else if (p.T == 128) {
+        if (bf16) hipLaunchKernelGGL((append_kernel<128, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((append_kernel<128, false>), grid, block, 0, stream, p);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(advance_kernel, dim3((p.B + 255) / 256), dim3(256), 0, stream, p.seq_lens,
+                       p.B, p.cap);
     return hipGetLastError();
 }
 

@@ -6,8 +6,9 @@ through ctypes, and raises on a non-OK status.  There is no fallback: if the lib
 or cannot be loaded, every call raises.
 
 Names follow the C ABI: ``quantize_k_append``, ``decode_sparse``, ``decode_dense``,
-``quantize_k_residual_append``, ``decode_sparse_residual``, ``workspace_bytes``,
-``workspace_init``, ``num_splits``.
+``quantize_k_residual_append``, ``decode_sparse_residual``, ``append_token``,
+``decode_sparse_varlen``, ``decode_dense_varlen``, ``workspace_bytes``, ``workspace_init``,
+``num_splits``.
 """
 from __future__ import annotations
 
@@ -68,6 +69,12 @@ def lib():
         L.ffd_decode_sparse_residual.argtypes = [D, P, P, P, P, P, P, P, i32, f32, i32, P, P, P, P,
                                                  sz, P]
         L.ffd_decode_sparse_residual.restype = i32
+        L.ffd_append_token.argtypes = [D, P, P, P, P, P, i32, P, P, P]
+        L.ffd_append_token.restype = i32
+        L.ffd_decode_sparse_varlen.argtypes = [D, P, P, P, P, P, P, f32, i32, P, P, P, P, sz, P]
+        L.ffd_decode_sparse_varlen.restype = i32
+        L.ffd_decode_dense_varlen.argtypes = [D, P, P, P, P, i32, P, P, P, sz, P]
+        L.ffd_decode_dense_varlen.restype = i32
         _lib = L
     return _lib
 
@@ -298,4 +305,73 @@ def decode_sparse_residual(q: torch.Tensor, K_tail: torch.Tensor | None, V: torc
                                             float(delta), block, _ptr(out), _ptr(lse),
                                             _ptr(keep_mask), _ptr(workspace), workspace.numel(),
                                             _stream(stream)))
+    return out, lse
+
+
+def append_token(k_new: torch.Tensor, v_new: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                 seq_lens: torch.Tensor, block: int, Kq: torch.Tensor, scales: torch.Tensor,
+                 stream=None) -> None:
+    """Decode-loop cache update on the device: the new token's rows go to position seq_lens[b],
+    a key block it completes is quantized, and seq_lens advances by one (capped at capacity)."""
+    B, Hkv, cap, d = K.shape
+    _need(k_new, "k_new", K.dtype, (B, Hkv, d), K.device)
+    _need(v_new, "v_new", K.dtype, (B, Hkv, d), K.device)
+    _need(V, "V", K.dtype, K.shape, K.device)
+    _need(seq_lens, "seq_lens", torch.int32, (B,), K.device)
+    _need(Kq, "Kq", torch.uint8, (B, Hkv, cap, d // 2), K.device)
+    _need(scales, "scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d), K.device)
+    dims = make_dims(B, Hkv, Hkv, cap, cap, _dtype_code(K), d)
+    _check(lib().ffd_append_token(ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _ptr(K), _ptr(V),
+                                  _ptr(seq_lens), block, _ptr(Kq), _ptr(scales), _stream(stream)))
+
+
+def decode_sparse_varlen(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, Kq: torch.Tensor,
+                         scales: torch.Tensor, seq_lens: torch.Tensor, delta: float, block: int,
+                         max_len: int | None = None, out: torch.Tensor | None = None,
+                         lse: torch.Tensor | None = None, keep_mask: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None, want_lse: bool = True,
+                         stream=None):
+    """Sparse decode step with per-sequence lengths in device memory (seq_lens int32 [B]);
+    max_len (default: the cache capacity) bounds them and sets the split coverage."""
+    B, Hkv, cap, d = K.shape
+    max_len = cap if max_len is None else max_len
+    dims = dims_of(q, K, max_len)
+    _need(V, "V", K.dtype, K.shape, K.device)
+    _need(q, "q", K.dtype, None, K.device)
+    _need(Kq, "Kq", torch.uint8, (B, Hkv, cap, d // 2), K.device)
+    _need(scales, "scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d),
+          K.device)
+    _need(seq_lens, "seq_lens", torch.int32, (B,), K.device)
+    out, lse = _decode_outputs(q, out, lse, want_lse)
+    if keep_mask is not None:
+        _need(keep_mask, "keep_mask", torch.uint8,
+              (q.shape[0], q.shape[1], math.ceil(max_len / block)), q.device)
+    if workspace is None:
+        workspace = alloc_workspace(dims, block, q.device)
+    _need(workspace, "workspace", torch.uint8, None, q.device)
+    _check(lib().ffd_decode_sparse_varlen(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V), _ptr(Kq),
+                                          _ptr(scales), _ptr(seq_lens), float(delta), block,
+                                          _ptr(out), _ptr(lse), _ptr(keep_mask), _ptr(workspace),
+                                          workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def decode_dense_varlen(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_lens: torch.Tensor,
+                        block: int, max_len: int | None = None, out: torch.Tensor | None = None,
+                        lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                        want_lse: bool = True, stream=None):
+    """Dense decode step with per-sequence lengths in device memory."""
+    B, Hkv, cap, d = K.shape
+    max_len = cap if max_len is None else max_len
+    dims = dims_of(q, K, max_len)
+    _need(V, "V", K.dtype, K.shape, K.device)
+    _need(q, "q", K.dtype, None, K.device)
+    _need(seq_lens, "seq_lens", torch.int32, (B,), K.device)
+    out, lse = _decode_outputs(q, out, lse, want_lse)
+    if workspace is None:
+        workspace = alloc_workspace(dims, block, q.device)
+    _need(workspace, "workspace", torch.uint8, None, q.device)
+    _check(lib().ffd_decode_dense_varlen(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V),
+                                         _ptr(seq_lens), block, _ptr(out), _ptr(lse),
+                                         _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse

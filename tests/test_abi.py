@@ -173,3 +173,33 @@ def test_residual_validation(L):
         ffd.FFD_ERR_UNSUPPORTED
     assert qa(ctypes.byref(d), A, 0, 64, 64, 2, A, A, None, A, None) == ffd.FFD_ERR_INVALID_ARG
     assert qa(ctypes.byref(d), A, 0, 63, 64, 2, A, A, A, A, None) == ffd.FFD_OK  # no block
+
+
+def test_decode_loop_validation(L):
+    """ffd_append_token and the per-sequence-length decode calls reject bad arguments before any
+    launch (so the fake pointers are never dereferenced)."""
+    d = dims()
+    lens = ctypes.c_void_p(0x20000)
+    lens_odd = ctypes.c_void_p(0x20002)
+    app = L.ffd_append_token
+    assert app(ctypes.byref(d), None, A, A, A, lens, 64, A, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert app(ctypes.byref(d), A, A, A, A, None, 64, A, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert app(ctypes.byref(d), A, A, A, A, lens_odd, 64, A, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert app(ctypes.byref(d), A, MISALIGNED, A, A, lens, 64, A, A, None) == \
+        ffd.FFD_ERR_INVALID_ARG
+    assert app(ctypes.byref(d), A, A, A, A, lens, 96, A, A, None) == ffd.FFD_ERR_UNSUPPORTED
+    assert app(ctypes.byref(dims(B=0)), A, A, A, A, lens, 64, A, A, None) == ffd.FFD_OK
+
+    sv = L.ffd_decode_sparse_varlen
+    assert sv(ctypes.byref(d), A, A, A, A, A, None, 5.0, 64, A, A, None, A, 1 << 30,
+              None) == ffd.FFD_ERR_INVALID_ARG
+    assert sv(ctypes.byref(d), A, A, A, A, A, lens_odd, 5.0, 64, A, A, None, A, 1 << 30,
+              None) == ffd.FFD_ERR_INVALID_ARG
+    assert sv(ctypes.byref(d), A, A, A, A, A, lens, float("nan"), 64, A, A, None, A, 1 << 30,
+              None) == ffd.FFD_ERR_INVALID_ARG
+    assert sv(ctypes.byref(d), A, A, A, A, A, lens, 5.0, 64, A, A, None, A, 16,
+              None) == ffd.FFD_ERR_WORKSPACE
+    dv = L.ffd_decode_dense_varlen
+    assert dv(ctypes.byref(d), A, A, A, None, 64, A, A, A, 1 << 30, None) == \
+        ffd.FFD_ERR_INVALID_ARG
+    assert dv(ctypes.byref(d), A, A, A, lens, 64, A, A, A, 16, None) == ffd.FFD_ERR_WORKSPACE
