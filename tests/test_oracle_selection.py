@@ -1,0 +1,145 @@
+"""Pins of the selection-comparator oracle (oracle/selection.py): each check uses something other
+than the function itself -- brute force over all subsets, closed forms, hand-worked examples and
+invariants ("Faster Than Flash" Sec. 3.2 Eqs. 1 and 3, Sec. 4.5 Table 3, Sec. 5.1-5.2)."""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+from long_context_decoding_amd import workloads as W
+from oracle import selection as S
+
+
+def rnd_keys(rng, n, d=128):
+    return W.f32_to_bf16_bits(rng.standard_normal((n, d)).astype(np.float32))
+
+
+def test_forced_blocks():
+    assert S.forced_mask(4, 5).tolist() == [1, 0, 0, 1, 1]
+    assert S.forced_mask(4, 4).tolist() == [1, 0, 0, 1]
+    assert S.forced_mask(1, 2).tolist() == [1, 1]
+    assert S.forced_mask(0, 1).tolist() == [1]
+
+
+def test_top_delta_hand_example():
+    # scores 5, 1, 3, 4, 2; pseudo-max max(s0, s4) = 5; delta 1.5 -> theta 3.5:
+    # block 3 (4 >= 3.5) joins the forced blocks 0 and 4
+    keep, mt, th = S.select_top_delta(np.array([5, 1, 3, 4, 2], np.float32), 5, 5, 1.5)
+    assert keep.tolist() == [1, 0, 0, 1, 1] and mt == 5.0 and th == 3.5
+    # an exact-score pseudo-max of 3.0 (Eq. 3) lowers theta to 1.5: blocks 2 and 3 and 4 (2 >= 1.5)
+    keep, _, th = S.select_top_delta(np.array([5, 1, 3, 4, 2], np.float32), 5, 5, 1.5, 3.0)
+    assert keep.tolist() == [1, 0, 1, 1, 1] and th == 1.5
+    keep, _, _ = S.select_top_delta(np.array([5, 1, 3, 4, 2], np.float32), 5, 6, math.inf)
+    assert keep.tolist() == [1] * 6
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_top_k_is_the_best_subset(seed):
+    rng = np.random.default_rng(seed)
+    n = 7
+    s = rng.integers(-3, 4, size=n).astype(np.float64)  # many ties
+    for k in range(n + 1):
+        keep = S.select_top_k(s, n, n, k)
+        forced = set(np.nonzero(S.forced_mask(n, n))[0])
+        chosen = set(np.nonzero(keep)[0])
+        # brute force: among all k-subsets, the largest score sum, ties broken towards the
+        # lexicographically smallest sorted index list
+        best = max(itertools.combinations(range(n), k),
+                   key=lambda c: (sum(s[list(c)]), [-j for j in sorted(c)]))
+        assert chosen == set(best) | forced, (k, s, chosen, best)
+
+
+def test_top_k_extremes():
+    s = np.array([0.5, 2.0, 2.0, -1.0, 0.0], np.float64)
+    assert S.select_top_k(s, 5, 6, 0).tolist() == [1, 0, 0, 0, 1, 1]
+    assert S.select_top_k(s, 5, 6, 1).tolist() == [1, 1, 0, 0, 1, 1]   # tie -> lower index
+    assert S.select_top_k(s, 5, 6, 99).tolist() == [1] * 6
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_top_p_is_the_shortest_prefix_reaching_p(seed):
+    rng = np.random.default_rng(seed)
+    n = 40
+    s = rng.standard_normal(n) * 2
+    probs = np.exp(s - s.max())
+    probs /= probs.sum()
+    prev = 0
+    for p in (1e-9, 0.1, 0.5, 0.8, 0.95, 0.999):
+        keep = S.select_top_p(s, n, n, p)
+        forced = S.forced_mask(n, n).astype(bool)
+        sel = np.zeros(n, bool)
+        n_sel, order, _ = S.top_p_prefix(s, p)
+        sel[order[:n_sel]] = True
+        assert (keep.astype(bool) == (sel | forced)).all()
+        # brute force on the definition: the n highest blocks reach p, the n-1 highest do not
+        desc = np.sort(probs)[::-1]
+        assert desc[:n_sel].sum() >= p - 1e-12
+        assert n_sel == 1 or desc[: n_sel - 1].sum() < p + 1e-12
+        assert n_sel >= prev  # monotone in p
+        prev = n_sel
+    assert S.top_p_prefix(s, 1e-12)[0] == 1            # the top block alone
+    assert S.top_p_prefix(s, 1.0)[0] == n              # everything
+
+
+def test_bounds_are_upper_bounds_and_tight_cases():
+    rng = np.random.default_rng(1)
+    T, nf, d = 64, 6, 128
+    K = rnd_keys(rng, nf * T, d)
+    for _ in range(5):
+        q = W.f32_to_bf16_bits(rng.standard_normal(d).astype(np.float32))
+        mn, mx = S.block_bounds(K, T, nf)
+        ub = S.bound_scores(q, mn, mx)
+        ex = S.exact_block_max(q, K, T, nf)
+        assert (ub >= ex - 1e-12).all()
+    # one-hot query: the bound of channel c is the exact maximum of a * k_tc
+    c, a = 17, 3.0
+    qo = np.zeros(d, np.float32)
+    qo[c] = a
+    mn, mx = S.block_bounds(K, T, nf)
+    kf = W.bf16_bits_to_f32(K).astype(np.float64)
+    for j in range(nf):
+        want = (a * kf[j * T:(j + 1) * T, c]).max() / math.sqrt(d)
+        assert S.bound_scores(qo, mn, mx)[j] == pytest.approx(want, abs=1e-12)
+        assert S.exact_block_max(qo, K, T, nf)[j] == pytest.approx(want, abs=1e-12)
+    # a block of one repeated token: min = max, the bound is exact
+    Kr = np.repeat(K[:1], T, axis=0)
+    q = W.f32_to_bf16_bits(rng.standard_normal(d).astype(np.float32))
+    mn, mx = S.block_bounds(Kr, T, 1)
+    assert S.bound_scores(q, mn, mx)[0] == pytest.approx(S.exact_block_max(q, Kr, T, 1)[0],
+                                                         abs=1e-9)
+
+
+def test_exact_block_max_planted_token():
+    rng = np.random.default_rng(2)
+    T, nf, d = 64, 4, 128
+    Kf = rng.standard_normal((nf * T, d)).astype(np.float32) * 0.1
+    qf = rng.standard_normal(d).astype(np.float32)
+    q = W.f32_to_bf16_bits(qf)
+    qv = W.bf16_bits_to_f32(q).astype(np.float64)
+    Kf[2 * T + 5] = 0.0
+    Kf[2 * T + 5, 7] = 4.0  # one token whose score is 4 q_7 / sqrt(d) by hand
+    K = W.f32_to_bf16_bits(Kf)
+    got = S.exact_block_max(q, K, T, nf)
+    kv = W.bf16_bits_to_f32(K).astype(np.float64)
+    hand = max(4.0 * qv[7] / math.sqrt(d),
+               max(float(kv[t] @ qv) for t in range(2 * T, 3 * T) if t != 2 * T + 5) / math.sqrt(d))
+    assert got[2] == pytest.approx(hand, rel=1e-12)
+
+
+def test_eq3_pseudo_max_never_exceeds_the_true_max():
+    # Eq. 3: mtilde over the sink and local blocks' exact scores is at most the global max (the
+    # fail-safe direction of Sec. 5.2), with equality when the argmax token is in the sink block
+    rng = np.random.default_rng(4)
+    T, nf, d = 64, 10, 128
+    for trial in range(8):
+        Kf = rng.standard_normal((nf * T, d)).astype(np.float32)
+        qf = rng.standard_normal(d).astype(np.float32)
+        if trial % 2:
+            Kf[3] = qf / np.linalg.norm(qf) * 12.0  # planted in the sink block
+        K, q = W.f32_to_bf16_bits(Kf), W.f32_to_bf16_bits(qf)
+        e = S.exact_block_max(q, K, T, nf)
+        mtilde = max(e[0], e[nf - 1])
+        assert mtilde <= e.max()
+        if trial % 2:
+            assert mtilde == e.max()
