@@ -196,6 +196,60 @@ ffd_status ffd_decode_dense_varlen(const ffd_dims* dims, const void* q, const vo
                                    float* out, float* lse, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Selection comparators and fidelity diagnostics (Sec. 4.5 Table 3: top-delta against top-k and
+ * top-p at a matched keep ratio; Sec. 5.1 Fig. 6: a Quest-style min/max scan as the comparator;
+ * Sec. 3.2 Eq. 3 and Sec. 5.2 Fig. 5: the pseudo-max from exact scores and its gap to the true
+ * maximum).  Unlike ffd_decode_sparse, which decides each block as it scans it, these run as
+ * separate steps: per-block scores, then a rule over every block of a (sequence, query head),
+ * then exact attention over the chosen blocks.
+ */
+typedef enum {
+    FFD_SCORE_SCAN = 0,    /* the scan estimate of the block's largest score (Alg. 1), from Kq/scales */
+    FFD_SCORE_BOUNDS = 1,  /* sum_c max(q_c kmin_c, q_c kmax_c) / sqrt(d): an upper bound from the
+                              block's per-channel min/max (Quest-style page metadata) */
+    FFD_SCORE_EXACT = 2    /* the block's exact largest score max_t q.k_t / sqrt(d), from K */
+} ffd_score_kind;
+
+typedef enum {
+    FFD_SELECT_TOP_DELTA = 0,  /* Eq. 1: keep s_j >= RN(mtilde - param); mtilde = pseudo_max[row]
+                                  if given, else max(s_0, s_{nf-1}) (Alg. 1) */
+    FFD_SELECT_TOP_K = 1,      /* the floor(param) highest-scoring full blocks */
+    FFD_SELECT_TOP_P = 2       /* the fewest highest-scoring full blocks whose share
+                                  exp(s_j - max s) / sum_i exp(s_i - max s) reaches param */
+} ffd_select_rule;
+
+/* Per-channel min and max over every key block completed by tokens [tok_begin, tok_end) (the
+ * blocks of ffd_quantize_k_append): kmin, kmax [B, Hkv, seq_cap/block, d] in dims->dtype. */
+ffd_status ffd_block_bounds(const ffd_dims* dims, const void* K, int32_t tok_begin,
+                            int32_t tok_end, int32_t block, void* kmin, void* kmax,
+                            hipStream_t stream);
+
+/* Scores of every full block (nf = dims->seq_len / block of them) for every query head:
+ * scores [B, Hq, nf] fp32.  FFD_SCORE_SCAN needs Kq and scales (bit-identical to the decode
+ * kernel's estimates), FFD_SCORE_BOUNDS kmin and kmax, FFD_SCORE_EXACT K; the other inputs may
+ * be NULL.  q is [B, Hq, d] in dims->dtype. */
+ffd_status ffd_block_scores(const ffd_dims* dims, int32_t kind, const void* q, const void* K,
+                            const uint8_t* Kq, const float* scales, const void* kmin,
+                            const void* kmax, int32_t block, float* scores, hipStream_t stream);
+
+/* One selection rule over every row of scores [B, Hq, nf] -> keep_mask [B, Hq, ceil(seq_len /
+ * block)] (0/1).  Every rule also keeps block 0, the last full block and a partial tail.  Full
+ * blocks are ranked by score, ties going to the lower index.  param: delta (>= 0 or +inf) for
+ * top-delta, k (>= 0) for top-k, p in (0, 1] for top-p; pseudo_max [B, Hq] (optional, top-delta
+ * only) replaces Alg. 1's max(s_0, s_{nf-1}), e.g. by the exact-score maximum of Eq. 3.  Top-k and
+ * top-p sort each row in LDS: nf <= 16384 (else FFD_ERR_UNSUPPORTED).  Top-p sums in fp32. */
+ffd_status ffd_select_blocks(const ffd_dims* dims, int32_t rule, const float* scores,
+                             const float* pseudo_max, float param, int32_t block,
+                             uint8_t* keep_mask, hipStream_t stream);
+
+/* Exact attention and split combine over the blocks a caller-made keep_mask [B, Hq,
+ * ceil(seq_len / block)] marks (per query head), e.g. from ffd_select_blocks; otherwise as
+ * ffd_decode_sparse (same workspace).  A head with no kept block gets out = 0, lse = -inf. */
+ffd_status ffd_decode_masked(const ffd_dims* dims, const void* q, const void* K, const void* V,
+                             const uint8_t* keep_mask, int32_t block, float* out, float* lse,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes needed by ffd_decode_sparse / ffd_decode_dense for these dims and block
  * (the maximum of the two); 0 for invalid dims.  The size depends on the split count, which the
  * environment variable FFD_NUM_SPLITS (a positive integer) overrides. */

@@ -14,6 +14,9 @@ using ffd::kMaxBlocksPerSplit;
 using ffd::kMaxSplits;
 using ffd::kWaves;
 
+// the ranked selection rules sort a row of block scores in LDS (8-byte keys)
+constexpr int kMaxRankedBlocks = 16384;
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Shape checks shared by every call.  `block` must be known (64/128) for the decode calls.
@@ -87,7 +90,8 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
                          float* out, float* lse, uint8_t* keep_mask, void* workspace,
                          size_t workspace_bytes, hipStream_t stream, bool sparse,
                          const int8_t* Kr = nullptr, const float* res_scales = nullptr,
-                         int bits = 0, const int32_t* seq_lens = nullptr)
+                         int bits = 0, const int32_t* seq_lens = nullptr,
+                         const uint8_t* ext_mask = nullptr)
 {
     const bool res = bits != 0;
     ffd_status st = check_dims(dims, block);
@@ -101,7 +105,7 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
     if (!aligned16(q) || (K && !aligned16(K)) || !aligned16(V) || !aligned16(out) ||
         (lse && !aligned16(lse)) || (keep_mask && !aligned16(keep_mask)))
         return FFD_ERR_INVALID_ARG;
-    if (sparse) {
+    if (sparse && !ext_mask) {
         if (!Kq || !scales || !aligned16(Kq) || !aligned16(scales)) return FFD_ERR_INVALID_ARG;
         if (isnan(delta) || delta < 0.0f) return FFD_ERR_INVALID_ARG;
     }
@@ -140,6 +144,7 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
     p.R = (p.n_blocks + S - 1) / S;
     p.seq_lens = seq_lens;
     p.mask_stride = p.n_blocks;
+    p.ext_mask = ext_mask;
     p.delta = delta;
     p.kappa = (float)(0.5 / (127.0 * sqrt((double)kHeadDim)));
     p.c_log2 = (float)(1.4426950408889634 / sqrt((double)kHeadDim));
@@ -334,6 +339,105 @@ ffd_status ffd_append_token(const ffd_dims* dims, const void* k_new, const void*
     a.cap = dims->seq_cap;
     a.T = block;
     return finish(ffd::launch_append(a, dims->dtype == FFD_BF16, stream));
+}
+
+ffd_status ffd_decode_masked(const ffd_dims* dims, const void* q, const void* K, const void* V,
+                             const uint8_t* keep_mask, int32_t block, float* out, float* lse,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!keep_mask) return FFD_ERR_INVALID_ARG;
+    return decode_common(dims, q, K, V, nullptr, nullptr, 0.0f, block, out, lse, nullptr,
+                         workspace, workspace_bytes, stream, true, nullptr, nullptr, 0, nullptr,
+                         keep_mask);
+}
+
+ffd_status ffd_block_bounds(const ffd_dims* dims, const void* K, int32_t tok_begin,
+                            int32_t tok_end, int32_t block, void* kmin, void* kmax,
+                            hipStream_t stream)
+{
+    int j_first = 0, j_last = -1;
+    ffd_status st = append_range(dims, tok_begin, tok_end, block, &j_first, &j_last);
+    if (st != FFD_OK) return st;
+    if (dims->batch == 0) return FFD_OK;
+    if (!K || !kmin || !kmax || !aligned16(K) || !aligned16(kmin) || !aligned16(kmax))
+        return FFD_ERR_INVALID_ARG;
+    ffd::BoundsParams b{};
+    b.K = K;
+    b.kmin = kmin;
+    b.kmax = kmax;
+    b.B = dims->batch;
+    b.Hkv = dims->n_kv_heads;
+    b.cap = dims->seq_cap;
+    b.T = block;
+    b.j_first = j_first;
+    b.n_blocks = j_last - j_first + 1;
+    return finish(ffd::launch_bounds(b, dims->dtype == FFD_BF16, stream));
+}
+
+ffd_status ffd_block_scores(const ffd_dims* dims, int32_t kind, const void* q, const void* K,
+                            const uint8_t* Kq, const float* scales, const void* kmin,
+                            const void* kmax, int32_t block, float* scores, hipStream_t stream)
+{
+    ffd_status st = check_dims(dims, block);
+    if (st != FFD_OK) return st;
+    if (kind < FFD_SCORE_SCAN || kind > FFD_SCORE_EXACT) return FFD_ERR_INVALID_ARG;
+    if (dims->batch == 0) return FFD_OK;
+    if (!q || !scores || !aligned16(q) || !aligned16(scores)) return FFD_ERR_INVALID_ARG;
+    if (kind == FFD_SCORE_SCAN && (!Kq || !scales || !aligned16(Kq) || !aligned16(scales)))
+        return FFD_ERR_INVALID_ARG;
+    if (kind == FFD_SCORE_BOUNDS && (!kmin || !kmax || !aligned16(kmin) || !aligned16(kmax)))
+        return FFD_ERR_INVALID_ARG;
+    if (kind == FFD_SCORE_EXACT && (!K || !aligned16(K))) return FFD_ERR_INVALID_ARG;
+    ffd::ScoreParams p{};
+    p.q = q;
+    p.K = K;
+    p.Kq = Kq;
+    p.scales = scales;
+    p.kmin = kmin;
+    p.kmax = kmax;
+    p.scores = scores;
+    p.B = dims->batch;
+    p.Hq = dims->n_q_heads;
+    p.Hkv = dims->n_kv_heads;
+    p.G = dims->n_q_heads / dims->n_kv_heads;
+    p.cap = dims->seq_cap;
+    p.T = block;
+    p.n_full = dims->seq_len / block;
+    p.kappa = (float)(0.5 / (127.0 * sqrt((double)kHeadDim)));
+    p.inv_sqrt_d = (float)(1.0 / sqrt((double)kHeadDim));
+    return finish(ffd::launch_scores(p, kind, dims->dtype == FFD_BF16, stream));
+}
+
+ffd_status ffd_select_blocks(const ffd_dims* dims, int32_t rule, const float* scores,
+                             const float* pseudo_max, float param, int32_t block,
+                             uint8_t* keep_mask, hipStream_t stream)
+{
+    ffd_status st = check_dims(dims, block);
+    if (st != FFD_OK) return st;
+    if (rule < FFD_SELECT_TOP_DELTA || rule > FFD_SELECT_TOP_P || isnan(param))
+        return FFD_ERR_INVALID_ARG;
+    if (rule == FFD_SELECT_TOP_DELTA && param < 0.0f) return FFD_ERR_INVALID_ARG;
+    if (rule == FFD_SELECT_TOP_K && !(param >= 0.0f && param < 2147483648.0f))
+        return FFD_ERR_INVALID_ARG;
+    if (rule == FFD_SELECT_TOP_P && !(param > 0.0f && param <= 1.0f)) return FFD_ERR_INVALID_ARG;
+    const int n_full = dims->seq_len / block;
+    if (rule != FFD_SELECT_TOP_DELTA && n_full > kMaxRankedBlocks) return FFD_ERR_UNSUPPORTED;
+    if (dims->batch == 0) return FFD_OK;
+    if (!scores || !keep_mask || (pseudo_max && (reinterpret_cast<uintptr_t>(pseudo_max) & 3u)) ||
+        (reinterpret_cast<uintptr_t>(scores) & 3u))
+        return FFD_ERR_INVALID_ARG;
+    ffd::SelectParams p{};
+    p.scores = scores;
+    p.pseudo_max = rule == FFD_SELECT_TOP_DELTA ? pseudo_max : nullptr;
+    p.keep = keep_mask;
+    p.rows = dims->batch * dims->n_q_heads;
+    p.n_full = n_full;
+    p.n_blocks = (dims->seq_len + block - 1) / block;
+    int n2 = 1;
+    while (n2 < n_full) n2 <<= 1;
+    p.n_pow2 = n2;
+    p.param = param;
+    return finish(ffd::launch_select(p, rule, stream));
 }
 
 }  // extern "C"

@@ -41,6 +41,8 @@ struct DecodeParams {
                               // to [0, L]; L, n_full and n_blocks are then the bounds the splits
                               // cover and each work-group derives its sequence's own
     int mask_stride;          // keep_mask row length in blocks
+    const uint8_t* ext_mask;  // optional [B][Hq][mask_stride] selection made by the caller: the
+                              // sparse kernel then attends over these blocks and scans nothing
 };
 
 struct QuantParams {
@@ -66,7 +68,43 @@ struct AppendParams {
     int B, Hkv, cap, T;
 };
 
+// Per-block metadata of the selection comparators: min and max of every channel of a key block.
+struct BoundsParams {
+    const void* K;
+    void* kmin;  // [B][Hkv][cap/T][d], in K's dtype
+    void* kmax;
+    int B, Hkv, cap, T;
+    int j_first, n_blocks;
+};
+
+// Block scores for the selection comparators: kind 0 = the scan estimate (Alg. 1), 1 = the
+// min/max upper bound, 2 = the exact largest score of the block.
+struct ScoreParams {
+    const void* q;
+    const void* K;
+    const uint8_t* Kq;
+    const float* scales;
+    const void* kmin;
+    const void* kmax;
+    float* scores;  // [B][Hq][n_full]
+    int B, Hq, Hkv, G, cap, T, n_full;
+    float kappa;       // as DecodeParams
+    float inv_sqrt_d;  // (float)(1 / sqrt(d))
+};
+
+// One selection rule over per-block scores, one work-group per (b, query head) row.
+struct SelectParams {
+    const float* scores;      // [rows][n_full]
+    const float* pseudo_max;  // optional [rows] (top-delta)
+    uint8_t* keep;            // [rows][n_blocks]
+    int rows, n_full, n_blocks, n_pow2;
+    float param;              // delta, k or p
+};
+
 // Launchers (ffd_kernels.hip).  Return the hipError_t of the launch.
+hipError_t launch_bounds(const BoundsParams& p, bool bf16, hipStream_t stream);
+hipError_t launch_scores(const ScoreParams& p, int kind, bool bf16, hipStream_t stream);
+hipError_t launch_select(const SelectParams& p, int rule, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, bool bf16, bool sparse, hipStream_t stream);
 hipError_t launch_quantize(const QuantParams& p, bool bf16, hipStream_t stream);

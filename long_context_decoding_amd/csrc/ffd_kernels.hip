@@ -717,108 +717,122 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
     };
 
     if constexpr (SPARSE) {
-        constexpr int HPL = (G + 3) / 4;
-        float qw[HPL][8];
-#pragma unroll
-        for (int k = 0; k < HPL; ++k) {
-            const int h = (G >= 4) ? (kg + 4 * k) : (kg % G);
-            const int hq = h0 + h;
-            if constexpr (BF16) {
-                const uint4 x = *reinterpret_cast<const uint4*>(
-                    static_cast<const __bf16*>(p.q) + (size_t)hq * D + col * 8);
-                qw[k][0] = bf16_lo(x.x); qw[k][1] = bf16_hi(x.x);
-                qw[k][2] = bf16_lo(x.y); qw[k][3] = bf16_hi(x.y);
-                qw[k][4] = bf16_lo(x.z); qw[k][5] = bf16_hi(x.z);
-                qw[k][6] = bf16_lo(x.w); qw[k][7] = bf16_hi(x.w);
-            } else {
-                const float4* qp = reinterpret_cast<const float4*>(
-                    static_cast<const float*>(p.q) + (size_t)hq * D + col * 8);
-                const float4 a = qp[0], c = qp[1];
-                qw[k][0] = a.x; qw[k][1] = a.y; qw[k][2] = a.z; qw[k][3] = a.w;
-                qw[k][4] = c.x; qw[k][5] = c.y; qw[k][6] = c.z; qw[k][7] = c.w;
-            }
-        }
-
-        const uint8_t* kq_bg = p.Kq + (size_t)bg * p.cap * (D * BITS / 8);
-        const float* sc_bg = p.scales + (size_t)bg * (p.cap / T) * D;
-        const int nf = nf_b;
-        const u32 all_heads = (1u << G) - 1u;
-        // Forced blocks of the split (sink 0, the local block nf-1 and a partial tail) are kept
-        // for every head; every other block of the split is a scan item of exactly one wave.
-        if (w == 0) {
-            for (int t = lane; t < je - jb; t += 64) {
-                const int j = jb + t;
-                if (j == 0 || j >= nf - 1) {
-                    sh.kbits[t] = (uint8_t)all_heads;
-                    if (p.keep_mask)
-#pragma unroll
-                        for (int h = 0; h < G; ++h) p.keep_mask[(size_t)(h0 + h) * p.mask_stride + j] = 1;
-                }
-            }
-        }
-        // Scan items of this wave: the sink and local blocks (each wave forms the pseudo-max of
-        // Eq. 3 itself, so that it can apply Eq. 1 to its own blocks at once), then the split's
-        // non-forced full blocks j_lo + w, j_lo + w + kWaves, ...
-        const int n_pro = nf >= 1 ? 2 : 0;
-        const int j_lo = max(jb, 1);
-        const int j_hi = min(je, nf - 1);
-        const int n_main = max(j_hi - j_lo, 0);
-        const int n_items = n_pro + (n_main > w ? (n_main - w + kWaves - 1) / kWaves : 0);
-        auto block_of = [&](int k) -> int {
-            if (k < n_pro) return k == 0 ? 0 : nf - 1;
-            return j_lo + w + (k - n_pro) * kWaves;
-        };
-        if (n_items > 0) {
-            float pro0 = 0.0f, theta = 0.0f;  // lanes < G: head = lane
-            auto load = [&](ScanRegs<T, BITS>& r, int k) {
-                const int j = block_of(k);
-                scan_load<T, BITS>(r, kq_bg + (size_t)j * T * (D * BITS / 8), sc_bg + (size_t)j * D,
-                                   lane);
-            };
-            auto process = [&](const ScanRegs<T, BITS>& r, int k) {
-                const float shat = scan_compute<T, G, BITS>(r, qw, p.kappa, ws, lane);
-                if (k == 0) {
-                    pro0 = shat;
-                } else if (k == 1) {
-                    theta = __fsub_rn(fmaxf(pro0, shat), p.delta);
+        if (!p.ext_mask) {
+            constexpr int HPL = (G + 3) / 4;
+            float qw[HPL][8];
+    #pragma unroll
+            for (int k = 0; k < HPL; ++k) {
+                const int h = (G >= 4) ? (kg + 4 * k) : (kg % G);
+                const int hq = h0 + h;
+                if constexpr (BF16) {
+                    const uint4 x = *reinterpret_cast<const uint4*>(
+                        static_cast<const __bf16*>(p.q) + (size_t)hq * D + col * 8);
+                    qw[k][0] = bf16_lo(x.x); qw[k][1] = bf16_hi(x.x);
+                    qw[k][2] = bf16_lo(x.y); qw[k][3] = bf16_hi(x.y);
+                    qw[k][4] = bf16_lo(x.z); qw[k][5] = bf16_hi(x.z);
+                    qw[k][6] = bf16_lo(x.w); qw[k][7] = bf16_hi(x.w);
                 } else {
-                    // selection, Eq. 1 with the pseudo-max: shat >= mtilde - delta
-                    const int j = block_of(k);
-                    const bool keep = lane < G && shat >= theta;
-                    const u32 bits = (u32)__ballot(keep) & all_heads;
-                    if (lane == 0) sh.kbits[j - jb] = (uint8_t)bits;
-                    if (p.keep_mask && lane < G)
-                        p.keep_mask[(size_t)(h0 + lane) * p.mask_stride + j] = keep ? 1 : 0;
+                    const float4* qp = reinterpret_cast<const float4*>(
+                        static_cast<const float*>(p.q) + (size_t)hq * D + col * 8);
+                    const float4 a = qp[0], c = qp[1];
+                    qw[k][0] = a.x; qw[k][1] = a.y; qw[k][2] = a.z; qw[k][3] = a.w;
+                    qw[k][4] = c.x; qw[k][5] = c.y; qw[k][6] = c.z; qw[k][7] = c.w;
                 }
-            };
-            // Two items in flight: item k + 1 is loaded while item k is computed.  The steady
-            // loop issues loads only for items that exist and the epilogue issues none past the
-            // end, so no load is left outstanding.  The scheduling barriers keep each prefetch
-            // issued before the computation that follows it in program order (otherwise the
-            // scheduler hoists that computation's first use of its buffer above the loads, and
-            // the in-order wait counter then waits for the prefetch too).
-            ScanRegs<T, BITS> ra, rb;
-            load(ra, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            publish_q();
-            int k = 0;
-            for (; k + 2 < n_items; k += 2) {
-                load(rb, k + 1);
-                __builtin_amdgcn_sched_barrier(0);
-                process(ra, k);
-                load(ra, k + 2);
-                __builtin_amdgcn_sched_barrier(0);
-                process(rb, k + 1);
             }
-            if (k + 1 < n_items) {
-                load(rb, k + 1);
+
+            const uint8_t* kq_bg = p.Kq + (size_t)bg * p.cap * (D * BITS / 8);
+            const float* sc_bg = p.scales + (size_t)bg * (p.cap / T) * D;
+            const int nf = nf_b;
+            const u32 all_heads = (1u << G) - 1u;
+            // Forced blocks of the split (sink 0, the local block nf-1 and a partial tail) are kept
+            // for every head; every other block of the split is a scan item of exactly one wave.
+            if (w == 0) {
+                for (int t = lane; t < je - jb; t += 64) {
+                    const int j = jb + t;
+                    if (j == 0 || j >= nf - 1) {
+                        sh.kbits[t] = (uint8_t)all_heads;
+                        if (p.keep_mask)
+    #pragma unroll
+                            for (int h = 0; h < G; ++h) p.keep_mask[(size_t)(h0 + h) * p.mask_stride + j] = 1;
+                    }
+                }
+            }
+            // Scan items of this wave: the sink and local blocks (each wave forms the pseudo-max of
+            // Eq. 3 itself, so that it can apply Eq. 1 to its own blocks at once), then the split's
+            // non-forced full blocks j_lo + w, j_lo + w + kWaves, ...
+            const int n_pro = nf >= 1 ? 2 : 0;
+            const int j_lo = max(jb, 1);
+            const int j_hi = min(je, nf - 1);
+            const int n_main = max(j_hi - j_lo, 0);
+            const int n_items = n_pro + (n_main > w ? (n_main - w + kWaves - 1) / kWaves : 0);
+            auto block_of = [&](int k) -> int {
+                if (k < n_pro) return k == 0 ? 0 : nf - 1;
+                return j_lo + w + (k - n_pro) * kWaves;
+            };
+            if (n_items > 0) {
+                float pro0 = 0.0f, theta = 0.0f;  // lanes < G: head = lane
+                auto load = [&](ScanRegs<T, BITS>& r, int k) {
+                    const int j = block_of(k);
+                    scan_load<T, BITS>(r, kq_bg + (size_t)j * T * (D * BITS / 8), sc_bg + (size_t)j * D,
+                                       lane);
+                };
+                auto process = [&](const ScanRegs<T, BITS>& r, int k) {
+                    const float shat = scan_compute<T, G, BITS>(r, qw, p.kappa, ws, lane);
+                    if (k == 0) {
+                        pro0 = shat;
+                    } else if (k == 1) {
+                        theta = __fsub_rn(fmaxf(pro0, shat), p.delta);
+                    } else {
+                        // selection, Eq. 1 with the pseudo-max: shat >= mtilde - delta
+                        const int j = block_of(k);
+                        const bool keep = lane < G && shat >= theta;
+                        const u32 bits = (u32)__ballot(keep) & all_heads;
+                        if (lane == 0) sh.kbits[j - jb] = (uint8_t)bits;
+                        if (p.keep_mask && lane < G)
+                            p.keep_mask[(size_t)(h0 + lane) * p.mask_stride + j] = keep ? 1 : 0;
+                    }
+                };
+                // Two items in flight: item k + 1 is loaded while item k is computed.  The steady
+                // loop issues loads only for items that exist and the epilogue issues none past the
+                // end, so no load is left outstanding.  The scheduling barriers keep each prefetch
+                // issued before the computation that follows it in program order (otherwise the
+                // scheduler hoists that computation's first use of its buffer above the loads, and
+                // the in-order wait counter then waits for the prefetch too).
+                ScanRegs<T, BITS> ra, rb;
+                load(ra, 0);
                 __builtin_amdgcn_sched_barrier(0);
-                process(ra, k);
-                process(rb, k + 1);
+                publish_q();
+                int k = 0;
+                for (; k + 2 < n_items; k += 2) {
+                    load(rb, k + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    process(ra, k);
+                    load(ra, k + 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                    process(rb, k + 1);
+                }
+                if (k + 1 < n_items) {
+                    load(rb, k + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    process(ra, k);
+                    process(rb, k + 1);
+                } else {
+                    process(ra, k);
+                }
             } else {
-                process(ra, k);
+                publish_q();
             }
         } else {
+            // selection made outside (a comparator rule): every block's head mask is read from
+            // the caller's keep mask; nothing is scanned
+            for (int t = threadIdx.x; t < je - jb; t += kWaves * 64) {
+                u32 bits = 0;
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+                    bits |= (p.ext_mask[(size_t)(h0 + h) * p.mask_stride + jb + t] != 0 ? 1u : 0u)
+                            << h;
+                sh.kbits[t] = (uint8_t)bits;
+            }
             publish_q();
         }
         __syncthreads();  // kbits complete, query rows in LDS
@@ -1332,6 +1346,260 @@ hipError_t launch_res_g(const DecodeParams& p, hipStream_t stream)
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------------
+// Selection comparators (Sec. 4.5 Table 3; Sec. 5.1 Fig. 6; Sec. 5.2 Fig. 5): per-block scores
+// written out, then one rule per (b, query head) row.  They are unfused on purpose: the rules
+// other than top-delta need every block's score of a row before they can decide.
+// ------------------------------------------------------------------------------------------
+
+// Min and max of every channel over a key block's T tokens (one thread per channel), stored in
+// K's dtype (the min and max of bf16 values are bf16 values).
+template <int T, bool BF16>
+__global__ __launch_bounds__(128) void bounds_kernel(BoundsParams p)
+{
+    const int j = p.j_first + blockIdx.x;
+    const int bg = blockIdx.y;
+    const int c = threadIdx.x;
+    const size_t row0 = (size_t)bg * p.cap + (size_t)j * T;
+    const size_t o = ((size_t)bg * (p.cap / T) + j) * D + c;
+    if constexpr (BF16) {
+        const unsigned short* K = static_cast<const unsigned short*>(p.K);
+        unsigned short bmn = K[row0 * D + c], bmx = bmn;
+        float mn = as_f((int)((u32)bmn << 16)), mx = mn;
+        for (int t = 1; t < T; ++t) {
+            const unsigned short b = K[(row0 + t) * D + c];
+            const float x = as_f((int)((u32)b << 16));
+            if (x < mn) { mn = x; bmn = b; }
+            if (x > mx) { mx = x; bmx = b; }
+        }
+        static_cast<unsigned short*>(p.kmin)[o] = bmn;
+        static_cast<unsigned short*>(p.kmax)[o] = bmx;
+    } else {
+        const float* K = static_cast<const float*>(p.K);
+        float mn = K[row0 * D + c], mx = mn;
+        for (int t = 1; t < T; ++t) {
+            const float x = K[(row0 + t) * D + c];
+            mn = fminf(mn, x);
+            mx = fmaxf(mx, x);
+        }
+        static_cast<float*>(p.kmin)[o] = mn;
+        static_cast<float*>(p.kmax)[o] = mx;
+    }
+}
+
+__device__ __forceinline__ float elem(const void* base, size_t i, bool bf16)
+{
+    return bf16 ? as_f((int)((u32) static_cast<const unsigned short*>(base)[i] << 16))
+                : static_cast<const float*>(base)[i];
+}
+
+// Block scores of the full blocks, one work-group (4 waves) per (b, kv head, 16 blocks); wave w
+// takes blocks w, w + 4, ... of the chunk.  KIND 0: the scan estimate shat of Alg. 1 (the decode
+// kernel's integer scan); KIND 1: sum_c max(q_c mn_c, q_c mx_c) / sqrt(d) (a Quest-style upper
+// bound; fp32, lane-parallel over channels, fixed reduction order); KIND 2: the exact largest
+// q.k / sqrt(d) of the block (bf16 or fp32 MFMA over its 16-token tiles).
+template <int T, int G, bool BF16, int KIND>
+__global__ __launch_bounds__(kWaves * 64) void score_kernel(ScoreParams p)
+{
+    constexpr int kChunk = 16;
+    __shared__ WaveScratch<G> wsh[kWaves];
+    __shared__ float4 qs[G * D * (BF16 ? 2 : 4) / 16];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int col = lane & 15, kg = lane >> 4;
+    const int bg = blockIdx.y;
+    const int b = bg / p.Hkv, g = bg % p.Hkv;
+    const int h0 = b * p.Hq + g * G;
+    const int j0 = blockIdx.x * kChunk;
+    const int j1 = min(p.n_full, j0 + kChunk);
+    const size_t esz = BF16 ? 2 : 4;
+    if constexpr (KIND == 2) {
+        constexpr int kQ16 = G * D * (BF16 ? 2 : 4) / 16;
+        const float4* src =
+            reinterpret_cast<const float4*>(static_cast<const char*>(p.q) + (size_t)h0 * D * esz);
+        for (int i = threadIdx.x; i < kQ16; i += kWaves * 64) qs[i] = src[i];
+        __syncthreads();
+    }
+    if constexpr (KIND == 0) {
+        constexpr int HPL = (G + 3) / 4;
+        float qw[HPL][8];
+#pragma unroll
+        for (int k = 0; k < HPL; ++k) {
+            const int h = (G >= 4) ? (kg + 4 * k) : (kg % G);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                qw[k][i] = elem(p.q, (size_t)(h0 + h) * D + col * 8 + i, BF16);
+        }
+        const uint8_t* kq_bg = p.Kq + (size_t)bg * p.cap * (D / 2);
+        const float* sc_bg = p.scales + (size_t)bg * (p.cap / T) * D;
+        for (int j = j0 + w; j < j1; j += kWaves) {
+            ScanRegs<T, 4> r;
+            scan_load<T, 4>(r, kq_bg + (size_t)j * T * (D / 2), sc_bg + (size_t)j * D, lane);
+            const float shat = scan_compute<T, G, 4>(r, qw, p.kappa, wsh[w], lane);
+            if (lane < G) p.scores[(size_t)(h0 + lane) * p.n_full + j] = shat;
+        }
+    } else if constexpr (KIND == 1) {
+        const size_t mrow = (size_t)bg * (p.cap / T);
+        for (int j = j0 + w; j < j1; j += kWaves) {
+            const size_t mo = (mrow + j) * D;
+            const float mn0 = elem(p.kmin, mo + 2 * lane, BF16);
+            const float mn1 = elem(p.kmin, mo + 2 * lane + 1, BF16);
+            const float mx0 = elem(p.kmax, mo + 2 * lane, BF16);
+            const float mx1 = elem(p.kmax, mo + 2 * lane + 1, BF16);
+            for (int h = 0; h < G; ++h) {
+                const float q0 = elem(p.q, (size_t)(h0 + h) * D + 2 * lane, BF16);
+                const float q1 = elem(p.q, (size_t)(h0 + h) * D + 2 * lane + 1, BF16);
+                float x = fmaxf(__fmul_rn(q0, mn0), __fmul_rn(q0, mx0)) +
+                          fmaxf(__fmul_rn(q1, mn1), __fmul_rn(q1, mx1));
+                x = wave_sum(x);
+                if (lane == 0) p.scores[(size_t)(h0 + h) * p.n_full + j] = x * p.inv_sqrt_d;
+            }
+        }
+    } else {
+        const void* qrow = reinterpret_cast<const char*>(qs) + (size_t)(col % G) * D * esz;
+        v8bf qv[4];
+        if constexpr (BF16) {
+            const __bf16* qb = static_cast<const __bf16*>(qrow);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                qv[ks] = *reinterpret_cast<const v8bf*>(qb + ks * 32 + kg * 8);
+        }
+        const char* Kbg = static_cast<const char*>(p.K) + (size_t)bg * p.cap * D * esz;
+        for (int j = j0 + w; j < j1; j += kWaves) {
+            float m = kNegInf;
+            for (int t = 0; t < T / 16; ++t) {
+                TileRegs<BF16> r;
+                const int t0 = j * T + 16 * t;
+                if constexpr (BF16) {
+                    const __bf16* Kp = reinterpret_cast<const __bf16*>(Kbg);
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        r.k[ks] = *reinterpret_cast<const uint4*>(Kp + (size_t)(t0 + col) * D +
+                                                                  ks * 32 + kg * 8);
+                } else {
+                    const float* Kp = reinterpret_cast<const float*>(Kbg);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        r.k[i] = *reinterpret_cast<const float4*>(Kp + (size_t)(t0 + col) * D +
+                                                                  kg * 32 + i * 4);
+                }
+                const v4f acc = tile_scores<BF16>(r, qrow, qv, lane);
+                m = fmaxf(m, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+            }
+            m = fmax32(fmax16(m));  // over the four token groups: column col = head col % G
+            if (kg == 0 && col < G) p.scores[(size_t)(h0 + col) * p.n_full + j] = m * p.inv_sqrt_d;
+        }
+    }
+}
+
+// Order-preserving map of a float's bits to an unsigned integer, and its inverse.
+__device__ __forceinline__ u32 f_ord(float x)
+{
+    const u32 u = (u32)as_i(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float f_unord(u32 o)
+{
+    return as_f((int)((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o));
+}
+
+// One selection rule over a row of block scores (one work-group of 256 threads per (b, query
+// head)).  RULE 0 top-delta: theta = RN(mtilde - delta), mtilde the given pseudo-max or
+// max(s_0, s_{nf-1}); keep s_j >= theta.  RULE 1 top-k and RULE 2 top-p rank the row by a bitonic
+// sort in LDS of keys (~ord(s_j) << 32 | j) -- descending score, ties to the lower index --; top-k
+// keeps the first k, top-p the shortest prefix whose exp(s - s_max) mass reaches p of the total
+// (fp32 sums in a fixed order: 256 contiguous chunks, then their running sum).  Every rule keeps
+// block 0, the last full block and a partial tail.
+template <int RULE>
+__global__ __launch_bounds__(256) void select_kernel(SelectParams p)
+{
+    extern __shared__ unsigned long long keys[];  // n_pow2 keys, then n_blocks keep flags
+    __shared__ float csum[256];
+    __shared__ float cpre[256];
+    __shared__ float ctot;
+    __shared__ int first_hit;
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nf = p.n_full, nb = p.n_blocks;
+    const float* s = p.scores + (size_t)row * nf;
+    uint8_t* keep = p.keep + (size_t)row * nb;
+    auto forced = [&](int j) { return j == 0 || j >= nf - 1; };
+    if (RULE == 0 || nf == 0) {
+        float theta = kNegInf;
+        if (nf > 0) {
+            const float mt = p.pseudo_max ? p.pseudo_max[row] : fmaxf(s[0], s[nf - 1]);
+            theta = __fsub_rn(mt, p.param);
+        }
+        for (int j = tid; j < nb; j += 256) {
+            bool k = forced(j);  // every j >= nf - 1 is forced, so s[j] is read only for j < nf
+            if (!k && RULE == 0) k = s[j] >= theta;
+            keep[j] = k ? 1 : 0;
+        }
+        return;
+    }
+    uint8_t* flag = reinterpret_cast<uint8_t*>(keys + p.n_pow2);
+    const int N = p.n_pow2;
+    for (int i = tid; i < N; i += 256)
+        keys[i] = i < nf ? ((unsigned long long)(~f_ord(s[i])) << 32) | (u32)i : ~0ull;
+    for (int j = tid; j < nb; j += 256) flag[j] = forced(j) ? 1 : 0;
+    __syncthreads();
+    for (int k = 2; k <= N; k <<= 1) {
+        for (int jj = k >> 1; jj > 0; jj >>= 1) {
+            for (int i = tid; i < N; i += 256) {
+                const int ixj = i ^ jj;
+                if (ixj > i) {
+                    const unsigned long long a = keys[i], c = keys[ixj];
+                    if ((a > c) == ((i & k) == 0)) {
+                        keys[i] = c;
+                        keys[ixj] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    int n_sel;
+    if (RULE == 1) {
+        n_sel = min(max((int)p.param, 0), nf);
+    } else {
+        // mass of every ranked block relative to the top one, in fp32; chunk sums, their running
+        // sum, then the first position whose cumulative mass reaches p of the total
+        const float smax = f_unord(~(u32)(keys[0] >> 32));
+        const int per = (nf + 255) / 256;
+        const int c0 = tid * per, c1 = min(nf, c0 + per);
+        float run = 0.0f;
+        for (int i = c0; i < c1; ++i)
+            run += __builtin_amdgcn_exp2f((f_unord(~(u32)(keys[i] >> 32)) - smax) *
+                                          1.4426950408889634f);
+        csum[tid] = run;
+        if (tid == 0) first_hit = nf;
+        __syncthreads();
+        if (tid == 0) {
+            float acc = 0.0f;
+            for (int t = 0; t < 256; ++t) {
+                cpre[t] = acc;
+                acc += csum[t];
+            }
+            ctot = acc;
+        }
+        __syncthreads();
+        const float target = p.param * ctot;
+        run = cpre[tid];
+        for (int i = c0; i < c1; ++i) {
+            run += __builtin_amdgcn_exp2f((f_unord(~(u32)(keys[i] >> 32)) - smax) *
+                                          1.4426950408889634f);
+            if (run >= target) {
+                atomicMin(&first_hit, i);
+                break;
+            }
+        }
+        __syncthreads();
+        n_sel = min(first_hit + 1, nf);
+    }
+    for (int r = tid; r < n_sel; r += 256) flag[(u32)keys[r]] = 1;
+    __syncthreads();
+    for (int j = tid; j < nb; j += 256) keep[j] = flag[j];
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, bool bf16, bool sparse, hipStream_t stream)
@@ -1409,6 +1677,68 @@ hipError_t launch_quantize(const QuantParams& p, bool bf16, hipStream_t stream)
     } else {
         return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_bounds(const BoundsParams& p, bool bf16, hipStream_t stream)
+{
+    if (p.n_blocks <= 0) return hipSuccess;
+    const dim3 grid(p.n_blocks, p.B * p.Hkv), block(D);
+    if (p.T == 64) {
+        if (bf16) hipLaunchKernelGGL((bounds_kernel<64, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((bounds_kernel<64, false>), grid, block, 0, stream, p);
+    } else if (p.T == 128) {
+        if (bf16) hipLaunchKernelGGL((bounds_kernel<128, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((bounds_kernel<128, false>), grid, block, 0, stream, p);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+namespace {
+template <int T, int G, bool BF16>
+void launch_scores_k(const ScoreParams& p, int kind, hipStream_t stream)
+{
+    const dim3 grid((p.n_full + 15) / 16, p.B * p.Hkv), block(kWaves * 64);
+    if (kind == 0) hipLaunchKernelGGL((score_kernel<T, G, BF16, 0>), grid, block, 0, stream, p);
+    else if (kind == 1) hipLaunchKernelGGL((score_kernel<T, G, BF16, 1>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((score_kernel<T, G, BF16, 2>), grid, block, 0, stream, p);
+}
+template <int T, bool BF16>
+hipError_t launch_scores_g(const ScoreParams& p, int kind, hipStream_t stream)
+{
+    switch (p.G) {
+    case 1: launch_scores_k<T, 1, BF16>(p, kind, stream); break;
+    case 2: launch_scores_k<T, 2, BF16>(p, kind, stream); break;
+    case 4: launch_scores_k<T, 4, BF16>(p, kind, stream); break;
+    case 8: launch_scores_k<T, 8, BF16>(p, kind, stream); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_scores(const ScoreParams& p, int kind, bool bf16, hipStream_t stream)
+{
+    if (p.n_full <= 0 || p.B <= 0) return hipSuccess;
+    if (p.T == 64) return bf16 ? launch_scores_g<64, true>(p, kind, stream)
+                               : launch_scores_g<64, false>(p, kind, stream);
+    if (p.T == 128) return bf16 ? launch_scores_g<128, true>(p, kind, stream)
+                                : launch_scores_g<128, false>(p, kind, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_select(const SelectParams& p, int rule, hipStream_t stream)
+{
+    if (p.rows <= 0) return hipSuccess;
+    const size_t dyn = rule == 0 ? 0 : (size_t)p.n_pow2 * 8 + (size_t)((p.n_blocks + 15) & ~15);
+    if (rule == 0)
+        hipLaunchKernelGGL(select_kernel<0>, dim3(p.rows), dim3(256), dyn, stream, p);
+    else if (rule == 1)
+        hipLaunchKernelGGL(select_kernel<1>, dim3(p.rows), dim3(256), dyn, stream, p);
+    else
+        hipLaunchKernelGGL(select_kernel<2>, dim3(p.rows), dim3(256), dyn, stream, p);
     return hipGetLastError();
 }
 

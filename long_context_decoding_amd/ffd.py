@@ -7,8 +7,8 @@ or cannot be loaded, every call raises.
 
 Names follow the C ABI: ``quantize_k_append``, ``decode_sparse``, ``decode_dense``,
 ``quantize_k_residual_append``, ``decode_sparse_residual``, ``append_token``,
-``decode_sparse_varlen``, ``decode_dense_varlen``, ``workspace_bytes``, ``workspace_init``,
-``num_splits``.
+``decode_sparse_varlen``, ``decode_dense_varlen``, ``block_bounds``, ``block_scores``,
+``select_blocks``, ``decode_masked``, ``workspace_bytes``, ``workspace_init``, ``num_splits``.
 """
 from __future__ import annotations
 
@@ -75,6 +75,14 @@ def lib():
         L.ffd_decode_sparse_varlen.restype = i32
         L.ffd_decode_dense_varlen.argtypes = [D, P, P, P, P, i32, P, P, P, sz, P]
         L.ffd_decode_dense_varlen.restype = i32
+        L.ffd_block_bounds.argtypes = [D, P, i32, i32, i32, P, P, P]
+        L.ffd_block_bounds.restype = i32
+        L.ffd_block_scores.argtypes = [D, i32, P, P, P, P, P, P, i32, P, P]
+        L.ffd_block_scores.restype = i32
+        L.ffd_select_blocks.argtypes = [D, i32, P, P, f32, i32, P, P]
+        L.ffd_select_blocks.restype = i32
+        L.ffd_decode_masked.argtypes = [D, P, P, P, P, i32, P, P, P, sz, P]
+        L.ffd_decode_masked.restype = i32
         _lib = L
     return _lib
 
@@ -374,4 +382,85 @@ def decode_dense_varlen(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_l
     _check(lib().ffd_decode_dense_varlen(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V),
                                          _ptr(seq_lens), block, _ptr(out), _ptr(lse),
                                          _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+SCORE_SCAN, SCORE_BOUNDS, SCORE_EXACT = 0, 1, 2
+SELECT_TOP_DELTA, SELECT_TOP_K, SELECT_TOP_P = 0, 1, 2
+
+
+def alloc_bounds(K: torch.Tensor, block: int):
+    """Zeroed (kmin, kmax) [B, Hkv, cap/block, d] in K's dtype."""
+    B, Hkv, cap, d = K.shape
+    shape = (B, Hkv, cap // block, d)
+    return (torch.zeros(shape, dtype=K.dtype, device=K.device),
+            torch.zeros(shape, dtype=K.dtype, device=K.device))
+
+
+def block_bounds(K: torch.Tensor, tok_begin: int, tok_end: int, block: int, kmin: torch.Tensor,
+                 kmax: torch.Tensor, seq_len: int | None = None, stream=None) -> None:
+    """Per-channel min/max of every key block completed by tokens [tok_begin, tok_end)."""
+    B, Hkv, cap, d = K.shape
+    _need(K, "K", None, None, K.device)
+    for name, t in (("kmin", kmin), ("kmax", kmax)):
+        _need(t, name, K.dtype, (B, Hkv, cap // block, d), K.device)
+    dims = make_dims(B, Hkv, Hkv, cap if seq_len is None else seq_len, cap, _dtype_code(K), d)
+    _check(lib().ffd_block_bounds(ctypes.byref(dims), _ptr(K), tok_begin, tok_end, block,
+                                  _ptr(kmin), _ptr(kmax), _stream(stream)))
+
+
+def block_scores(kind: int, q: torch.Tensor, K: torch.Tensor, block: int, seq_len: int,
+                 Kq: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                 kmin: torch.Tensor | None = None, kmax: torch.Tensor | None = None,
+                 out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Per-block scores [B, Hq, seq_len // block] fp32 of one kind (SCORE_*)."""
+    dims = dims_of(q, K, seq_len)
+    B, Hq, d = q.shape
+    _need(q, "q", K.dtype, None, K.device)
+    nf = seq_len // block
+    if out is None:
+        out = torch.empty((B, Hq, nf), dtype=torch.float32, device=q.device)
+    _need(out, "scores", torch.float32, (B, Hq, nf), q.device)
+    _check(lib().ffd_block_scores(ctypes.byref(dims), kind, _ptr(q), _ptr(K), _ptr(Kq),
+                                  _ptr(scales), _ptr(kmin), _ptr(kmax), block, _ptr(out),
+                                  _stream(stream)))
+    return out
+
+
+def select_blocks(rule: int, scores: torch.Tensor, param: float, block: int, seq_len: int,
+                  Hkv: int, pseudo_max: torch.Tensor | None = None,
+                  keep_mask: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One selection rule (SELECT_*) over scores [B, Hq, nf] -> keep_mask [B, Hq, n_blocks]."""
+    B, Hq, nf = scores.shape
+    _need(scores, "scores", torch.float32, None, scores.device)
+    n_blocks = math.ceil(seq_len / block)
+    if keep_mask is None:
+        keep_mask = torch.empty((B, Hq, n_blocks), dtype=torch.uint8, device=scores.device)
+    _need(keep_mask, "keep_mask", torch.uint8, (B, Hq, n_blocks), scores.device)
+    if pseudo_max is not None:
+        _need(pseudo_max, "pseudo_max", torch.float32, (B, Hq), scores.device)
+    cap = n_blocks * block
+    dims = make_dims(B, Hq, Hkv, seq_len, cap, FFD_BF16)
+    _check(lib().ffd_select_blocks(ctypes.byref(dims), rule, _ptr(scores), _ptr(pseudo_max),
+                                   float(param), block, _ptr(keep_mask), _stream(stream)))
+    return keep_mask
+
+
+def decode_masked(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, keep_mask: torch.Tensor,
+                  block: int, seq_len: int, out: torch.Tensor | None = None,
+                  lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                  want_lse: bool = True, stream=None):
+    """Exact attention over the blocks keep_mask [B, Hq, n_blocks] marks."""
+    dims = dims_of(q, K, seq_len)
+    _need(V, "V", K.dtype, K.shape, K.device)
+    _need(q, "q", K.dtype, None, K.device)
+    _need(keep_mask, "keep_mask", torch.uint8,
+          (q.shape[0], q.shape[1], math.ceil(seq_len / block)), q.device)
+    out, lse = _decode_outputs(q, out, lse, want_lse)
+    if workspace is None:
+        workspace = alloc_workspace(dims, block, q.device)
+    _need(workspace, "workspace", torch.uint8, None, q.device)
+    _check(lib().ffd_decode_masked(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V),
+                                   _ptr(keep_mask), block, _ptr(out), _ptr(lse), _ptr(workspace),
+                                   workspace.numel(), _stream(stream)))
     return out, lse

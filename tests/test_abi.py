@@ -203,3 +203,35 @@ def test_decode_loop_validation(L):
     assert dv(ctypes.byref(d), A, A, A, None, 64, A, A, A, 1 << 30, None) == \
         ffd.FFD_ERR_INVALID_ARG
     assert dv(ctypes.byref(d), A, A, A, lens, 64, A, A, A, 16, None) == ffd.FFD_ERR_WORKSPACE
+
+
+def test_comparator_validation(L):
+    """Block scores, selection rules and masked decode reject bad arguments before any launch."""
+    d = dims()
+    sc = L.ffd_block_scores
+    assert sc(ctypes.byref(d), 3, A, A, A, A, A, A, 64, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert sc(ctypes.byref(d), 0, A, A, None, A, None, None, 64, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert sc(ctypes.byref(d), 1, A, A, A, A, None, A, 64, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert sc(ctypes.byref(d), 2, A, None, None, None, None, None, 64, A, None) == \
+        ffd.FFD_ERR_INVALID_ARG
+    assert sc(ctypes.byref(d), 2, A, A, None, None, None, None, 64, None, None) == \
+        ffd.FFD_ERR_INVALID_ARG
+    sel = L.ffd_select_blocks
+    assert sel(ctypes.byref(d), 3, A, None, 1.0, 64, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert sel(ctypes.byref(d), 0, A, None, -1.0, 64, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert sel(ctypes.byref(d), 0, A, None, float("nan"), 64, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert sel(ctypes.byref(d), 1, A, None, -2.0, 64, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert sel(ctypes.byref(d), 2, A, None, 0.0, 64, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert sel(ctypes.byref(d), 2, A, None, 1.5, 64, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert sel(ctypes.byref(d), 1, None, None, 4.0, 64, A, None) == ffd.FFD_ERR_INVALID_ARG
+    big = dims(seq_len=16385 * 64, seq_cap=16385 * 64)
+    assert sel(ctypes.byref(big), 1, A, None, 4.0, 64, A, None) == ffd.FFD_ERR_UNSUPPORTED
+    assert sel(ctypes.byref(big), 2, A, None, 0.5, 64, A, None) == ffd.FFD_ERR_UNSUPPORTED
+    dm = L.ffd_decode_masked
+    assert dm(ctypes.byref(d), A, A, A, None, 64, A, A, A, 1 << 30, None) == \
+        ffd.FFD_ERR_INVALID_ARG
+    assert dm(ctypes.byref(d), A, A, A, A, 64, A, A, A, 16, None) == ffd.FFD_ERR_WORKSPACE
+    bb = L.ffd_block_bounds
+    assert bb(ctypes.byref(d), A, 0, 4096, 64, None, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert bb(ctypes.byref(d), A, 0, 4097, 64, A, A, None) == ffd.FFD_ERR_INVALID_ARG
+    assert bb(ctypes.byref(d), A, 0, 4096, 96, A, A, None) == ffd.FFD_ERR_UNSUPPORTED
