@@ -85,8 +85,114 @@ def bytes_dense(w) -> int:
 # ------------------------------------------------------------------------------------------
 # GPU measurement
 # ------------------------------------------------------------------------------------------
+def selection_leg(w, qd, Kd, Vd, Kq, sc, out_d, lse_d, delta: float, steps: int, timed) -> dict:
+    """Selection comparators and fidelity diagnostics on one workload:
+    - Table 3: the standalone top-delta, top-k and top-p rules over the scan scores, timed at a
+      matched keep ratio (k and p found by bisection);
+    - Fig. 6: recall (cosine to dense) and LSE error against the IO budget, for FFD's fused top-delta
+      at several delta and, at the same budget, top-k over a min/max (Quest-style) bound and over
+      the exact block maxima;
+    - Fig. 5: the gap m - mtilde between the largest exact block score and the pseudo-max, for
+      Alg. 1's scan estimates and for Eq. 3's exact scores."""
+    import torch
+
+    from long_context_decoding_amd import ffd
+
+    T, L = w.T, w.L
+    nf, nb = w.n_full, w.n_blocks
+    dev = qd.device
+    s_scan = ffd.block_scores(ffd.SCORE_SCAN, qd, Kd, T, L, Kq=Kq, scales=sc)
+    s_ex = ffd.block_scores(ffd.SCORE_EXACT, qd, Kd, T, L)
+    kmin, kmax = ffd.alloc_bounds(Kd, T)
+    ffd.block_bounds(Kd, 0, L, T, kmin, kmax, seq_len=L)
+    s_bnd = ffd.block_scores(ffd.SCORE_BOUNDS, qd, Kd, T, L, kmin=kmin, kmax=kmax)
+    keep = torch.empty((w.B, w.Hq, nb), dtype=torch.uint8, device=dev)
+
+    def ratio(rule, param, scores=s_scan):
+        ffd.select_blocks(rule, scores, param, T, L, w.Hkv, keep_mask=keep)
+        return float(keep.float().mean().item())
+
+    def match_k(target, scores):
+        lo, hi = 0, nf
+        while lo < hi:  # smallest k whose keep ratio reaches the target
+            mid = (lo + hi) // 2
+            if ratio(ffd.SELECT_TOP_K, mid, scores) >= target:
+                hi = mid
+            else:
+                lo = mid + 1
+        return lo
+
+    def match_p(target):
+        lo, hi = 1e-9, 1.0
+        for _ in range(40):
+            mid = 0.5 * (lo + hi)
+            if ratio(ffd.SELECT_TOP_P, mid) >= target:
+                hi = mid
+            else:
+                lo = mid
+        return hi
+
+    r_delta = ratio(ffd.SELECT_TOP_DELTA, delta)
+    k = match_k(r_delta, s_scan)
+    p = match_p(r_delta)
+    rules = {"top_delta": (ffd.SELECT_TOP_DELTA, delta), "top_k": (ffd.SELECT_TOP_K, k),
+             "top_p": (ffd.SELECT_TOP_P, p)}
+    heads = w.B * w.Hq
+    table3 = {}
+    for name, (rule, param) in rules.items():
+        kr = ratio(rule, param)
+        us = timed(lambda r, rule=rule, param=param: ffd.select_blocks(
+            rule, s_scan, param, T, L, w.Hkv, keep_mask=keep), steps, rotate=False)
+        table3[name] = {"param": param, "keep_ratio": kr, "us_per_launch": us,
+                        "us_per_head": us / heads}
+    score_us = {
+        "scan": timed(lambda r: ffd.block_scores(ffd.SCORE_SCAN, qd, Kd, T, L, Kq=Kq, scales=sc,
+                                                 out=s_scan), steps, rotate=False),
+        "bounds": timed(lambda r: ffd.block_scores(ffd.SCORE_BOUNDS, qd, Kd, T, L, kmin=kmin,
+                                                   kmax=kmax, out=s_bnd), steps, rotate=False),
+        "exact": timed(lambda r: ffd.block_scores(ffd.SCORE_EXACT, qd, Kd, T, L, out=s_ex),
+                       steps, rotate=False),
+    }
+
+    o_d = out_d.double().cpu().numpy()
+    l_d = lse_d.double().cpu().numpy()
+
+    def fidelity(o, lse):
+        o = o.double().cpu().numpy()
+        cos = (o * o_d).sum(-1) / (np.linalg.norm(o, axis=-1) * np.linalg.norm(o_d, axis=-1))
+        return {"recall_cos_mean": float(cos.mean()), "recall_cos_min": float(cos.min()),
+                "lse_err_max": float(np.abs(lse.double().cpu().numpy() - l_d).max())}
+
+    fig6 = []
+    for dl in (1.0, 2.0, 3.0, 5.0, 8.0):
+        kf = torch.zeros_like(keep)
+        o, l = ffd.decode_sparse(qd, Kd, Vd, Kq, sc, dl, T, L, keep_mask=kf)
+        budget = float(kf.float().mean().item())
+        row = {"delta": dl, "budget": budget, "ffd": fidelity(o, l)}
+        for name, scores in (("minmax_topk", s_bnd), ("exact_topk", s_ex)):
+            kk = match_k(budget, scores)
+            km = ffd.select_blocks(ffd.SELECT_TOP_K, scores, kk, T, L, w.Hkv)
+            o, l = ffd.decode_masked(qd, Kd, Vd, km, T, L)
+            row[name] = dict(fidelity(o, l), budget=float(km.float().mean().item()), k=kk)
+        fig6.append(row)
+
+    m = s_ex.max(dim=-1).values
+    gaps = {}
+    for name, src in (("alg1_scan_estimate", s_scan), ("eq3_exact", s_ex)):
+        mt = torch.maximum(src[..., 0], src[..., nf - 1])
+        g = (m - mt).double().cpu().numpy().ravel()
+        gaps[name] = {"mean": float(g.mean()), "max": float(g.max()), "min": float(g.min()),
+                      "frac_below_true_max": float((g > 0).mean()),
+                      "frac_above_true_max": float((g < 0).mean())}
+    torch.cuda.synchronize()
+    return {"table3_matched_keep": table3, "score_kernels_us": score_us, "fig6": fig6,
+            "fig5_pseudo_max_gap": gaps,
+            "note": "full blocks only; the exact maxima come from the bf16 MFMA in fp32"}
+
+
 def run_workload(w, delta: float, steps: int, warmup: int, min_rotation_mib: int = 1024,
-                 graphs: bool = True, residual_bits: int = 0, decode_loop: bool = False):
+                 graphs: bool = True, residual_bits: int = 0, decode_loop: bool = False,
+                 selection: bool = False):
     """Time one decode step of workload w on cuda:0.
 
     Steps run back to back over R copies of the KV cache (like R layers of a model, each with
@@ -202,6 +308,9 @@ def run_workload(w, delta: float, steps: int, warmup: int, min_rotation_mib: int
     us_s_warm = timed(sparse, steps, rotate=False)
     us_d_warm = timed(dense, steps, rotate=False)
 
+    sel = selection_leg(w, qd, Kd, Vd, Kq, sc, out_d, lse_d, delta, steps, timed) \
+        if selection else None
+
     loop = None
     if decode_loop and R >= 2:
         # Decode loop: one step appends the new token's key and value on the device (quantizing
@@ -307,6 +416,7 @@ def run_workload(w, delta: float, steps: int, warmup: int, min_rotation_mib: int
         "quantize_us": quant_us,
         "residual_form": res_form,
         "decode_loop": loop,
+        "selection": sel,
     }
     if not residual_bits:
         del reps
@@ -366,6 +476,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--residual-bits", type=int, default=2, choices=(0, 2, 4),
                     help="also time the residual storage form on the primary workload (0: no)")
+    ap.add_argument("--no-selection", action="store_true",
+                    help="skip the selection-comparator and fidelity leg")
     ap.add_argument("--no-loop", action="store_true",
                     help="skip the decode-loop leg (append + decode with device-side lengths)")
     ap.add_argument("--eager", action="store_true",
@@ -395,9 +507,13 @@ def main() -> int:
     t_wall = time.time()
     prim, host = run_workload(w, delta, args.steps, args.warmup, args.rotation_mib,
                               graphs=not args.eager, residual_bits=args.residual_bits,
-                              decode_loop=not args.no_loop)
+                              decode_loop=not args.no_loop, selection=not args.no_selection)
     log(f"{w.name}: sparse {prim['sparse_us']:.1f} us, dense {prim['dense_us']:.1f} us, "
         f"{prim['sparse_GBps']:.0f} GB/s, keep {prim['union_keep']:.4f}")
+    if prim["selection"]:
+        t3 = prim["selection"]["table3_matched_keep"]
+        log(f"{w.name} selection at matched keep: " + ", ".join(
+            f"{k} {v['us_per_launch']:.1f} us (keep {v['keep_ratio']:.4f})" for k, v in t3.items()))
     if prim["decode_loop"]:
         lp = prim["decode_loop"]
         log(f"{w.name} decode loop: {lp['us_per_token']:.1f} us/token "
