@@ -144,7 +144,10 @@ def test_masked_attention_and_fused_equivalence(dtype, G, T, L):
         o_f, l_f = ffd.decode_sparse(qd, Kd, Vd, Kq, sc, delta, T, L, keep_mask=keep_f)
         torch.cuda.synchronize()
         assert torch.equal(keep_sel, keep_f), "top-delta on the scan scores differs from fused"
-        assert torch.equal(o_m, o_f) and torch.equal(l_m, l_f), "masked decode differs from fused"
+        # same kept set; the fused kernel may visit the kept blocks in another order, so the
+        # two agree to rounding, not bit for bit
+        assert_close(o_m.cpu().numpy(), o_f.cpu().numpy(), TOL[dtype], "masked vs fused out")
+        assert_close(l_m.cpu().numpy(), l_f.cpu().numpy(), TOL[dtype], "masked vs fused lse")
     # an arbitrary mask (top-k on exact scores) against the oracle's attention over it
     s_ex = ffd.block_scores(ffd.SCORE_EXACT, qd, Kd, T, L)
     keep = ffd.select_blocks(ffd.SELECT_TOP_K, s_ex, max(1, nf // 4), T, L, w.Hkv)
