@@ -1504,21 +1504,51 @@ __device__ __forceinline__ float f_unord(u32 o)
 
 // One selection rule over a row of block scores (one work-group of 256 threads per (b, query
 // head)).  RULE 0 top-delta: theta = RN(mtilde - delta), mtilde the given pseudo-max or
-// max(s_0, s_{nf-1}); keep s_j >= theta.  RULE 1 top-k and RULE 2 top-p rank the row by a bitonic
-// sort in LDS of keys (~ord(s_j) << 32 | j) -- descending score, ties to the lower index --; top-k
-// keeps the first k, top-p the shortest prefix whose exp(s - s_max) mass reaches p of the total
-// (fp32 sums in a fixed order: 256 contiguous chunks, then their running sum).  Every rule keeps
-// block 0, the last full block and a partial tail.
+// max(s_0, s_{nf-1}); keep s_j >= theta.  RULE 1 top-k and RULE 2 top-p keep a prefix of the row
+// ranked by descending score, ties to the lower index: top-k the first k, top-p the shortest
+// prefix whose mass exp(s - s_max) reaches p of the row's total.  Neither needs the ranking
+// itself, only the prefix's last key: a radix select over the keys ~ord(s_j) (ascending key =
+// descending score) finds it in four 8-bit passes, each a histogram in LDS of the weights of the
+// keys that share the bits found so far -- weight 1 for top-k, the mass as an integer multiple of
+// 2^-40 for top-p (integer sums: exact and independent of the order of the atomics).  The prefix
+// is then every key below the last one plus, of the keys equal to it, the first ones in index
+// order.  Every rule keeps block 0, the last full block and a partial tail.
+constexpr float kMassScale = 1099511627776.0f;  // 2^40
+
+// ceil(t * p) for 0 < p <= 1, exactly: p = m 2^-sh with a 24-bit integer m, the 128-bit product
+// t m shifted right by sh, rounding up (integer arithmetic only)
+__device__ __forceinline__ unsigned long long ceil_mul(unsigned long long t, float p)
+{
+    const u32 bits = (u32)as_i(p);
+    const int e = (int)((bits >> 23) & 0xFFu);
+    const unsigned long long m = (bits & 0x7FFFFFu) | (e != 0 ? 0x800000u : 0u);
+    const int sh = 150 - (e != 0 ? e : 1);  // >= 23
+    const unsigned long long lo = t * m, hi = __umul64hi(t, m);
+    unsigned long long q, rem;
+    if (sh < 64) {
+        q = (lo >> sh) | (hi << (64 - sh));
+        rem = lo & ((1ull << sh) - 1ull);
+    } else if (sh < 128) {
+        q = hi >> (sh - 64);
+        rem = lo | (hi & ((1ull << (sh - 64)) - 1ull));
+    } else {
+        q = 0ull;
+        rem = lo | hi;
+    }
+    return q + (rem != 0ull ? 1ull : 0ull);
+}
+
 template <int RULE>
 __global__ __launch_bounds__(256) void select_kernel(SelectParams p)
 {
-    extern __shared__ unsigned long long keys[];  // n_pow2 keys, then n_blocks keep flags
-    __shared__ float csum[256];
-    __shared__ float cpre[256];
-    __shared__ float ctot;
-    __shared__ int first_hit;
+    extern __shared__ u32 keys[];  // n_full keys, then n_blocks keep flags
+    __shared__ unsigned long long hist[256];
+    __shared__ unsigned long long s_total, s_above;
+    __shared__ u32 s_min, s_prefix;
+    __shared__ int s_ties[4];
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
     const int nf = p.n_full, nb = p.n_blocks;
     const float* s = p.scores + (size_t)row * nf;
     uint8_t* keep = p.keep + (size_t)row * nb;
@@ -1536,66 +1566,131 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p)
         }
         return;
     }
-    uint8_t* flag = reinterpret_cast<uint8_t*>(keys + p.n_pow2);
-    const int N = p.n_pow2;
-    for (int i = tid; i < N; i += 256)
-        keys[i] = i < nf ? ((unsigned long long)(~f_ord(s[i])) << 32) | (u32)i : ~0ull;
-    for (int j = tid; j < nb; j += 256) flag[j] = forced(j) ? 1 : 0;
+    uint8_t* flag = reinterpret_cast<uint8_t*>(keys + nf);
+    if (tid == 0) {
+        s_min = 0xFFFFFFFFu;
+        s_total = 0ull;
+        s_above = 0ull;
+        s_prefix = 0u;
+    }
     __syncthreads();
-    for (int k = 2; k <= N; k <<= 1) {
-        for (int jj = k >> 1; jj > 0; jj >>= 1) {
-            for (int i = tid; i < N; i += 256) {
-                const int ixj = i ^ jj;
-                if (ixj > i) {
-                    const unsigned long long a = keys[i], c = keys[ixj];
-                    if ((a > c) == ((i & k) == 0)) {
-                        keys[i] = c;
-                        keys[ixj] = a;
+    u32 kmin = 0xFFFFFFFFu;
+    for (int i = tid; i < nf; i += 256) {
+        const u32 k = ~f_ord(s[i]);
+        keys[i] = k;
+        kmin = min(kmin, k);
+    }
+    for (int j = tid; j < nb; j += 256) flag[j] = forced(j) ? 1 : 0;
+    float smax = 0.0f;
+    if constexpr (RULE == 2) {
+        atomicMin(&s_min, kmin);
+        __syncthreads();
+        smax = f_unord(~s_min);
+    }
+    // weight of a key: 1, or its mass exp(s - s_max) in units of 2^-40 (truncated)
+    auto weight = [&](u32 k) -> unsigned long long {
+        if constexpr (RULE == 1) {
+            return 1ull;
+        } else {
+            const float x = f_unord(~k);
+            const float m = (x == smax) ? 1.0f
+                                        : __builtin_amdgcn_exp2f((x - smax) * 1.4426950408889634f);
+            return (unsigned long long)(m * kMassScale);
+        }
+    };
+    // target weight of the prefix; all = every full block is kept
+    unsigned long long target;
+    bool all = false, none = false;
+    if constexpr (RULE == 1) {
+        const float kk = p.param;
+        none = !(kk >= 1.0f);
+        all = kk >= (float)nf;
+        target = none || all ? 0ull : (unsigned long long)(u32)kk;
+    } else {
+        unsigned long long tot = 0ull;
+        for (int i = tid; i < nf; i += 256) tot += weight(keys[i]);
+        atomicAdd(&s_total, tot);
+        __syncthreads();
+        // the shortest prefix with mass >= p of the total: weight >= ceil(p total)
+        const float pp = p.param;
+        all = !(pp <= 1.0f);  // p above 1 (or NaN): every block
+        target = all ? 0ull : (pp > 0.0f ? ceil_mul(s_total, pp) : 1ull);
+        if (target == 0ull && !all) target = 1ull;  // p <= 0 or tiny: the top block
+    }
+    if (!none) {
+        if (all) {
+            for (int i = tid; i < nf; i += 256) flag[i] = 1;
+        } else {
+            // radix select: after the pass at bit sh, s_prefix holds the last key's bits from sh
+            // up and s_above the weight of every key below the keys with those bits
+            for (int sh = 24; sh >= 0; sh -= 8) {
+                hist[tid] = 0ull;
+                __syncthreads();
+                const u32 pre = s_prefix;
+                const u32 hi_mask = sh == 24 ? 0u : (0xFFFFFFFFu << (sh + 8));
+                for (int i = tid; i < nf; i += 256) {
+                    const u32 k = keys[i];
+                    if (((k ^ pre) & hi_mask) == 0u)
+                        atomicAdd(&hist[(k >> sh) & 255u], weight(k));
+                }
+                __syncthreads();
+                if (w == 0) {
+                    // lane l holds bins 4l .. 4l + 3; inclusive scan over the lanes
+                    unsigned long long b4[4], loc = 0ull;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        b4[u] = hist[4 * lane + u];
+                        loc += b4[u];
+                    }
+                    unsigned long long inc = loc;
+#pragma unroll
+                    for (int d = 1; d < 64; d <<= 1) {
+                        const unsigned long long o = __shfl_up(inc, d);
+                        if (lane >= d) inc += o;
+                    }
+                    const unsigned long long above = s_above;
+                    // first bin whose inclusive weight reaches the target
+                    const bool hit = above + inc >= target;
+                    const unsigned long long ball = __ballot(hit);
+                    const int L0 = (int)__builtin_ctzll(ball);  // exists: the range holds the target
+                    if (lane == L0) {
+                        unsigned long long run = above + inc - loc;  // weight below bin 4 L0
+                        int bin = 4 * L0;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            if (run + b4[u] >= target) break;
+                            run += b4[u];
+                            ++bin;
+                        }
+                        s_prefix = pre | ((u32)bin << sh);
+                        s_above = run;
                     }
                 }
+                __syncthreads();
             }
-            __syncthreads();
+            // keys below the last key v: kept; keys equal to v: the first c in index order
+            const u32 v = s_prefix;
+            const unsigned long long rest = target - s_above;
+            const unsigned long long wv = weight(v);
+            const int c = (int)((rest + wv - 1ull) / wv);
+            int taken = 0;  // ties already met in earlier chunks
+            for (int base = 0; base < nf; base += 256) {
+                const int i = base + tid;
+                const u32 k = i < nf ? keys[i] : 0xFFFFFFFFu;
+                if (k < v) flag[i] = 1;
+                const bool tie = i < nf && k == v;
+                const unsigned long long ball = __ballot(tie);
+                if (lane == 0) s_ties[w] = (int)__popcll(ball);
+                __syncthreads();
+                int before = taken;
+                for (int u = 0; u < w; ++u) before += s_ties[u];
+                const int rank = before + (int)__popcll(ball & ((1ull << lane) - 1ull));
+                if (tie && rank < c) flag[i] = 1;
+                taken += s_ties[0] + s_ties[1] + s_ties[2] + s_ties[3];
+                __syncthreads();
+            }
         }
     }
-    int n_sel;
-    if (RULE == 1) {
-        n_sel = min(max((int)p.param, 0), nf);
-    } else {
-        // mass of every ranked block relative to the top one, in fp32; chunk sums, their running
-        // sum, then the first position whose cumulative mass reaches p of the total
-        const float smax = f_unord(~(u32)(keys[0] >> 32));
-        const int per = (nf + 255) / 256;
-        const int c0 = tid * per, c1 = min(nf, c0 + per);
-        float run = 0.0f;
-        for (int i = c0; i < c1; ++i)
-            run += __builtin_amdgcn_exp2f((f_unord(~(u32)(keys[i] >> 32)) - smax) *
-                                          1.4426950408889634f);
-        csum[tid] = run;
-        if (tid == 0) first_hit = nf;
-        __syncthreads();
-        if (tid == 0) {
-            float acc = 0.0f;
-            for (int t = 0; t < 256; ++t) {
-                cpre[t] = acc;
-                acc += csum[t];
-            }
-            ctot = acc;
-        }
-        __syncthreads();
-        const float target = p.param * ctot;
-        run = cpre[tid];
-        for (int i = c0; i < c1; ++i) {
-            run += __builtin_amdgcn_exp2f((f_unord(~(u32)(keys[i] >> 32)) - smax) *
-                                          1.4426950408889634f);
-            if (run >= target) {
-                atomicMin(&first_hit, i);
-                break;
-            }
-        }
-        __syncthreads();
-        n_sel = min(first_hit + 1, nf);
-    }
-    for (int r = tid; r < n_sel; r += 256) flag[(u32)keys[r]] = 1;
     __syncthreads();
     for (int j = tid; j < nb; j += 256) keep[j] = flag[j];
 }
@@ -1732,7 +1827,7 @@ hipError_t launch_scores(const ScoreParams& p, int kind, bool bf16, hipStream_t 
 hipError_t launch_select(const SelectParams& p, int rule, hipStream_t stream)
 {
     if (p.rows <= 0) return hipSuccess;
-    const size_t dyn = rule == 0 ? 0 : (size_t)p.n_pow2 * 8 + (size_t)((p.n_blocks + 15) & ~15);
+    const size_t dyn = rule == 0 ? 0 : (size_t)p.n_full * 4 + (size_t)((p.n_blocks + 15) & ~15);
     if (rule == 0)
         hipLaunchKernelGGL(select_kernel<0>, dim3(p.rows), dim3(256), dyn, stream, p);
     else if (rule == 1)
