@@ -14,7 +14,12 @@ Readings (the pages name these rules but do not define them at block granularity
     pi_j = exp(s_j - max s) / sum_i exp(s_i - max s), and keeps the shortest ranked prefix whose
     mass reaches p (all full blocks when rounding keeps the total just below p);
   - top-delta is Eq. 1 with a pseudo-max: theta = RN32(mtilde - delta), keep s_j >= theta, with
-    mtilde = max(s_0, s_{nf-1}) (Alg. 1) or a given value (Eq. 3 with exact scores).
+    mtilde = max(s_0, s_{nf-1}) (Alg. 1) or a given value (Eq. 3 with exact scores);
+  - the running-max variant of top-delta (a threshold "from the local max", Sec. 1 Fig. 1, kept
+    local to a window of consecutive blocks): the blocks are cut into windows of W blocks; in each
+    window, in increasing block order, a non-forced full block j is kept iff
+    s_j >= RN32(M - delta), where M starts at the Alg. 1 pseudo-max and, after block j is judged,
+    becomes max(M, s_j).
 """
 from __future__ import annotations
 
@@ -118,4 +123,23 @@ def select_top_p(scores: np.ndarray, n_full: int, n_blocks: int, p: float) -> np
     n, order, _ = top_p_prefix(np.asarray(scores)[:n_full], p)
     for j in order[:n]:
         keep[j] = 1
+    return keep
+
+
+def select_running(scores: np.ndarray, mtilde: float, n_full: int, n_blocks: int, delta: float,
+                   window: int) -> np.ndarray:
+    """Top-delta against a running maximum local to each window of `window` blocks (the module
+    docstring's reading), decided in fp32 -> keep u8[n_blocks]."""
+    s = np.asarray(scores, dtype=np.float32)
+    forced = forced_mask(n_full, n_blocks)
+    keep = forced.copy()
+    dl = np.float32(delta)
+    for w0 in range(0, n_blocks, window):
+        M = np.float32(mtilde)
+        for j in range(w0, min(w0 + window, n_blocks)):
+            if forced[j]:  # kept, and its score does not enter the running maximum
+                continue
+            if s[j] >= np.float32(M - dl):  # one fp32 subtraction, round to nearest
+                keep[j] = 1
+            M = max(M, s[j])
     return keep

@@ -143,3 +143,52 @@ def test_eq3_pseudo_max_never_exceeds_the_true_max():
         assert mtilde <= e.max()
         if trial % 2:
             assert mtilde == e.max()
+
+
+def test_running_max_hand_example():
+    # mtilde 3, delta 1; blocks 0 and 5 forced.  One window of 6: block 1 (2.5 >= 2) kept, block 2
+    # (5 >= 2) kept and raises the maximum to 5, so blocks 3 (3.5) and 4 (3.9) fall below 4.
+    # Windows of 2 restart the maximum at 3 for blocks 2-3 and 4-5: block 4 is kept again.
+    s = np.array([9.0, 2.5, 5.0, 3.5, 3.9, 0.0], np.float32)
+    assert S.select_running(s, 3.0, 6, 6, 1.0, 6).tolist() == [1, 1, 1, 0, 0, 1]
+    assert S.select_running(s, 3.0, 6, 6, 1.0, 2).tolist() == [1, 1, 1, 0, 1, 1]
+    assert S.select_running(s, 3.0, 6, 6, 1.0, 1).tolist() == [1] * 6
+    assert S.select_running(s, 3.0, 6, 7, 1.0, 6).tolist() == [1, 1, 1, 0, 0, 1, 1]  # tail
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_running_max_invariants(seed):
+    rng = np.random.default_rng(100 + seed)
+    nf = 37
+    nb = nf + (seed % 2)
+    s = (rng.standard_normal(nf) * 2).astype(np.float32)
+    mt = float(np.float32(max(s[0], s[nf - 1])))
+    forced = S.forced_mask(nf, nb).astype(bool)
+    for delta in (0.0, 0.7, 2.0, 5.0):
+        alg1 = S.select_top_delta(s, nf, nb, delta, pseudo_max=mt)[0].astype(bool)
+        prev = None
+        for W in (1, 2, 4, 8, 16, 64):
+            run = S.select_running(s, mt, nf, nb, delta, W).astype(bool)
+            # a window of one block never raises the maximum: Alg. 1 itself
+            if W == 1:
+                assert (run == alg1).all()
+            # the running maximum is at least mtilde: never more blocks than Alg. 1
+            assert not (run & ~alg1).any()
+            assert run[forced].all()
+            # nested windows (W divides 2W): the longer window's maximum is never lower
+            if prev is not None:
+                assert not (run & ~prev).any()
+            prev = run
+            # the definition written out per block: the maximum over the window's earlier
+            # non-forced blocks and mtilde
+            for j in range(nf):
+                if forced[j]:
+                    continue
+                w0 = (j // W) * W
+                M = max([np.float32(mt)] + [s[i] for i in range(w0, j) if not forced[i]])
+                assert run[j] == (s[j] >= np.float32(np.float32(M) - np.float32(delta))), (W, j)
+    assert S.select_running(s, mt, nf, nb, float("inf"), 8).all()
+    # every score below mtilde: the maximum never moves, Alg. 1 again at any window
+    low = np.minimum(s, np.float32(mt) - np.float32(0.01)).astype(np.float32)
+    np.testing.assert_array_equal(S.select_running(low, mt, nf, nb, 1.0, 64),
+                                  S.select_top_delta(low, nf, nb, 1.0, pseudo_max=mt)[0])
