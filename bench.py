@@ -176,6 +176,31 @@ def selection_leg(w, qd, Kd, Vd, Kq, sc, out_d, lse_d, delta: float, steps: int,
             row[name] = dict(fidelity(o, l), budget=float(km.float().mean().item()), k=kk)
         fig6.append(row)
 
+    # the running-max variant of top-delta at the same delta, per window of blocks: keep ratio,
+    # fidelity and warm-cache time, beside the fused Alg. 1 step's
+    o_buf = torch.empty_like(out_d)
+    l_buf = torch.empty_like(lse_d)
+    kf = torch.zeros_like(keep)
+    ws_a = ffd.alloc_workspace(ffd.dims_of(qd, Kd, L), T, dev)
+    o, l = ffd.decode_sparse(qd, Kd, Vd, Kq, sc, delta, T, L, keep_mask=kf, workspace=ws_a)
+    running = {"alg1": dict(fidelity(o, l), keep_ratio=float(kf.float().mean().item()),
+                            us_warm_cache=timed(lambda r: ffd.decode_sparse(
+                                qd, Kd, Vd, Kq, sc, delta, T, L, out=o_buf, lse=l_buf,
+                                workspace=ws_a), steps, rotate=False)),
+               "windows": []}
+    for window in (4, 16, 64, 256):
+        if math.ceil(nb / window) > 256:
+            continue
+        ws_r = ffd.alloc_workspace_window(ffd.dims_of(qd, Kd, L), T, window, dev)
+        kr = torch.zeros_like(keep)
+        o, l = ffd.decode_sparse_running(qd, Kd, Vd, Kq, sc, delta, T, window, L, keep_mask=kr,
+                                         workspace=ws_r)
+        row = dict(fidelity(o, l), window=window, keep_ratio=float(kr.float().mean().item()))
+        row["us_warm_cache"] = timed(lambda r, window=window, ws_r=ws_r: ffd.decode_sparse_running(
+            qd, Kd, Vd, Kq, sc, delta, T, window, L, out=o_buf, lse=l_buf, workspace=ws_r),
+            steps, rotate=False)
+        running["windows"].append(row)
+
     m = s_ex.max(dim=-1).values
     gaps = {}
     for name, src in (("alg1_scan_estimate", s_scan), ("eq3_exact", s_ex)):
@@ -186,6 +211,7 @@ def selection_leg(w, qd, Kd, Vd, Kq, sc, out_d, lse_d, delta: float, steps: int,
                       "frac_above_true_max": float((g < 0).mean())}
     torch.cuda.synchronize()
     return {"table3_matched_keep": table3, "score_kernels_us": score_us, "fig6": fig6,
+            "running_max": running,
             "fig5_pseudo_max_gap": gaps,
             "note": "full blocks only; the exact maxima come from the bf16 MFMA in fp32"}
 
@@ -514,6 +540,11 @@ def main() -> int:
         t3 = prim["selection"]["table3_matched_keep"]
         log(f"{w.name} selection at matched keep: " + ", ".join(
             f"{k} {v['us_per_launch']:.1f} us (keep {v['keep_ratio']:.4f})" for k, v in t3.items()))
+        rm = prim["selection"]["running_max"]
+        log(f"{w.name} running max (delta {prim['delta']}): Alg. 1 keep {rm['alg1']['keep_ratio']:.4f} "
+            f"{rm['alg1']['us_warm_cache']:.1f} us; " + ", ".join(
+                f"W={r['window']} keep {r['keep_ratio']:.4f} cos {r['recall_cos_min']:.4f} "
+                f"{r['us_warm_cache']:.1f} us" for r in rm["windows"]))
     if prim["decode_loop"]:
         lp = prim["decode_loop"]
         log(f"{w.name} decode loop: {lp['us_per_token']:.1f} us/token "

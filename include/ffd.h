@@ -238,7 +238,8 @@ ffd_status ffd_block_scores(const ffd_dims* dims, int32_t kind, const void* q, c
  * blocks are ranked by score, ties going to the lower index.  param: delta (>= 0 or +inf) for
  * top-delta, k (>= 0) for top-k, p in (0, 1] for top-p; pseudo_max [B, Hq] (optional, top-delta
  * only) replaces Alg. 1's max(s_0, s_{nf-1}), e.g. by the exact-score maximum of Eq. 3.  Top-k and
- * top-p sort each row in LDS: nf <= 16384 (else FFD_ERR_UNSUPPORTED).  Top-p sums in fp32. */
+ * top-p hold each row in LDS: nf <= 16384 (else FFD_ERR_UNSUPPORTED).  Top-p evaluates each mass
+ * in fp32 and sums them exactly as integer multiples of 2^-40. */
 ffd_status ffd_select_blocks(const ffd_dims* dims, int32_t rule, const float* scores,
                              const float* pseudo_max, float param, int32_t block,
                              uint8_t* keep_mask, hipStream_t stream);
@@ -249,6 +250,26 @@ ffd_status ffd_select_blocks(const ffd_dims* dims, int32_t rule, const float* sc
 ffd_status ffd_decode_masked(const ffd_dims* dims, const void* q, const void* K, const void* V,
                              const uint8_t* keep_mask, int32_t block, float* out, float* lse,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Running-max variant of the sparse step (Sec. 1 Fig. 1: a threshold relative to the local max,
+ * with no global sort or synchronisation; Alg. 1's pseudo-max as the starting point).  The
+ * sequence is cut into windows of `window` blocks, each one split (work-group) of the step; in
+ * each window, per query head and in increasing block order, a full block that is not forced is
+ * kept iff its scan estimate is >= RN(M - delta), where M is the maximum of Alg. 1's pseudo-max
+ * and the estimates of the window's earlier non-forced full blocks.  Forced blocks (0, the last
+ * full block, a partial tail) are kept.  So the kept set is a subset of ffd_decode_sparse's at the
+ * same delta, equal to it for window = 1.  Arguments as ffd_decode_sparse, plus
+ *   window     blocks per window, 1 <= window <= 256, with ceil(seq_len / block / window) <= 256
+ *              (else FFD_ERR_UNSUPPORTED)
+ *   workspace  at least ffd_workspace_bytes_window(dims, block, window) bytes. */
+ffd_status ffd_decode_sparse_running(const ffd_dims* dims, const void* q, const void* K,
+                                     const void* V, const uint8_t* Kq, const float* scales,
+                                     float delta, int32_t block, int32_t window, float* out,
+                                     float* lse, uint8_t* keep_mask, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of ffd_decode_sparse_running for this window; 0 for invalid arguments. */
+size_t ffd_workspace_bytes_window(const ffd_dims* dims, int32_t block, int32_t window);
 
 /* Workspace bytes needed by ffd_decode_sparse / ffd_decode_dense for these dims and block
  * (the maximum of the two); 0 for invalid dims.  The size depends on the split count, which the

@@ -91,7 +91,7 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
                          size_t workspace_bytes, hipStream_t stream, bool sparse,
                          const int8_t* Kr = nullptr, const float* res_scales = nullptr,
                          int bits = 0, const int32_t* seq_lens = nullptr,
-                         const uint8_t* ext_mask = nullptr)
+                         const uint8_t* ext_mask = nullptr, int window = 0)
 {
     const bool res = bits != 0;
     ffd_status st = check_dims(dims, block);
@@ -111,7 +111,12 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
     }
     if (res && (!Kr || !res_scales || !aligned16(Kr) || !aligned16(res_scales)))
         return FFD_ERR_INVALID_ARG;
-    const int S = splits_for(dims, block);
+    // the running-max variant splits the sequence into the caller's windows
+    const int n_blk = (dims->seq_len + block - 1) / block;
+    if (window != 0 && (window < 1 || window > kMaxBlocksPerSplit ||
+                        (n_blk + window - 1) / window > kMaxSplits))
+        return FFD_ERR_UNSUPPORTED;
+    const int S = window != 0 ? (n_blk + window - 1) / window : splits_for(dims, block);
     const WsLayout lay = ws_layout(dims, S);
     if (!workspace || !aligned16(workspace)) return FFD_ERR_WORKSPACE;
     if (workspace_bytes < lay.total) return FFD_ERR_WORKSPACE;
@@ -141,7 +146,8 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
     p.n_full = dims->seq_len / block;
     p.n_blocks = (dims->seq_len + block - 1) / block;
     p.S = S;
-    p.R = (p.n_blocks + S - 1) / S;
+    p.R = window != 0 ? window : (p.n_blocks + S - 1) / S;
+    p.running = window != 0 ? 1 : 0;
     p.seq_lens = seq_lens;
     p.mask_stride = p.n_blocks;
     p.ext_mask = ext_mask;
@@ -302,6 +308,27 @@ ffd_status ffd_decode_sparse_varlen(const ffd_dims* dims, const void* q, const v
     if (!seq_lens) return FFD_ERR_INVALID_ARG;
     return decode_common(dims, q, K, V, Kq, scales, delta, block, out, lse, keep_mask, workspace,
                          workspace_bytes, stream, true, nullptr, nullptr, 0, seq_lens);
+}
+
+ffd_status ffd_decode_sparse_running(const ffd_dims* dims, const void* q, const void* K,
+                                     const void* V, const uint8_t* Kq, const float* scales,
+                                     float delta, int32_t block, int32_t window, float* out,
+                                     float* lse, uint8_t* keep_mask, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream)
+{
+    if (window < 1) return FFD_ERR_UNSUPPORTED;
+    return decode_common(dims, q, K, V, Kq, scales, delta, block, out, lse, keep_mask, workspace,
+                         workspace_bytes, stream, true, nullptr, nullptr, 0, nullptr, nullptr,
+                         window);
+}
+
+size_t ffd_workspace_bytes_window(const ffd_dims* dims, int32_t block, int32_t window)
+{
+    if (check_dims(dims, block) != FFD_OK || window < 1 || window > kMaxBlocksPerSplit) return 0;
+    const int n_blk = (dims->seq_len + block - 1) / block;
+    const int S = (n_blk + window - 1) / window;
+    if (S > kMaxSplits) return 0;
+    return ws_layout(dims, S).total;
 }
 
 ffd_status ffd_decode_dense_varlen(const ffd_dims* dims, const void* q, const void* K,

@@ -43,6 +43,8 @@ struct DecodeParams {
     int mask_stride;          // keep_mask row length in blocks
     const uint8_t* ext_mask;  // optional [B][Hq][mask_stride] selection made by the caller: the
                               // sparse kernel then attends over these blocks and scans nothing
+    int running;              // sparse: top-delta against the running maximum of each split (the
+                              // splits are then the caller's windows of R blocks)
 };
 
 struct QuantParams {

@@ -609,6 +609,11 @@ struct __attribute__((aligned(16))) DecodeShared {
             float M[G], Lsum[G];
             int cnt[G];
         } fin;
+        struct {                                            // running-max selection
+            float s[kMaxBlocksPerSplit][G];                 // scan estimates of the split's blocks
+            float mt[G];                                    // Alg. 1 pseudo-max of each head
+            u32 bits[kMaxBlocksPerSplit];                   // heads that keep each block
+        } run;
     } u;
     float4 q[G * D / 4];                   // the group's query rows (bf16 or fp32 bytes)
     uint8_t kbits[kMaxBlocksPerSplit];     // per-block head mask (bit h = query head h of group)
@@ -754,7 +759,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
                         if (p.keep_mask)
     #pragma unroll
                             for (int h = 0; h < G; ++h) p.keep_mask[(size_t)(h0 + h) * p.mask_stride + j] = 1;
+                    } else if (p.running) {
+                        sh.kbits[t] = 0;  // decided after the scan
                     }
+                    if (p.running) sh.u.run.bits[t] = 0u;
                 }
             }
             // Scan items of this wave: the sink and local blocks (each wave forms the pseudo-max of
@@ -782,6 +790,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
                         pro0 = shat;
                     } else if (k == 1) {
                         theta = __fsub_rn(fmaxf(pro0, shat), p.delta);
+                        if (p.running && w == 0 && lane < G) sh.u.run.mt[lane] = fmaxf(pro0, shat);
+                    } else if (p.running) {
+                        // running-max variant: the estimate is kept for the decision after the
+                        // scan, which needs every earlier block of the split
+                        if (lane < G) sh.u.run.s[block_of(k) - jb][lane] = shat;
                     } else {
                         // selection, Eq. 1 with the pseudo-max: shat >= mtilde - delta
                         const int j = block_of(k);
@@ -836,6 +849,40 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
             publish_q();
         }
         __syncthreads();  // kbits complete, query rows in LDS
+
+        if (p.running && !p.ext_mask) {
+            // Running-max variant of Eq. 1: per head, the split's scanned blocks in increasing
+            // order; block j is kept iff shat_j >= RN(M - delta), M the maximum of mtilde and the
+            // estimates of the split's earlier scanned blocks.  One wave per head, 64 blocks at a
+            // time: an exclusive prefix maximum over the lanes plus the earlier chunks' maximum.
+            const int nf = nf_b;
+            for (int h = w; h < G; h += kWaves) {
+                float carry = sh.u.run.mt[h];
+                for (int base = 0; base < je - jb; base += 64) {
+                    const int t = base + lane;
+                    const int j = jb + t;
+                    const bool scanned = t < je - jb && j >= 1 && j < nf - 1;
+                    const float sv = scanned ? sh.u.run.s[t][h] : kNegInf;
+                    float inc = sv;
+#pragma unroll
+                    for (int d = 1; d < 64; d <<= 1) {
+                        const float o = __shfl_up(inc, d);
+                        if (lane >= d) inc = fmaxf(inc, o);
+                    }
+                    float before = __shfl_up(inc, 1);
+                    if (lane == 0) before = kNegInf;
+                    const bool keep = scanned && sv >= __fsub_rn(fmaxf(carry, before), p.delta);
+                    if (keep) atomicOr(&sh.u.run.bits[t], 1u << h);
+                    if (scanned && p.keep_mask)
+                        p.keep_mask[(size_t)(h0 + h) * p.mask_stride + j] = keep ? 1 : 0;
+                    carry = fmaxf(carry, __shfl(inc, 63));
+                }
+            }
+            __syncthreads();
+            for (int t = threadIdx.x; t < je - jb; t += kWaves * 64)
+                sh.kbits[t] |= (uint8_t)sh.u.run.bits[t];
+            __syncthreads();
+        }
 
         // every wave compacts the kept blocks of the split, in increasing order, into its own
         // list (identical in all waves)

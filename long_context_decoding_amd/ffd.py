@@ -83,6 +83,11 @@ def lib():
         L.ffd_select_blocks.restype = i32
         L.ffd_decode_masked.argtypes = [D, P, P, P, P, i32, P, P, P, sz, P]
         L.ffd_decode_masked.restype = i32
+        L.ffd_decode_sparse_running.argtypes = [D, P, P, P, P, P, f32, i32, i32, P, P, P, P, sz,
+                                                P]
+        L.ffd_decode_sparse_running.restype = i32
+        L.ffd_workspace_bytes_window.argtypes = [D, i32, i32]
+        L.ffd_workspace_bytes_window.restype = sz
         _lib = L
     return _lib
 
@@ -171,6 +176,18 @@ def alloc_workspace(dims: Dims, block: int, device) -> torch.Tensor:
     return ws
 
 
+def alloc_workspace_window(dims: Dims, block: int, window: int, device) -> torch.Tensor:
+    """A prepared workspace for decode_sparse_running with this window (also large enough for
+    the other decode calls with these dims)."""
+    n = lib().ffd_workspace_bytes_window(ctypes.byref(dims), block, window)
+    if n == 0:
+        raise FFDError(FFD_ERR_UNSUPPORTED, "invalid dims or window for workspace")
+    n = max(n, workspace_bytes(dims, block))
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    workspace_init(dims, block, ws)
+    return ws
+
+
 def alloc_kq(K: torch.Tensor, block: int):
     """Zero-filled Kq [B, Hkv, seq_cap, d/2] u8 and scales [B, Hkv, seq_cap/block, d] fp32."""
     B, Hkv, cap, d = K.shape
@@ -230,6 +247,36 @@ def decode_sparse(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, Kq: torch.T
                                    _ptr(scales), float(delta), block, _ptr(out), _ptr(lse),
                                    _ptr(keep_mask), _ptr(workspace), workspace.numel(),
                                    _stream(stream)))
+    return out, lse
+
+
+def decode_sparse_running(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, Kq: torch.Tensor,
+                          scales: torch.Tensor, delta: float, block: int, window: int,
+                          seq_len: int, out: torch.Tensor | None = None,
+                          lse: torch.Tensor | None = None, keep_mask: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None, want_lse: bool = True,
+                          stream=None):
+    """Sparse step with top-delta against the running maximum of each window of `window`
+    blocks.  Returns (out, lse) as decode_sparse."""
+    dims = dims_of(q, K, seq_len)
+    for name, t in (("q", q), ("K", K), ("V", V)):
+        _need(t, name, K.dtype, None, K.device)
+    _need(V, "V", K.dtype, K.shape, K.device)
+    B, Hkv, cap, d = K.shape
+    _need(Kq, "Kq", torch.uint8, (B, Hkv, cap, d // 2), K.device)
+    _need(scales, "scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d),
+          K.device)
+    out, lse = _decode_outputs(q, out, lse, want_lse)
+    if keep_mask is not None:
+        _need(keep_mask, "keep_mask", torch.uint8,
+              (q.shape[0], q.shape[1], math.ceil(seq_len / block)), q.device)
+    if workspace is None:
+        workspace = alloc_workspace_window(dims, block, window, q.device)
+    _need(workspace, "workspace", torch.uint8, None, q.device)
+    _check(lib().ffd_decode_sparse_running(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V),
+                                           _ptr(Kq), _ptr(scales), float(delta), block,
+                                           int(window), _ptr(out), _ptr(lse), _ptr(keep_mask),
+                                           _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse
 
 

@@ -235,3 +235,28 @@ def test_comparator_validation(L):
     assert bb(ctypes.byref(d), A, 0, 4096, 64, None, A, None) == ffd.FFD_ERR_INVALID_ARG
     assert bb(ctypes.byref(d), A, 0, 4097, 64, A, A, None) == ffd.FFD_ERR_INVALID_ARG
     assert bb(ctypes.byref(d), A, 0, 4096, 96, A, A, None) == ffd.FFD_ERR_UNSUPPORTED
+
+
+def test_running_validation(L):
+    """The running-max step rejects bad windows and small workspaces before any launch."""
+    d = dims()  # 4096 tokens: 64 blocks of 64
+    run = L.ffd_decode_sparse_running
+    for window in (0, -3, 257):
+        assert run(ctypes.byref(d), A, A, A, A, A, 5.0, 64, window, A, A, None, A, 1 << 30,
+                   None) == ffd.FFD_ERR_UNSUPPORTED
+        assert L.ffd_workspace_bytes_window(ctypes.byref(d), 64, window) == 0
+    assert run(ctypes.byref(d), A, A, A, A, A, float("nan"), 64, 8, A, A, None, A, 1 << 30,
+               None) == ffd.FFD_ERR_INVALID_ARG
+    assert run(ctypes.byref(d), A, A, A, None, A, 5.0, 64, 8, A, A, None, A, 1 << 30,
+               None) == ffd.FFD_ERR_INVALID_ARG
+    need = L.ffd_workspace_bytes_window(ctypes.byref(d), 64, 8)
+    assert need > 0
+    # fewer, longer windows need no more workspace than more, shorter ones
+    assert L.ffd_workspace_bytes_window(ctypes.byref(d), 64, 64) <= need
+    assert run(ctypes.byref(d), A, A, A, A, A, 5.0, 64, 8, A, A, None, A, need - 16,
+               None) == ffd.FFD_ERR_WORKSPACE
+    # more than 256 windows
+    big = dims(seq_len=257 * 64, seq_cap=257 * 64)
+    assert run(ctypes.byref(big), A, A, A, A, A, 5.0, 64, 1, A, A, None, A, 1 << 30,
+               None) == ffd.FFD_ERR_UNSUPPORTED
+    assert L.ffd_workspace_bytes_window(ctypes.byref(big), 64, 1) == 0
