@@ -489,6 +489,57 @@ def traffic_entry(bytes_alg: int):
     return rec.get("hbm_bytes_per_launch")
 
 
+def running_leg(names=("h1_4k_f32_needles", "gqa4_32k_sink_needles")) -> dict:
+    """Keep ratio and fidelity (cosine to the dense output, LSE error) of the running-max variant
+    against Alg. 1's fixed pseudo-max, on workloads without (4K, one head) and with (32K) a planted
+    sink block.  Not timed: these steps are a few microseconds."""
+    import torch
+
+    from long_context_decoding_amd import ffd
+    from long_context_decoding_amd import workloads as W
+
+    res = {}
+    for name in names:
+        w = W.WORKLOADS[name]
+        q, K, V, _ = W.make_inputs(w)
+
+        def up(a):
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+            return torch.from_numpy(a).to("cuda")
+
+        qd, Kd, Vd = up(q), up(K), up(V)
+        Kq, sc = ffd.alloc_kq(Kd, w.T)
+        ffd.quantize_k_append(Kd, 0, w.L, w.T, Kq, sc, seq_len=w.L)
+        o_d, l_d = ffd.decode_dense(qd, Kd, Vd, w.T, w.L)
+        o_d = o_d.double().cpu().numpy()
+        l_d = l_d.double().cpu().numpy()
+
+        def fid(o, lse, keep):
+            o = o.double().cpu().numpy()
+            cos = (o * o_d).sum(-1) / (np.linalg.norm(o, axis=-1) * np.linalg.norm(o_d, axis=-1))
+            return {"keep_ratio": float(keep.float().mean().item()),
+                    "recall_cos_min": float(cos.min()),
+                    "lse_err_max": float(np.abs(lse.double().cpu().numpy() - l_d).max())}
+
+        rows = []
+        for delta in sorted(set((2.0, 5.0) + tuple(w.deltas))):
+            keep = torch.zeros((w.B, w.Hq, w.n_blocks), dtype=torch.uint8, device="cuda")
+            o, l = ffd.decode_sparse(qd, Kd, Vd, Kq, sc, delta, w.T, w.L, keep_mask=keep)
+            row = {"delta": delta, "alg1": fid(o, l, keep), "running": []}
+            for window in (4, 16, 64):
+                if math.ceil(w.n_blocks / window) > 256:
+                    continue
+                keep = torch.zeros_like(keep)
+                o, l = ffd.decode_sparse_running(qd, Kd, Vd, Kq, sc, delta, w.T, window, w.L,
+                                                 keep_mask=keep)
+                row["running"].append(dict(fid(o, l, keep), window=window))
+            rows.append(row)
+        res[name] = rows
+    torch.cuda.synchronize()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -553,6 +604,15 @@ def main() -> int:
         rf = prim["residual_form"]
         log(f"{w.name} residual form: sparse {rf['sparse_us']:.1f} us, {rf['GBps']:.0f} GB/s, "
             f"{rf['speedup_vs_dense_bf16']:.2f}x vs dense")
+    run_small = None
+    if not args.no_selection:
+        run_small = running_leg()
+        for name, rows in run_small.items():
+            for r in rows:
+                log(f"{name} delta {r['delta']}: Alg. 1 keep {r['alg1']['keep_ratio']:.4f} "
+                    f"cos {r['alg1']['recall_cos_min']:.5f}; running " + ", ".join(
+                        f"W={x['window']} keep {x['keep_ratio']:.4f} cos {x['recall_cos_min']:.5f}"
+                        for x in r["running"]))
     sec = None
     if args.secondary and not args.no_secondary and args.secondary != args.workload:
         w2 = W.WORKLOADS[args.secondary]
@@ -601,6 +661,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "primary": prim,
         "secondary": sec,
+        "running_max_small": run_small,
         "pages_context": {
             "kernel_speedup_peak": "11.6x over FlashAttention-2 (RTX 4090, 2-bit scan + 8-bit "
                                    "residual, real Llama-3.1 traces)",
