@@ -464,7 +464,7 @@ def cpu_baseline(w, delta: float, host, budget_s: float = 12.0) -> dict:
     quant_s = time.time() - t0
     times = []
     t_start = time.time()
-    while len(times) < 3 or (time.time() - t_start < budget_s and len(times) < 100):
+    while len(times) < 3 or (time.time() - t_start < budget_s and len(times) < 1000):
         t0 = time.perf_counter()
         oracle.decode(q, K, V, w.L, w.T, delta=delta, Kq=Kq, scales=sc, n_threads=nthreads)
         times.append(time.perf_counter() - t0)
@@ -543,8 +543,8 @@ def running_leg(names=("h1_4k_f32_needles", "gqa4_32k_sink_needles")) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=PRIMARY)
     ap.add_argument("--delta", type=float, default=None)
     ap.add_argument("--secondary", default=SECONDARY,
