@@ -39,6 +39,7 @@ namespace {
 
 constexpr int D = kHeadDim;
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kResWaves = 8;  // decode waves per work-group in the residual storage form
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -594,14 +595,14 @@ __device__ __forceinline__ void tile_compute_res(const TileRes& r, const v8bf* q
 // ------------------------------------------------------------------------------------------
 // Decode kernel (sparse and dense)
 // ------------------------------------------------------------------------------------------
-template <int G>
+template <int G, int NW>
 struct __attribute__((aligned(16))) DecodeShared {
-    WaveScratch<G> wave[kWaves];
+    WaveScratch<G> wave[NW];
     union {
         struct {                                            // the waves' softmax states
-            float o[kWaves][G][D];
-            float m[kWaves][G];
-            float l[kWaves][G];
+            float o[NW][G][D];
+            float m[NW][G];
+            float l[NW][G];
         } merge;
         struct {                                            // final merge of the splits
             float wgt[G][kMaxSplits];                       // weight of each non-empty split
@@ -617,7 +618,7 @@ struct __attribute__((aligned(16))) DecodeShared {
     } u;
     float4 q[G * D / 4];                   // the group's query rows (bf16 or fp32 bytes)
     uint8_t kbits[kMaxBlocksPerSplit];     // per-block head mask (bit h = query head h of group)
-    uint8_t list[kWaves][kMaxBlocksPerSplit];  // kept blocks (offsets in the split), per wave
+    uint8_t list[NW][kMaxBlocksPerSplit];  // kept blocks (offsets in the split), per wave
     int is_last;
     u32 mask;                              // non-empty splits (when S <= 32)
 };
@@ -675,9 +676,11 @@ __device__ __forceinline__ float2 ld_dev2(const float2* p)
 // BITS is the width of the scanned codes; RES selects the residual storage form (thumbnail +
 // 8-bit residual instead of stored keys; bf16 values; sparse only).
 template <int T, int G, bool BF16, bool SPARSE, int BITS, bool RES>
-__global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
+__global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_kernel(DecodeParams p)
 {
-    __shared__ DecodeShared<G> sh;
+    // waves per work-group: eight in the residual form, whose exact tiles cost more arithmetic
+    constexpr int NW = RES ? kResWaves : kWaves;
+    __shared__ DecodeShared<G, NW> sh;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int col = lane & 15, kg = lane >> 4;
@@ -714,7 +717,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
     // loads are in flight; the load is unconditional (clamped index) so that it is issued
     // before them and the copy waits only for itself
     constexpr int kQ16 = (int)(G * D * (BF16 ? 2 : 4) / 16);
-    static_assert(kQ16 <= kWaves * 64, "query rows exceed one 16-byte load per thread");
+    static_assert(kQ16 <= NW * 64, "query rows exceed one 16-byte load per thread");
     const float4 qcopy = reinterpret_cast<const float4*>(
         static_cast<const char*>(p.q) + (size_t)h0 * D * esz)[min((int)threadIdx.x, kQ16 - 1)];
     auto publish_q = [&]() {
@@ -767,15 +770,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
             }
             // Scan items of this wave: the sink and local blocks (each wave forms the pseudo-max of
             // Eq. 3 itself, so that it can apply Eq. 1 to its own blocks at once), then the split's
-            // non-forced full blocks j_lo + w, j_lo + w + kWaves, ...
+            // non-forced full blocks j_lo + w, j_lo + w + NW, ...
             const int n_pro = nf >= 1 ? 2 : 0;
             const int j_lo = max(jb, 1);
             const int j_hi = min(je, nf - 1);
             const int n_main = max(j_hi - j_lo, 0);
-            const int n_items = n_pro + (n_main > w ? (n_main - w + kWaves - 1) / kWaves : 0);
+            const int n_items = n_pro + (n_main > w ? (n_main - w + NW - 1) / NW : 0);
             auto block_of = [&](int k) -> int {
                 if (k < n_pro) return k == 0 ? 0 : nf - 1;
-                return j_lo + w + (k - n_pro) * kWaves;
+                return j_lo + w + (k - n_pro) * NW;
             };
             if (n_items > 0) {
                 float pro0 = 0.0f, theta = 0.0f;  // lanes < G: head = lane
@@ -838,7 +841,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
         } else {
             // selection made outside (a comparator rule): every block's head mask is read from
             // the caller's keep mask; nothing is scanned
-            for (int t = threadIdx.x; t < je - jb; t += kWaves * 64) {
+            for (int t = threadIdx.x; t < je - jb; t += NW * 64) {
                 u32 bits = 0;
 #pragma unroll
                 for (int h = 0; h < G; ++h)
@@ -856,7 +859,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
             // estimates of the split's earlier scanned blocks.  One wave per head, 64 blocks at a
             // time: an exclusive prefix maximum over the lanes plus the earlier chunks' maximum.
             const int nf = nf_b;
-            for (int h = w; h < G; h += kWaves) {
+            for (int h = w; h < G; h += NW) {
                 float carry = sh.u.run.mt[h];
                 for (int base = 0; base < je - jb; base += 64) {
                     const int t = base + lane;
@@ -879,7 +882,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
                 }
             }
             __syncthreads();
-            for (int t = threadIdx.x; t < je - jb; t += kWaves * 64)
+            for (int t = threadIdx.x; t < je - jb; t += NW * 64)
                 sh.kbits[t] |= (uint8_t)sh.u.run.bits[t];
             __syncthreads();
         }
@@ -925,10 +928,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
     st.l = 0.0f;
     {
         const int n_tiles = n_kept * NT;
-        const int n_w = n_tiles > w ? (n_tiles - w + kWaves - 1) / kWaves : 0;
+        const int n_w = n_tiles > w ? (n_tiles - w + NW - 1) / NW : 0;
         if (n_w > 0) {
             auto tile_of = [&](int k, int& t0, u32& kb) {
-                const int it = w + k * kWaves;
+                const int it = w + k * NW;
                 const int kk = it / NT;
                 int off;
                 if constexpr (SPARSE) {
@@ -1018,14 +1021,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
     const size_t rec0 = ((size_t)bg * p.S + split) * G;
     const bool fast = p.S <= 32;  // the counter word can carry a mask of the non-empty splits
     if (n_kept > 0) {
-        for (int e = threadIdx.x; e < G * D; e += kWaves * 64) {
+        for (int e = threadIdx.x; e < G * D; e += NW * 64) {
             const int h = e / D, c = e % D;
             float M = kNegInf;
 #pragma unroll
-            for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sh.u.merge.m[v][h]);
+            for (int v = 0; v < NW; ++v) M = fmaxf(M, sh.u.merge.m[v][h]);
             float o = 0.0f, l = 0.0f;
 #pragma unroll
-            for (int v = 0; v < kWaves; ++v) {
+            for (int v = 0; v < NW; ++v) {
                 const float mv = sh.u.merge.m[v][h];
                 const float sc = (mv == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
                 o = fmaf(sh.u.merge.o[v][h][c], sc, o);
@@ -1064,7 +1067,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
         // Non-empty splits in increasing order, read from the (wave-uniform) mask with scalar
         // bit operations; their (m, l) and o in one round of loads for every output of this
         // thread; then the log-sum-exp merge in split order: max, weights, weighted sums.
-        constexpr int NE = (G * D + kWaves * 64 - 1) / (kWaves * 64);
+        constexpr int NE = (G * D + NW * 64 - 1) / (NW * 64);
         constexpr int kMB = NE >= 4 ? 8 : 16;
         u32 mrest = __builtin_amdgcn_readfirstlane(sh.mask);
         float M[NE], L[NE], acc[NE];
@@ -1090,7 +1093,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
             float v[NE][kMB];
 #pragma unroll
             for (int i = 0; i < NE; ++i) {
-                const int e = min((int)threadIdx.x + i * kWaves * 64, G * D - 1);
+                const int e = min((int)threadIdx.x + i * NW * 64, G * D - 1);
                 const int h = e / D, c = e % D;
 #pragma unroll
                 for (int u = 0; u < kMB; ++u) {
@@ -1127,7 +1130,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
         }
 #pragma unroll
         for (int i = 0; i < NE; ++i) {
-            const int e = (int)threadIdx.x + i * kWaves * 64;
+            const int e = (int)threadIdx.x + i * NW * 64;
             if (e < G * D) {
                 const int h = e / D, c = e % D;
                 // an empty sequence (length 0) has no softmax: out = 0, lse = -inf
@@ -1141,7 +1144,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
     }
 
     // general path: (m, l) of every split first, then o of the non-empty ones
-    for (int h = w; h < G; h += kWaves) {
+    for (int h = w; h < G; h += NW) {
         float M = kNegInf;
         for (int s = lane; s < p.S; s += 64)
             M = fmaxf(M, ld_dev2(&p.part_ml[base + (size_t)s * G + h]).x);
@@ -1175,7 +1178,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_kernel(DecodeParams p)
         }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < G * D; e += kWaves * 64) {
+    for (int e = threadIdx.x; e < G * D; e += NW * 64) {
         const int h = e / D, c = e % D;
         const int n = sh.u.fin.cnt[h];
         float acc = 0.0f;
@@ -1382,7 +1385,7 @@ hipError_t launch_decode_g(const DecodeParams& p, bool sparse, hipStream_t strea
 template <int T, int BITS>
 hipError_t launch_res_g(const DecodeParams& p, hipStream_t stream)
 {
-    const dim3 grid(p.B * p.Hkv * p.S), block(kWaves * 64);
+    const dim3 grid(p.B * p.Hkv * p.S), block(kResWaves * 64);
     switch (p.G) {
     case 1: hipLaunchKernelGGL((decode_kernel<T, 1, true, true, BITS, true>), grid, block, 0, stream, p); break;
     case 2: hipLaunchKernelGGL((decode_kernel<T, 2, true, true, BITS, true>), grid, block, 0, stream, p); break;
