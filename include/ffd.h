@@ -276,9 +276,11 @@ size_t ffd_workspace_bytes_window(const ffd_dims* dims, int32_t block, int32_t w
  * environment variable FFD_NUM_SPLITS (a positive integer) overrides. */
 size_t ffd_workspace_bytes(const ffd_dims* dims, int32_t block);
 
-/* Prepares a workspace for the decode calls: zeroes its per-(sequence, kv head) counters with a
- * small kernel on `stream` (no memset, so it may be recorded into a graph).  Needed once per new
- * allocation; a completed decode call leaves the workspace prepared. */
+/* Prepares a workspace for the decode calls: zeroes its per-(sequence, kv head) counters (the
+ * first 8 * batch * n_kv_heads bytes, rounded up to 256) with a small kernel on `stream` (no
+ * memset, so it may be recorded into a graph).  FFD_ERR_WORKSPACE if workspace_bytes is smaller
+ * than that region; each decode call checks its own size.  Needed once per new allocation; a
+ * completed decode call leaves the workspace prepared. */
 ffd_status ffd_workspace_init(const ffd_dims* dims, int32_t block, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 

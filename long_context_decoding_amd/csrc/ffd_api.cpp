@@ -202,7 +202,9 @@ ffd_status ffd_workspace_init(const ffd_dims* dims, int32_t block, void* workspa
     if (st != FFD_OK) return st;
     if (dims->batch == 0) return FFD_OK;
     if (!workspace || !aligned16(workspace)) return FFD_ERR_WORKSPACE;
-    if (workspace_bytes < ws_layout(dims, splits_for(dims, block)).total) return FFD_ERR_WORKSPACE;
+    // only the counters are prepared: any workspace holding them qualifies (a decode call checks
+    // its own size requirement, which depends on its split count)
+    if (workspace_bytes < ws_layout(dims, 1).off_ml) return FFD_ERR_WORKSPACE;
     return finish(ffd::launch_zero_counters(static_cast<uint32_t*>(workspace),
                                             2 * dims->batch * dims->n_kv_heads, stream));
 }

@@ -177,12 +177,10 @@ def alloc_workspace(dims: Dims, block: int, device) -> torch.Tensor:
 
 
 def alloc_workspace_window(dims: Dims, block: int, window: int, device) -> torch.Tensor:
-    """A prepared workspace for decode_sparse_running with this window (also large enough for
-    the other decode calls with these dims)."""
+    """A prepared workspace for decode_sparse_running with this window."""
     n = lib().ffd_workspace_bytes_window(ctypes.byref(dims), block, window)
     if n == 0:
         raise FFDError(FFD_ERR_UNSUPPORTED, "invalid dims or window for workspace")
-    n = max(n, workspace_bytes(dims, block))
     ws = torch.empty(n, dtype=torch.uint8, device=device)
     workspace_init(dims, block, ws)
     return ws

@@ -125,7 +125,10 @@ def test_workspace_init_validation(L):
     wi = L.ffd_workspace_init
     assert wi(ctypes.byref(d), 64, None, n, None) == ffd.FFD_ERR_WORKSPACE
     assert wi(ctypes.byref(d), 64, MISALIGNED, n, None) == ffd.FFD_ERR_WORKSPACE
-    assert wi(ctypes.byref(d), 64, A, n - 1, None) == ffd.FFD_ERR_WORKSPACE
+    # only the counters need to fit: 8 bytes per (sequence, kv head), rounded up to 256
+    assert wi(ctypes.byref(d), 64, A, 255, None) == ffd.FFD_ERR_WORKSPACE
+    big = dims(B=40)  # 320 counters = 2560 bytes
+    assert wi(ctypes.byref(big), 64, A, 2559, None) == ffd.FFD_ERR_WORKSPACE
     assert wi(ctypes.byref(d), 96, A, n, None) == ffd.FFD_ERR_UNSUPPORTED
     assert wi(ctypes.byref(dims(B=0)), 64, None, 0, None) == ffd.FFD_OK
 
