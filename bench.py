@@ -489,6 +489,49 @@ def traffic_entry(bytes_alg: int):
     return rec.get("hbm_bytes_per_launch")
 
 
+def probe_leg(nbytes: int, steps: int, groups=(256, 1024)) -> dict:
+    """Achievable HBM read bandwidth on this chip: the plain streaming-read probe
+    (include/ffd_probe.h) over `nbytes` (the decode step's algorithmic bytes, rounded up to
+    16), graph-replayed `steps` times rotating over buffers that total >= 1 GiB, like the decode
+    step's own timing.  One figure per work-group count."""
+    import torch
+
+    from long_context_decoding_amd import probe
+
+    n = (nbytes + 15) // 16 * 16
+    R = max(2, math.ceil((1 << 30) / n) + 1)
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    for b in bufs:
+        b.fill_(1)
+    sink = torch.empty((max(groups), 4), dtype=torch.int32, device="cuda")
+    out = {"bytes": n, "copies": R}
+    for g in groups:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            probe.stream_read(bufs[0], g, sink)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                probe.stream_read(bufs[i % R], g, sink)
+        graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / steps
+        out[f"groups_{g}"] = {"us": us, "GBps": n / us * 1e-3}
+        del graph
+    out["GBps"] = max(v["GBps"] for k, v in out.items() if k.startswith("groups_"))
+    del bufs
+    torch.cuda.synchronize()
+    return out
+
+
 def running_leg(names=("h1_4k_f32_needles", "gqa4_32k_sink_needles")) -> dict:
     """Keep ratio and fidelity (cosine to the dense output, LSE error) of the running-max variant
     against Alg. 1's fixed pseudo-max, on workloads without (4K, one head) and with (32K) a planted
@@ -620,6 +663,14 @@ def main() -> int:
                               graphs=not args.eager)
         log(f"{w2.name}: sparse {sec['sparse_us']:.1f} us, dense {sec['dense_us']:.1f} us, "
             f"{sec['sparse_GBps']:.0f} GB/s, keep {sec['union_keep']:.4f}")
+        sec["probe"] = probe_leg(sec["bytes_read_sparse"], args.steps)
+        sec["frac_of_probe"] = sec["sparse_GBps"] / sec["probe"]["GBps"]
+        log(f"{w2.name}: streaming-read probe {sec['probe']['GBps']:.0f} GB/s; the sparse step "
+            f"reaches {sec['frac_of_probe']:.1%} of it")
+    prb = probe_leg(prim["bytes_read_sparse"], args.steps)
+    log(f"streaming-read probe over {prb['bytes'] / 1e6:.1f} MB: {prb['GBps']:.0f} GB/s "
+        f"({prb['GBps'] / HBM_PEAK_GBPS:.1%} of {HBM_PEAK_GBPS:.0f}); the sparse step reaches "
+        f"{prim['sparse_GBps'] / prb['GBps']:.1%} of it")
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
@@ -657,7 +708,10 @@ def main() -> int:
             "frac": round(prim["sparse_hbm_frac"], 4),
             "traffic": traffic,
             "bytes_per_launch": prim["bytes_read_sparse"],
+            "ceiling_probe_GBps": round(prb["GBps"], 1),
+            "frac_of_probe": round(prim["sparse_GBps"] / prb["GBps"], 4),
         },
+        "probe": prb,
         "cpu_baseline": cpu,
         "primary": prim,
         "secondary": sec,

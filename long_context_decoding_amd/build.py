@@ -1,4 +1,4 @@
-"""Build libffd.so (gfx950) in-tree with hipcc.
+"""Build libffd.so (gfx950) and the measurement aid libffd_probe.so in-tree with hipcc.
 
     python -m long_context_decoding_amd.build
 """
@@ -15,6 +15,8 @@ CSRC = PKG / "csrc"
 LIB = PKG / "libffd.so"
 SOURCES = [CSRC / "ffd_kernels.hip", CSRC / "ffd_api.cpp"]
 HEADERS = [CSRC / "ffd_internal.h", ROOT / "include" / "ffd.h"]
+PROBE_LIB = PKG / "libffd_probe.so"
+PROBE_SOURCES = [CSRC / "probe.hip"]
 ARCH = os.environ.get("FFD_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -39,9 +41,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> Path:
-    tmp = LIB.with_suffix(".so.tmp")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", str(tmp), *map(str, SOURCES)]
+def _compile(lib: Path, sources, verbose: bool) -> Path:
+    tmp = lib.with_suffix(".so.tmp")
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", str(tmp), *map(str, sources)]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,7 +53,14 @@ def build(verbose: bool = False) -> Path:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> Path:
+    """Compile libffd.so and libffd_probe.so; returns the path of libffd.so."""
+    _compile(LIB, SOURCES, verbose)
+    _compile(PROBE_LIB, PROBE_SOURCES, verbose)
     return LIB
 
 

@@ -263,3 +263,25 @@ def test_running_validation(L):
     assert run(ctypes.byref(big), A, A, A, A, A, 5.0, 64, 1, A, A, None, A, 1 << 30,
                None) == ffd.FFD_ERR_UNSUPPORTED
     assert L.ffd_workspace_bytes_window(ctypes.byref(big), 64, 1) == 0
+
+
+def test_probe_library_exports_and_validates():
+    """The measurement aid's header and library agree, and invalid arguments launch nothing."""
+    from long_context_decoding_amd import probe
+    if not probe.LIB_PATH.exists():
+        pytest.skip("libffd_probe.so not built")
+    header = Path(__file__).resolve().parents[1] / "include" / "ffd_probe.h"
+    text = re.sub(r"/\*.*?\*/", "", header.read_text(), flags=re.S)
+    names = set(re.findall(r"\b(ffd_[a-z_0-9]+)\s*\(", text))
+    assert names == {"ffd_probe_stream_read"}
+    nm = subprocess.run(["nm", "-D", "--defined-only", str(probe.LIB_PATH)], capture_output=True,
+                        text=True, check=True).stdout
+    assert names <= set(re.findall(r"\bT (ffd_\w+)", nm))
+    f = probe.lib().ffd_probe_stream_read
+    assert f(None, 1024, 4, A, None) == 1
+    assert f(A, 1024, 4, None, None) == 1
+    assert f(MISALIGNED, 1024, 4, A, None) == 1
+    assert f(A, 1000, 4, A, None) == 1
+    assert f(A, 0, 4, A, None) == 1
+    assert f(A, 1024, 0, A, None) == 1
+    assert f(A, 1024, 65536, A, None) == 1
