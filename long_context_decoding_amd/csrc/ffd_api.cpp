@@ -52,10 +52,16 @@ int splits_for(const ffd_dims* d, int32_t block)
         if (s > n_blocks) s = n_blocks;
     } else {
         // one work-group per CU: fewer, longer streams measured faster than more resident
-        // work-groups at every occupancy tried
+        // work-groups at every occupancy tried.  A split keeps at least two blocks per wave,
+        // except that a short sequence may go down to two blocks per split (at most 32 splits):
+        // such a step is latency-bound, and more work-groups finish it sooner (a 4K-token,
+        // one-head step: 22 us at 8 splits, 14 us at 32)
         const int64_t target_wgs = 256;
         s = bh > 0 ? (target_wgs + bh - 1) / bh : 1;
-        const int64_t max_s = n_blocks / (2 * kWaves) > 0 ? n_blocks / (2 * kWaves) : 1;
+        const int64_t few = n_blocks / 2 < 32 ? n_blocks / 2 : 32;
+        int64_t max_s = n_blocks / (2 * kWaves);
+        if (max_s < few) max_s = few;
+        if (max_s < 1) max_s = 1;
         if (s > max_s) s = max_s;
     }
     if (s > kMaxSplits) s = kMaxSplits;
