@@ -610,6 +610,10 @@ struct __attribute__((aligned(16))) DecodeShared {
             float M[G], Lsum[G];
             int cnt[G];
         } fin;
+        struct {                                            // final merge, fast path: the
+            v4f acc[NW * 64];                               // threads' shares of the splits
+            float M[NW * 64], L[NW * 64];
+        } share;
         struct {                                            // running-max selection
             float s[kMaxBlocksPerSplit][G];                 // scan estimates of the split's blocks
             float mt[G];                                    // Alg. 1 pseudo-max of each head
@@ -662,6 +666,36 @@ __device__ __forceinline__ float2 ld_dev2(const float2* p)
     const unsigned long long v = __hip_atomic_load(
         reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return make_float2(as_f((int)(u32)v), as_f((int)(u32)(v >> 32)));
+}
+
+// 16- and 8-byte device-scope accesses through a buffer resource (raw buffer, no swizzle, the
+// gfx9 default format word), with the same cache policy as the relaxed agent-scope atomics above
+// (sc1).  A buffer access outside the resource's byte range reads zero and writes nothing.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kCpolDevice = 16;  // sc1
+__device__ __forceinline__ rsrc_t dev_rsrc(const void* base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void st_dev16(rsrc_t r, int off, v4f v)
+{
+    typedef u32 v4u __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, off, 0, kCpolDevice);
+}
+__device__ __forceinline__ v4f ld_dev16(rsrc_t r, int off)
+{
+    return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolDevice));
+}
+__device__ __forceinline__ void st_dev8(rsrc_t r, int off, float a, float b)
+{
+    typedef u32 v2u __attribute__((ext_vector_type(2)));
+    const v2u v = {(u32)as_i(a), (u32)as_i(b)};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpolDevice);
+}
+__device__ __forceinline__ float2 ld_dev8(rsrc_t r, int off)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpolDevice);
+    return make_float2(as_f((int)v[0]), as_f((int)v[1]));
 }
 
 // One work-group per (sequence b, kv head g, split of the sequence).  Phases:
@@ -1021,21 +1055,27 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
     const size_t rec0 = ((size_t)bg * p.S + split) * G;
     const bool fast = p.S <= 32;  // the counter word can carry a mask of the non-empty splits
     if (n_kept > 0) {
-        for (int e = threadIdx.x; e < G * D; e += NW * 64) {
-            const int h = e / D, c = e % D;
+        // one 16-byte store per four channels of a head, (m, l) with the first four
+        const rsrc_t ro = dev_rsrc(p.part_o + rec0 * D, G * D * 4);
+        const rsrc_t rml = dev_rsrc(p.part_ml + rec0, G * 8);
+        for (int e = threadIdx.x; e < G * (D / 4); e += NW * 64) {
+            const int h = e / (D / 4), c = (e % (D / 4)) * 4;
             float M = kNegInf;
 #pragma unroll
             for (int v = 0; v < NW; ++v) M = fmaxf(M, sh.u.merge.m[v][h]);
-            float o = 0.0f, l = 0.0f;
+            v4f o = {0.0f, 0.0f, 0.0f, 0.0f};
+            float l = 0.0f;
 #pragma unroll
             for (int v = 0; v < NW; ++v) {
                 const float mv = sh.u.merge.m[v][h];
                 const float sc = (mv == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
-                o = fmaf(sh.u.merge.o[v][h][c], sc, o);
+                const v4f ov = *reinterpret_cast<const v4f*>(&sh.u.merge.o[v][h][c]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = fmaf(ov[i], sc, o[i]);
                 l = fmaf(sh.u.merge.l[v][h], sc, l);
             }
-            st_dev(&p.part_o[(rec0 + h) * D + c], o);
-            if (c == 0) st_dev2(&p.part_ml[rec0 + h], M, l);
+            st_dev16(ro, e * 16, o);
+            if (c == 0) st_dev8(rml, h * 8, M, l);
         }
     } else if (!fast && threadIdx.x < G) {
         st_dev2(&p.part_ml[rec0 + threadIdx.x], kNegInf, 0.0f);
@@ -1064,82 +1104,106 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
 
     const size_t base = (size_t)bg * p.S * G;
     if (fast) {
-        // Non-empty splits in increasing order, read from the (wave-uniform) mask with scalar
-        // bit operations; their (m, l) and o in one round of loads for every output of this
-        // thread; then the log-sum-exp merge in split order: max, weights, weighted sums.
-        constexpr int NE = (G * D + NW * 64 - 1) / (NW * 64);
-        constexpr int kMB = NE >= 4 ? 8 : 16;
-        u32 mrest = __builtin_amdgcn_readfirstlane(sh.mask);
-        float M[NE], L[NE], acc[NE];
-#pragma unroll
-        for (int i = 0; i < NE; ++i) {
-            M[i] = kNegInf;
-            L[i] = 0.0f;
-            acc[i] = 0.0f;
+        // Thread (part, e) merges four channels e of one head over a share of the non-empty
+        // splits: those of rank part, part + P, ... among them, in increasing split order, read
+        // with 16-byte device-scope loads in rounds of kMB splits.  The P shares are then merged
+        // in part order through LDS, so the result does not depend on timing.
+        constexpr int NT = NW * 64;
+        constexpr int NE4 = G * (D / 4);
+        static_assert(NT % NE4 == 0, "the group's outputs must tile the work-group");
+        constexpr int P = NT / NE4;
+        constexpr int kMB = P == 1 ? 16 : 8;
+        const int e = (int)threadIdx.x % NE4, part = (int)threadIdx.x / NE4;
+        const int h = e / (D / 4), c = (e % (D / 4)) * 4;
+        u32 mine = sh.mask;
+        if constexpr (P > 1) {
+            u32 rest = mine;
+            mine = 0u;
+            for (int r = 0; rest != 0u; ++r) {
+                const u32 low = rest & (0u - rest);
+                if (r % P == part) mine |= low;
+                rest ^= low;
+            }
         }
-        while (mrest != 0u) {
+        const rsrc_t ro = dev_rsrc(p.part_o + base * D, p.S * G * D * 4);
+        const rsrc_t rml = dev_rsrc(p.part_ml + base, p.S * G * 8);
+        float M = kNegInf, Ls = 0.0f;
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        while (mine != 0u) {
             int sidx[kMB];
             int nb = 0;
 #pragma unroll
             for (int u = 0; u < kMB; ++u) {
-                const int s = mrest ? __builtin_ctz(mrest) : -1;
-                if (mrest) {
-                    mrest &= mrest - 1u;
+                sidx[u] = mine ? __builtin_ctz(mine) : 0;
+                if (mine) {
+                    mine &= mine - 1u;
                     ++nb;
                 }
-                sidx[u] = s < 0 ? (u > 0 ? sidx[u - 1] : 0) : s;
             }
-            float2 ml[NE][kMB];
-            float v[NE][kMB];
+            float2 ml[kMB];
+            v4f v[kMB];
 #pragma unroll
-            for (int i = 0; i < NE; ++i) {
-                const int e = min((int)threadIdx.x + i * NW * 64, G * D - 1);
-                const int h = e / D, c = e % D;
-#pragma unroll
-                for (int u = 0; u < kMB; ++u) {
-                    if (u < nb) {
-                        const size_t r = base + (size_t)sidx[u] * G + h;
-                        ml[i][u] = ld_dev2(&p.part_ml[r]);
-                        v[i][u] = ld_dev(&p.part_o[r * D + c]);
-                    } else {
-                        ml[i][u] = make_float2(kNegInf, 0.0f);
-                        v[i][u] = 0.0f;
-                    }
+            for (int u = 0; u < kMB; ++u) {
+                if (u < nb) {
+                    const int r = sidx[u] * G + h;
+                    ml[u] = ld_dev8(rml, r * 8);
+                    v[u] = ld_dev16(ro, (r * D + c) * 4);
+                } else {
+                    ml[u] = make_float2(kNegInf, 0.0f);
+                    v[u] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
                 }
             }
+            // a head may have kept nothing in a split that another head used (m = -inf)
+            float Mb = M;
 #pragma unroll
-            for (int i = 0; i < NE; ++i) {
-                // a head may have kept nothing in a split that another head used (m = -inf)
-                float Mb = M[i];
+            for (int u = 0; u < kMB; ++u)
+                if (ml[u].y > 0.0f) Mb = fmaxf(Mb, ml[u].x);
+            const float a = (M == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(M - Mb);
+            v4f sa = acc * a;
+            float sl = Ls * a;
 #pragma unroll
-                for (int u = 0; u < kMB; ++u)
-                    if (ml[i][u].y > 0.0f) Mb = fmaxf(Mb, ml[i][u].x);
-                const float a = (M[i] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(M[i] - Mb);
-                float sa = acc[i] * a, sl = L[i] * a;
+            for (int u = 0; u < kMB; ++u) {
+                const float wgt = ml[u].y > 0.0f ? __builtin_amdgcn_exp2f(ml[u].x - Mb) : 0.0f;
 #pragma unroll
-                for (int u = 0; u < kMB; ++u) {
-                    const float wgt =
-                        ml[i][u].y > 0.0f ? __builtin_amdgcn_exp2f(ml[i][u].x - Mb) : 0.0f;
-                    sa = fmaf(v[i][u], wgt, sa);
-                    sl = fmaf(ml[i][u].y, wgt, sl);
-                }
-                M[i] = Mb;
-                acc[i] = sa;
-                L[i] = sl;
+                for (int i = 0; i < 4; ++i) sa[i] = fmaf(v[u][i], wgt, sa[i]);
+                sl = fmaf(ml[u].y, wgt, sl);
             }
+            M = Mb;
+            acc = sa;
+            Ls = sl;
         }
+        if constexpr (P > 1) {
+            sh.u.share.acc[threadIdx.x] = acc;
+            sh.u.share.M[threadIdx.x] = M;
+            sh.u.share.L[threadIdx.x] = Ls;
+            __syncthreads();
+            if (part != 0) return;
+            float Mb = M;
 #pragma unroll
-        for (int i = 0; i < NE; ++i) {
-            const int e = (int)threadIdx.x + i * NW * 64;
-            if (e < G * D) {
-                const int h = e / D, c = e % D;
-                // an empty sequence (length 0) has no softmax: out = 0, lse = -inf
-                p.out[(size_t)(h0 + h) * D + c] = L[i] > 0.0f ? acc[i] / L[i] : 0.0f;
-                if (p.lse && c == 0)
-                    p.lse[h0 + h] =
-                        L[i] > 0.0f ? (M[i] + __log2f(L[i])) * 0.69314718055994530942f : kNegInf;
+            for (int q = 1; q < P; ++q)
+                if (sh.u.share.L[q * NE4 + e] > 0.0f) Mb = fmaxf(Mb, sh.u.share.M[q * NE4 + e]);
+            const float a = (M == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(M - Mb);
+            acc = acc * a;
+            Ls = Ls * a;
+#pragma unroll
+            for (int q = 1; q < P; ++q) {
+                const float Lq = sh.u.share.L[q * NE4 + e];
+                const float wgt =
+                    Lq > 0.0f ? __builtin_amdgcn_exp2f(sh.u.share.M[q * NE4 + e] - Mb) : 0.0f;
+                const v4f vq = sh.u.share.acc[q * NE4 + e];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = fmaf(vq[i], wgt, acc[i]);
+                Ls = fmaf(Lq, wgt, Ls);
             }
+            M = Mb;
         }
+        // an empty sequence (length 0) has no softmax: out = 0, lse = -inf
+        v4f r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = Ls > 0.0f ? acc[i] / Ls : 0.0f;
+        *reinterpret_cast<v4f*>(p.out + (size_t)(h0 + h) * D + c) = r;
+        if (p.lse && c == 0)
+            p.lse[h0 + h] = Ls > 0.0f ? (M + __log2f(Ls)) * 0.69314718055994530942f : kNegInf;
         return;
     }
 
