@@ -426,7 +426,8 @@ def run_workload(w, delta: float, steps: int, warmup: int, min_rotation_mib: int
     res = {
         "workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "L": w.L,
         "block": w.T, "delta": delta, "kv_dtype": w.dtype, "scan_bits": 4,
-        "splits": ffd.num_splits(dims, w.T), "cache_copies": R,
+        "splits": ffd.num_splits(dims, w.T), "dense_splits": ffd.num_splits(dims, w.T, False),
+        "cache_copies": R,
         "sparse_us": us_s, "dense_us": us_d,
         "sparse_us_eager": us_s_eager, "dense_us_eager": us_d_eager,
         "sparse_us_warm_cache": us_s_warm, "dense_us_warm_cache": us_d_warm,

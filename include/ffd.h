@@ -284,7 +284,8 @@ size_t ffd_workspace_bytes(const ffd_dims* dims, int32_t block);
 ffd_status ffd_workspace_init(const ffd_dims* dims, int32_t block, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
-/* Number of sequence splits (work-groups per (sequence, kv head)) the decode calls use. */
+/* Number of sequence splits (work-groups per (sequence, kv head)) that ffd_decode_sparse (sparse
+ * != 0) or ffd_decode_dense (sparse == 0) uses for these dims and block; 0 for invalid dims. */
 int32_t ffd_num_splits(const ffd_dims* dims, int32_t block, int32_t sparse);
 
 /* Static description of a status code. */

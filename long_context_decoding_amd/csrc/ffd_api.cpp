@@ -40,7 +40,7 @@ ffd_status check_dims(const ffd_dims* d, int32_t block)
     return FFD_OK;
 }
 
-int splits_for(const ffd_dims* d, int32_t block)
+int splits_for(const ffd_dims* d, int32_t block, bool sparse)
 {
     const int n_blocks = (d->seq_len + block - 1) / block;
     const int64_t bh = (int64_t)d->batch * d->n_kv_heads;
@@ -63,6 +63,14 @@ int splits_for(const ffd_dims* d, int32_t block)
         if (max_s < few) max_s = few;
         if (max_s < 1) max_s = 1;
         if (s > max_s) s = max_s;
+        // dense: splits of at most 8192 tokens.  Its work per split is uniform, and the
+        // dispatcher balances the extra work-groups (128K x 8: 697 against 710 us at 16 splits
+        // instead of 8; 64K x 16: 708 against 717 us at 8 instead of 4); the sparse step, whose
+        // splits carry a per-split pseudo-max, ramp and partial, measured slower with them
+        if (!sparse) {
+            const int64_t s_tok = d->seq_len / 8192;
+            if (s < s_tok) s = s_tok;
+        }
     }
     if (s > kMaxSplits) s = kMaxSplits;
     if (s < min_s) s = min_s;
@@ -122,7 +130,7 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
     if (window != 0 && (window < 1 || window > kMaxBlocksPerSplit ||
                         (n_blk + window - 1) / window > kMaxSplits))
         return FFD_ERR_UNSUPPORTED;
-    const int S = window != 0 ? (n_blk + window - 1) / window : splits_for(dims, block);
+    const int S = window != 0 ? (n_blk + window - 1) / window : splits_for(dims, block, sparse);
     const WsLayout lay = ws_layout(dims, S);
     if (!workspace || !aligned16(workspace)) return FFD_ERR_WORKSPACE;
     if (workspace_bytes < lay.total) return FFD_ERR_WORKSPACE;
@@ -198,7 +206,8 @@ const char* ffd_status_string(ffd_status s)
 size_t ffd_workspace_bytes(const ffd_dims* dims, int32_t block)
 {
     if (check_dims(dims, block) != FFD_OK) return 0;
-    return ws_layout(dims, splits_for(dims, block)).total;
+    const int s_sparse = splits_for(dims, block, true), s_dense = splits_for(dims, block, false);
+    return ws_layout(dims, s_sparse > s_dense ? s_sparse : s_dense).total;
 }
 
 ffd_status ffd_workspace_init(const ffd_dims* dims, int32_t block, void* workspace,
@@ -217,9 +226,8 @@ ffd_status ffd_workspace_init(const ffd_dims* dims, int32_t block, void* workspa
 
 int32_t ffd_num_splits(const ffd_dims* dims, int32_t block, int32_t sparse)
 {
-    (void)sparse;
     if (check_dims(dims, block) != FFD_OK) return 0;
-    return splits_for(dims, block);
+    return splits_for(dims, block, sparse != 0);
 }
 
 ffd_status ffd_quantize_k_append(const ffd_dims* dims, const void* K, int32_t tok_begin,
