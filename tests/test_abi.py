@@ -71,6 +71,13 @@ def test_workspace_and_splits(L):
     big = dims(B=8, seq_len=131072, seq_cap=131072)
     S = ffd.num_splits(big, 64)
     assert -(-2048 // S) <= 256
+    # the dense step splits further (at most 8192 tokens per split); the workspace covers both
+    Sd = ffd.num_splits(big, 64, sparse=False)
+    assert Sd == 131072 // 8192 and Sd > S
+    rec = 8 * 8 * Sd * 4
+    assert ffd.workspace_bytes(big, 64) == r256(8 * 8 * 8) + r256(rec * 8) + rec * 128 * 4
+    long1 = dims(seq_len=262144, seq_cap=262144)
+    assert ffd.num_splits(long1, 128, sparse=False) == ffd.num_splits(long1, 128) == 32
     assert ffd.workspace_bytes(dims(head_dim=64), 64) == 0
     assert ffd.workspace_bytes(d, 96) == 0
 
