@@ -478,16 +478,19 @@ def cpu_baseline(w, delta: float, host, budget_s: float = 12.0) -> dict:
                        f"{quant_s:.2f}s not included")}
 
 
-def traffic_entry(bytes_alg: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
-    current kernel source; else None."""
+def traffic_entry(workload: str):
+    """HBM bytes per launch of the sparse step on `workload`, from the committed rocprofv3 counter
+    summaries, if they were taken on the current kernel source and cover that workload; else
+    None."""
     try:
         rec = json.loads(TRAFFIC_FILE.read_text())
     except (OSError, ValueError):
         return None
     if rec.get("kernel_src_sha256_16") != kernel_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    if rec.get("workload") == workload:
+        return rec.get("hbm_bytes_per_launch")
+    return rec.get("other_workloads", {}).get(workload, {}).get("hbm_bytes_per_launch")
 
 
 def probe_leg(nbytes: int, steps: int, groups=(256, 1024)) -> dict:
@@ -679,7 +682,7 @@ def main() -> int:
     del host
 
     us = prim["sparse_us"]
-    traffic = traffic_entry(prim["bytes_read_sparse"])
+    traffic = traffic_entry(w.name)
     line = {
         "metric": METRIC,
         "value": round(us, 3),
@@ -711,6 +714,18 @@ def main() -> int:
             "bytes_per_launch": prim["bytes_read_sparse"],
             "ceiling_probe_GBps": round(prb["GBps"], 1),
             "frac_of_probe": round(prim["sparse_GBps"] / prb["GBps"], 4),
+        },
+        "roofline_secondary": None if sec is None else {
+            "bound": "hbm",
+            "kernel": f"ffd sparse decode step, {sec['workload']}",
+            "achieved": round(sec["sparse_GBps"], 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(sec["sparse_hbm_frac"], 4),
+            "traffic": traffic_entry(sec["workload"]),
+            "bytes_per_launch": sec["bytes_read_sparse"],
+            "ceiling_probe_GBps": round(sec["probe"]["GBps"], 1) if sec.get("probe") else None,
+            "frac_of_probe": round(sec["frac_of_probe"], 4) if sec.get("frac_of_probe") else None,
         },
         "probe": prb,
         "cpu_baseline": cpu,
