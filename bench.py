@@ -478,6 +478,38 @@ def cpu_baseline(w, delta: float, host, budget_s: float = 12.0) -> dict:
                        f"{quant_s:.2f}s not included")}
 
 
+def cpu_single_thread(names=("h1_4k_f32_needles", "gqa4_32k_sink_needles")) -> list:
+    """The oracle, unchanged, on one host thread for the two small workloads: quantization of
+    the cache, the sparse step (delta of the workload's first entry) and the dense step, each
+    the median of 3 runs after a warm one."""
+    import oracle
+    from long_context_decoding_amd import workloads as W
+
+    rows = []
+    for name in names:
+        w = W.WORKLOADS[name]
+        q, K, V, _ = W.make_inputs(w)
+        t0 = time.perf_counter()
+        Kq, sc = oracle.quantize_k(K, w.T, 0, w.L)
+        quant = time.perf_counter() - t0
+
+        def med(fn):
+            fn()
+            ts = []
+            for _ in range(3):
+                t = time.perf_counter()
+                fn()
+                ts.append(time.perf_counter() - t)
+            return float(np.median(ts)) * 1e3
+
+        sp = med(lambda: oracle.decode(q, K, V, w.L, w.T, delta=w.deltas[0], Kq=Kq, scales=sc,
+                                       n_threads=1))
+        de = med(lambda: oracle.decode(q, K, V, w.L, w.T, sparse=False, n_threads=1))
+        rows.append({"workload": name, "delta": w.deltas[0], "threads": 1,
+                     "quantize_ms": quant * 1e3, "sparse_ms": sp, "dense_ms": de})
+    return rows
+
+
 def traffic_entry(workload: str):
     """HBM bytes per launch of the sparse step on `workload`, from the committed rocprofv3 counter
     summaries, if they were taken on the current kernel source and cover that workload; else
@@ -679,6 +711,10 @@ def main() -> int:
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(w, delta, host)
+        cpu["single_thread"] = cpu_single_thread()
+        log("oracle on one host thread: " + ", ".join(
+            f"{r['workload']} sparse {r['sparse_ms']:.1f} ms, dense {r['dense_ms']:.1f} ms"
+            for r in cpu["single_thread"]))
     del host
 
     us = prim["sparse_us"]
