@@ -722,14 +722,16 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
     // work-group -> (b, kv head, split).  Sparse: the S splits of one (b, g) are consecutive
     // work-groups, which the dispatcher deals round-robin to the XCDs, so every XCD holds
     // splits of every (b, g) and the exact work of a (b, g) that keeps many blocks is spread
-    // over all of them; ranks 0 and 1 are the splits holding the sink (0) and the local block
-    // (S-1), which always carry exact work.  Dense (the same work in every split): all splits
-    // of one (b, g) share blockIdx.x mod (B*Hkv), one XCD when B*Hkv is a multiple of 8.  Each
-    // layout measured faster than the other for its kernel.
+    // over all of them.  Ranks 0 and 1 are the splits holding the sink (0) and the local block
+    // (S-1), which always carry exact work; the ranks of (b, g) start at work-group offset
+    // S - bg mod S, so that these forced splits of different (b, g) fall on different XCDs.
+    // Dense (the same work in every split): all splits of one (b, g) share blockIdx.x mod
+    // (B*Hkv), one XCD when B*Hkv is a multiple of 8.  Each layout measured faster than the
+    // other for its kernel.
     const int bh = p.B * p.Hkv;
     const int id = blockIdx.x;
     const int bg = SPARSE ? id / p.S : id % bh;
-    const int rank = SPARSE ? id % p.S : id / bh;
+    const int rank = SPARSE ? (id % p.S + bg) % p.S : id / bh;
     int split = rank;
     if (SPARSE && p.S > 1) split = rank == 0 ? 0 : (rank == 1 ? p.S - 1 : rank - 1);
     const int b = bg / p.Hkv, g = bg % p.Hkv;
