@@ -172,7 +172,7 @@ ffd_status ffd_decode_sparse_residual(const ffd_dims* dims, const void* q, const
  *   K, V, Kq, scales  the caches (layouts of ffd_decode_sparse), updated in place
  *   seq_lens   device int32 [B], the current lengths; a sequence already at dims->seq_cap (or
  *              with a negative length) is left unchanged and nothing of it is written
- * dims->seq_len is not used (it must still be valid). Two kernel launches, no host synchronisation.
+ * dims->seq_len is not used (it must still be valid). One kernel launch, no host synchronisation.
  */
 ffd_status ffd_append_token(const ffd_dims* dims, const void* k_new, const void* v_new, void* K,
                             void* V, int32_t* seq_lens, int32_t block, uint8_t* Kq,

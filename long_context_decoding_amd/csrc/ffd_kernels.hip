@@ -1329,43 +1329,52 @@ __global__ __launch_bounds__(128) void quantize_kernel(QuantParams p)
 // Fig. 2).  A sequence already at the capacity is left as it is.  The lengths advance in a
 // separate launch, after every (b, kv head) of the step has read them.
 // ------------------------------------------------------------------------------------------
+// One decode-loop step of the cache, in one launch.  One work-group per sequence b; thread
+// (gi, c) handles channel c of kv heads g = gi, gi + nh, ... (nh = blockDim.x / d): the new key and
+// value rows go to position seq_lens[b], and the key block they complete, if any, is quantized
+// (this thread wrote the block's last key of its channel; the other rows are older).  Every thread
+// reads the length before the barrier and thread 0 advances it after, so no thread of the launch
+// sees the advanced value.
+constexpr int kAppendHeads = 4;  // kv heads handled side by side by one work-group (a column
+                                 // of T keys per thread stays in registers at 512 threads)
 template <int T, bool BF16>
-__global__ __launch_bounds__(128) void append_kernel(AppendParams a)
+__global__ __launch_bounds__(kAppendHeads * 128) void append_kernel(AppendParams a)
 {
-    const int bg = blockIdx.x;
-    const int b = bg / a.Hkv;
-    const int c = threadIdx.x;
+    const int b = blockIdx.x;
+    const int c = threadIdx.x % D;
+    const int nh = blockDim.x / D;
     const int pos = a.seq_lens[b];
-    if (pos < 0 || pos >= a.cap) return;  // uniform over the work-group
-    const size_t src = (size_t)bg * D + c;
-    const size_t dst = ((size_t)bg * a.cap + pos) * D + c;
-    if constexpr (BF16) {
-        static_cast<unsigned short*>(a.K)[dst] = static_cast<const unsigned short*>(a.k_new)[src];
-        static_cast<unsigned short*>(a.V)[dst] = static_cast<const unsigned short*>(a.v_new)[src];
-    } else {
-        static_cast<float*>(a.K)[dst] = static_cast<const float*>(a.k_new)[src];
-        static_cast<float*>(a.V)[dst] = static_cast<const float*>(a.v_new)[src];
+    const bool ok = pos >= 0 && pos < a.cap;  // uniform over the work-group
+    if (ok) {
+        // the kv head is uniform over a wave (D = 2 waves per head): held in a scalar register,
+        // the block's row addresses stay scalar
+#pragma unroll 1
+        for (int g = __builtin_amdgcn_readfirstlane((int)threadIdx.x / D); g < a.Hkv; g += nh) {
+            const int bg = b * a.Hkv + g;
+            const size_t src = (size_t)bg * D + c;
+            const size_t dst = ((size_t)bg * a.cap + pos) * D + c;
+            if constexpr (BF16) {
+                static_cast<unsigned short*>(a.K)[dst] =
+                    static_cast<const unsigned short*>(a.k_new)[src];
+                static_cast<unsigned short*>(a.V)[dst] =
+                    static_cast<const unsigned short*>(a.v_new)[src];
+            } else {
+                static_cast<float*>(a.K)[dst] = static_cast<const float*>(a.k_new)[src];
+                static_cast<float*>(a.V)[dst] = static_cast<const float*>(a.v_new)[src];
+            }
+            if ((pos + 1) % T == 0) {
+                QuantParams q{};
+                q.K = a.K;
+                q.Kq = a.Kq;
+                q.scales = a.scales;
+                q.cap = a.cap;
+                q.T = T;
+                quantize_block<T, BF16>(q, bg, pos / T, c);
+            }
+        }
     }
-    if ((pos + 1) % T == 0) {
-        // this thread wrote the block's last key of its channel; the other rows are older
-        QuantParams q{};
-        q.K = a.K;
-        q.Kq = a.Kq;
-        q.scales = a.scales;
-        q.cap = a.cap;
-        q.T = T;
-        quantize_block<T, BF16>(q, bg, pos / T, c);
-    }
-}
-
-__global__ __launch_bounds__(256) void advance_kernel(int32_t* __restrict__ seq_lens, int B,
-                                                      int cap)
-{
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b < B) {
-        const int L = seq_lens[b];
-        if (L >= 0 && L < cap) seq_lens[b] = L + 1;
-    }
+    __syncthreads();
+    if (ok && threadIdx.x == 0) a.seq_lens[b] = pos + 1;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1862,7 +1871,7 @@ hipError_t launch_zero_counters(uint32_t* counters, int n, hipStream_t stream)
 hipError_t launch_append(const AppendParams& p, bool bf16, hipStream_t stream)
 {
     if (p.B <= 0) return hipSuccess;
-    const dim3 grid(p.B * p.Hkv), block(D);
+    const dim3 grid(p.B), block(D * (p.Hkv < kAppendHeads ? p.Hkv : kAppendHeads));
     if (p.T == 64) {
         if (bf16) hipLaunchKernelGGL((append_kernel<64, true>), grid, block, 0, stream, p);
         else hipLaunchKernelGGL((append_kernel<64, false>), grid, block, 0, stream, p);
@@ -1872,10 +1881,6 @@ hipError_t launch_append(const AppendParams& p, bool bf16, hipStream_t stream)
     } else {
         return hipErrorInvalidValue;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(advance_kernel, dim3((p.B + 255) / 256), dim3(256), 0, stream, p.seq_lens,
-                       p.B, p.cap);
     return hipGetLastError();
 }
 
