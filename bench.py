@@ -42,7 +42,10 @@ def log(msg: str) -> None:
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()[:16]
+    try:
+        return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()[:16]
+    except OSError:  # a tree with the built library but not its source: no counter figure applies
+        return None
 
 
 # ------------------------------------------------------------------------------------------
@@ -518,7 +521,8 @@ def traffic_entry(workload: str):
         rec = json.loads(TRAFFIC_FILE.read_text())
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_src_sha256_16") != kernel_hash():
+    h = kernel_hash()
+    if h is None or rec.get("kernel_src_sha256_16") != h:
         return None
     if rec.get("workload") == workload:
         return rec.get("hbm_bytes_per_launch")
