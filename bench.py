@@ -41,7 +41,7 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_hash() -> str:
+def kernel_hash() -> str | None:
     try:
         return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()[:16]
     except OSError:  # a tree with the built library but not its source: no counter figure applies
