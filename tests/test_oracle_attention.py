@@ -120,3 +120,33 @@ def test_needle_workload_keeps_needles():
             for g in range(w.Hkv) for j in info["needles"][(0, g)]]
     assert np.mean(hits) > 0.75  # needle max ~ 6 + 2.5 vs threshold ~ 12.5 - 5: most pass
     assert res["keep"].mean() < 0.3
+
+
+@pytest.mark.parametrize("n_parts", [2, 3, 7])
+def test_split_combine_of_disjoint_parts_equals_one_pass(n_parts):
+    """The split-KV combine (FlashDecoding, Sec. 2 of the paper): attention over a set of blocks
+    equals the log-sum-exp merge of attention over any partition of it into disjoint parts,
+    lse = ln sum_s e^(lse_s) and o = sum_s e^(lse_s - lse) o_s.  Checked for the dense set and
+    for a sparse kept set, with the parts taken from the oracle's own attention over masks."""
+    w = W.small("t", B=1, Hq=4, Hkv=1, L=9 * 64 + 21, T=64, dtype="bf16", seed=40 + n_parts)
+    q, K, V, _ = W.make_inputs(w)
+    nb = (w.L + w.T - 1) // w.T
+    rng = np.random.default_rng(n_parts)
+    for h in range(w.Hq):
+        for keep_all in (np.ones(nb, np.uint8), (rng.random(nb) < 0.5).astype(np.uint8)):
+            keep_all[0] = 1  # a non-empty set
+            o_ref, lse_ref = oracle.attend_head(q[0, h], K[0, 0], V[0, 0], w.L, w.T, keep_all)
+            part = rng.integers(0, n_parts, nb)
+            outs, lses = [], []
+            for s in range(n_parts):
+                ks = (keep_all * (part == s)).astype(np.uint8)
+                if not ks.any():
+                    continue
+                o_s, l_s = oracle.attend_head(q[0, h], K[0, 0], V[0, 0], w.L, w.T, ks)
+                outs.append(o_s)
+                lses.append(l_s)
+            lses = np.array(lses)
+            lse = float(np.log(np.exp(lses - lses.max()).sum()) + lses.max())
+            o = sum(np.exp(l_s - lse) * o_s for o_s, l_s in zip(outs, lses))
+            assert abs(lse - lse_ref) <= 1e-12
+            np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
