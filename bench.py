@@ -248,8 +248,10 @@ def run_workload(w, delta: float, steps: int, warmup: int, min_rotation_mib: int
     Kq, sc = ffd.alloc_kq(Kd, w.T)
     stream = torch.cuda.current_stream()
 
-    # quantize (append of the whole cache): off the per-step path, timed for reference
+    # quantize (append of the whole cache): off the per-step path, timed for reference on a
+    # second, identical call (the first one also loads the kernels' code)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ffd.quantize_k_append(Kd, 0, w.L, w.T, Kq, sc, seq_len=w.L)
     ev0.record(stream)
     ffd.quantize_k_append(Kd, 0, w.L, w.T, Kq, sc, seq_len=w.L)
     ev1.record(stream)
@@ -385,6 +387,7 @@ def run_workload(w, delta: float, steps: int, warmup: int, min_rotation_mib: int
         del reps
         torch.cuda.empty_cache()
         kres = ffd.alloc_kres(Kd, w.T, bits)
+        ffd.quantize_k_residual_append(Kd, 0, w.L, w.T, bits, kres, seq_len=w.L)
         ev0.record(stream)
         ffd.quantize_k_residual_append(Kd, 0, w.L, w.T, bits, kres, seq_len=w.L)
         ev1.record(stream)

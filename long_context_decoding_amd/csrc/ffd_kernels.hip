@@ -1316,19 +1316,77 @@ __device__ __forceinline__ void quantize_block(QuantParams p, int bg, int j, int
     }
 }
 
+// App. A quantizer of whole blocks: one work-group of 256 threads per (b, kv head, block).
+// Thread (rg, cg) = (t / 16, t % 16) loads channels 8 cg .. 8 cg + 7 of rows rg, rg + 16, ...
+// (16-byte loads, 16 threads per row), takes their absolute maxima over its rows, and the
+// per-channel maxima over the 16 row groups meet in LDS.  It then writes the codes of its eight
+// channels of each of its rows as one 4-byte word (low nibble = even channel).  The arithmetic is
+// quantize_block's, so the codes and scales are the same bytes: s = RN(amax / 7.5),
+// u = clamp(floor(RN(x * RN(7.5 / amax))) + 8, 0, 15), and u = 8 for an all-zero channel (its
+// stored reciprocal is 0).
 template <int T, bool BF16>
-__global__ __launch_bounds__(128) void quantize_kernel(QuantParams p)
+__global__ __launch_bounds__(256) void quantize_kernel(QuantParams p)
 {
-    quantize_block<T, BF16>(p, blockIdx.y, p.j_first + blockIdx.x, threadIdx.x);
+    constexpr int RPT = T / 16;  // rows per thread
+    __shared__ float part[16][D];
+    __shared__ float inv_s[D];
+    const int t = threadIdx.x, rg = t >> 4, cg = t & 15;
+    const int bg = blockIdx.y, j = p.j_first + blockIdx.x;
+    const size_t row0 = (size_t)bg * p.cap + (size_t)j * T;
+    float x[RPT][8];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const size_t e0 = (row0 + rg + 16 * r) * D + cg * 8;
+        if constexpr (BF16) {
+            const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const unsigned short*>(p.K) + e0);
+            x[r][0] = bf16_lo(v.x); x[r][1] = bf16_hi(v.x);
+            x[r][2] = bf16_lo(v.y); x[r][3] = bf16_hi(v.y);
+            x[r][4] = bf16_lo(v.z); x[r][5] = bf16_hi(v.z);
+            x[r][6] = bf16_lo(v.w); x[r][7] = bf16_hi(v.w);
+        } else {
+            const float4* fp = reinterpret_cast<const float4*>(static_cast<const float*>(p.K) + e0);
+            const float4 a = fp[0], b = fp[1];
+            x[r][0] = a.x; x[r][1] = a.y; x[r][2] = a.z; x[r][3] = a.w;
+            x[r][4] = b.x; x[r][5] = b.y; x[r][6] = b.z; x[r][7] = b.w;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float am = 0.0f;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) am = fmaxf(am, fabsf(x[r][i]));
+        part[rg][cg * 8 + i] = am;
+    }
+    __syncthreads();
+    if (t < D) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) amax = fmaxf(amax, part[g][t]);
+        float s = 0.0f, inv = 0.0f;
+        if (amax > 0.0f) {
+            s = __fdiv_rn(amax, 7.5f);
+            inv = __fdiv_rn(7.5f, amax);
+        }
+        p.scales[((size_t)bg * (p.cap / T) + j) * D + t] = s;
+        inv_s[t] = inv;
+    }
+    __syncthreads();
+    float iv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) iv[i] = inv_s[cg * 8 + i];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        u32 word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            int u = (int)floorf(__fmul_rn(x[r][i], iv[i])) + 8;
+            u = min(max(u, 0), 15);
+            word |= (u32)u << (4 * i);
+        }
+        *reinterpret_cast<u32*>(p.Kq + (row0 + rg + 16 * r) * (D / 2) + cg * 4) = word;
+    }
 }
 
-// ------------------------------------------------------------------------------------------
-// Decode-loop cache update, one work-group of 128 threads (one per channel) per (b, kv head):
-// the new token's key and value go to position seq_lens[b]; when that token completes a key
-// block, the block is quantized right away (the key copy is maintained at block boundaries,
-// Fig. 2).  A sequence already at the capacity is left as it is.  The lengths advance in a
-// separate launch, after every (b, kv head) of the step has read them.
-// ------------------------------------------------------------------------------------------
 // One decode-loop step of the cache, in one launch.  One work-group per sequence b; thread
 // (gi, c) handles channel c of kv heads g = gi, gi + nh, ... (nh = blockDim.x / d): the new key and
 // value rows go to position seq_lens[b], and the key block they complete, if any, is quantized
@@ -1887,7 +1945,7 @@ hipError_t launch_append(const AppendParams& p, bool bf16, hipStream_t stream)
 hipError_t launch_quantize(const QuantParams& p, bool bf16, hipStream_t stream)
 {
     if (p.n_blocks <= 0) return hipSuccess;
-    const dim3 grid(p.n_blocks, p.B * p.Hkv), block(D);
+    const dim3 grid(p.n_blocks, p.B * p.Hkv), block(256);
     if (p.T == 64) {
         if (bf16) hipLaunchKernelGGL((quantize_kernel<64, true>), grid, block, 0, stream, p);
         else hipLaunchKernelGGL((quantize_kernel<64, false>), grid, block, 0, stream, p);
