@@ -1442,57 +1442,117 @@ __global__ __launch_bounds__(kAppendHeads * 128) void append_kernel(AppendParams
 // r_q = clamp(rint(RN(r * RN(127 / max|r|))), -127, 127).
 // ------------------------------------------------------------------------------------------
 template <int T, int BITS>
-__global__ __launch_bounds__(128) void quantize_res_kernel(QuantParams p)
+__global__ __launch_bounds__(256) void quantize_res_kernel(QuantParams p)
 {
+    // one 256-thread work-group per (block, b g): thread (rg, cg) = (t / 16, t % 16) holds
+    // channels 8 cg .. 8 cg + 7 of rows rg, rg + 16, ... (16-byte loads); the per-channel maxima
+    // of the keys and then of the residuals meet in LDS; an all-zero channel gets reciprocal 0,
+    // which gives the same codes (the middle one) as the per-channel form
     constexpr float half = (float)((1 << BITS) - 1) * 0.5f;
     constexpr int top = (1 << BITS) - 1;
+    constexpr int RPT = T / 16;  // rows per thread
+    __shared__ float part[16][D];
+    __shared__ float sc_s[D], sc_inv[D];
+    const int t = threadIdx.x, rg = t >> 4, cg = t & 15;
     const int j = p.j_first + blockIdx.x;
     const int bg = blockIdx.y;
-    const int c = threadIdx.x;
     const size_t row0 = (size_t)bg * p.cap + (size_t)j * T;
-    const unsigned short* Kb = static_cast<const unsigned short*>(p.K);
-    float x[T];
-    float amax = 0.0f;
+    const size_t srow = ((size_t)bg * (p.cap / T) + j) * D;
+    float x[RPT][8];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        x[t] = as_f((int)((u32)Kb[(row0 + t) * D + c] << 16));
-        amax = fmaxf(amax, fabsf(x[t]));
+    for (int r = 0; r < RPT; ++r) {
+        const uint4 v = *reinterpret_cast<const uint4*>(
+            static_cast<const unsigned short*>(p.K) + (row0 + rg + 16 * r) * D + cg * 8);
+        x[r][0] = bf16_lo(v.x); x[r][1] = bf16_hi(v.x);
+        x[r][2] = bf16_lo(v.y); x[r][3] = bf16_hi(v.y);
+        x[r][4] = bf16_lo(v.z); x[r][5] = bf16_hi(v.z);
+        x[r][6] = bf16_lo(v.w); x[r][7] = bf16_hi(v.w);
     }
-    float s = 0.0f, inv = 0.0f;
-    if (amax > 0.0f) {
-        s = __fdiv_rn(amax, half);
-        inv = __fdiv_rn(half, amax);
-    }
-    // codes, and the residual in place of x
-    int u[T];
-    float ramax = 0.0f;
+    // 1. the thumbnail scale of each channel
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        int v = 1 << (BITS - 1);
-        if (amax > 0.0f) v = min(max((int)floorf(__fmul_rn(x[t], inv)) + (1 << (BITS - 1)), 0), top);
-        u[t] = v;
-        x[t] = __fsub_rn(x[t], __fmul_rn((float)v - half, s));
-        ramax = fmaxf(ramax, fabsf(x[t]));
-    }
-    float s_r = 0.0f, inv_r = 0.0f;
-    if (ramax > 0.0f) {
-        s_r = __fdiv_rn(ramax, 127.0f);
-        inv_r = __fdiv_rn(127.0f, ramax);
-    }
-    const size_t srow = ((size_t)bg * (p.cap / T) + j) * D + c;
-    p.scales[srow] = s;
-    p.res_scales[srow] = s_r;
-    constexpr int per = 8 / BITS;
+    for (int i = 0; i < 8; ++i) {
+        float am = 0.0f;
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        float rq = 0.0f;
-        if (ramax > 0.0f) rq = fminf(fmaxf(rintf(__fmul_rn(x[t], inv_r)), -127.0f), 127.0f);
-        p.Kr[(row0 + t) * D + c] = (int8_t)(int)rq;
-        // channel c's code sits at bit (c % per) * BITS of byte c / per
-        int byte = u[t];
+        for (int r = 0; r < RPT; ++r) am = fmaxf(am, fabsf(x[r][i]));
+        part[rg][cg * 8 + i] = am;
+    }
+    __syncthreads();
+    if (t < D) {
+        float amax = 0.0f;
 #pragma unroll
-        for (int i = 1; i < per; ++i) byte |= __shfl_down(u[t], i, per) << (i * BITS);
-        if (c % per == 0) p.Kq[(row0 + t) * (D * BITS / 8) + c / per] = (uint8_t)byte;
+        for (int g = 0; g < 16; ++g) amax = fmaxf(amax, part[g][t]);
+        float sv = 0.0f, inv = 0.0f;
+        if (amax > 0.0f) {
+            sv = __fdiv_rn(amax, half);
+            inv = __fdiv_rn(half, amax);
+        }
+        p.scales[srow + t] = sv;
+        sc_s[t] = sv;
+        sc_inv[t] = inv;
+    }
+    __syncthreads();
+    // 2. codes, the residual in place of x, and the residual scale of each channel
+    int u[RPT][8];
+    {
+        float sv[8], iv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            sv[i] = sc_s[cg * 8 + i];
+            iv[i] = sc_inv[cg * 8 + i];
+        }
+        float rm[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rm[i] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int v = min(max((int)floorf(__fmul_rn(x[r][i], iv[i])) + (1 << (BITS - 1)), 0),
+                                  top);
+                u[r][i] = v;
+                x[r][i] = __fsub_rn(x[r][i], __fmul_rn((float)v - half, sv[i]));
+                rm[i] = fmaxf(rm[i], fabsf(x[r][i]));
+            }
+        // part[] was last read before the previous barrier
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part[rg][cg * 8 + i] = rm[i];
+    }
+    __syncthreads();
+    if (t < D) {
+        float ramax = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) ramax = fmaxf(ramax, part[g][t]);
+        float s_r = 0.0f, inv_r = 0.0f;
+        if (ramax > 0.0f) {
+            s_r = __fdiv_rn(ramax, 127.0f);
+            inv_r = __fdiv_rn(127.0f, ramax);
+        }
+        p.res_scales[srow + t] = s_r;
+        sc_inv[t] = inv_r;
+    }
+    __syncthreads();
+    // 3. the 8-bit residual codes (8 bytes per row) and the packed thumbnail codes (channel i of
+    // the eight at bit i * BITS of a 4- or 2-byte word)
+    float ir[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ir[i] = sc_inv[cg * 8 + i];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const size_t row = row0 + rg + 16 * r;
+        u32 rq_lo = 0, rq_hi = 0, code = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float rq = fminf(fmaxf(rintf(__fmul_rn(x[r][i], ir[i])), -127.0f), 127.0f);
+            const u32 byte = (u32)(uint8_t)(int8_t)(int)rq;
+            if (i < 4) rq_lo |= byte << (8 * i);
+            else rq_hi |= byte << (8 * (i - 4));
+            code |= (u32)u[r][i] << (i * BITS);
+        }
+        *reinterpret_cast<uint2*>(p.Kr + row * D + cg * 8) = make_uint2(rq_lo, rq_hi);
+        if constexpr (BITS == 4)
+            *reinterpret_cast<u32*>(p.Kq + row * (D / 2) + cg * 4) = code;
+        else
+            *reinterpret_cast<uint16_t*>(p.Kq + row * (D / 4) + cg * 2) = (uint16_t)code;
     }
 }
 
@@ -1906,7 +1966,7 @@ hipError_t launch_decode_res(const DecodeParams& p, int bits, hipStream_t stream
 hipError_t launch_quantize_res(const QuantParams& p, int bits, hipStream_t stream)
 {
     if (p.n_blocks <= 0) return hipSuccess;
-    const dim3 grid(p.n_blocks, p.B * p.Hkv), block(D);
+    const dim3 grid(p.n_blocks, p.B * p.Hkv), block(256);
     if (p.T == 64) {
         if (bits == 2) hipLaunchKernelGGL((quantize_res_kernel<64, 2>), grid, block, 0, stream, p);
         else hipLaunchKernelGGL((quantize_res_kernel<64, 4>), grid, block, 0, stream, p);
