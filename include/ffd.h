@@ -10,7 +10,7 @@
  *   4. runs exact softmax(q K^T / sqrt(d)) V over the kept blocks only (Alg. 1, refinement), and
  *   5. merges the per-split partial softmax states with a log-sum-exp combine (the split-KV
  *      decoding of Sec. 2, FlashDecoding).  Steps 1-5 run in one kernel launch; the merge is done
- *      by the last work-group of each (sequence, kv head) to finish.
+ *      by the last work-group of each work unit (query heads of one kv head) to finish.
  *
  * Conventions shared by every call
  *   - All tensors are dense, row-major, contiguous device allocations owned by the caller.
@@ -26,6 +26,12 @@
  *         lse      [B, Hq]                fp32, natural log of the softmax denominator
  *         keep_mask[B, Hq, ceil(L/T)]     uint8, 1 = block used for that query head
  *     Query head h reads kv head h / (Hq/Hkv) (contiguous groups).
+ *   - Query groups: any G = Hq/Hkv >= 1 (Llama-3's 4, Qwen2.5's 7, ...).  A kernel works on a
+ *     unit of G_u query heads of one kv head, G_u = 1, 2, 4 or 8, the narrowest that holds G;
+ *     other group sizes run padded (3 as 4; 5, 6 and 7 as 8): the padding heads cost arithmetic
+ *     but no memory traffic.  Groups of more than 8 are cut into ceil(G/8) units of 8, each of
+ *     which reads the kv head's keys (and scans them) on its own.  Units = B * Hkv * ceil(G/8)
+ *     must not exceed 65535.
  *   - Calls are asynchronous on `stream` and never synchronize.  They are thread-safe: no
  *     mutable global state.  No C++ exception crosses the ABI.
  *   - Argument validation runs before any HIP call: on failure a call returns
@@ -67,7 +73,7 @@ typedef enum {
     FFD_OK = 0,
     FFD_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, NaN/negative delta */
     FFD_ERR_UNSUPPORTED = 2, /* valid but not implemented: head_dim != 128, block not 64/128,
-                                Hq/Hkv not in {1, 2, 4, 8} */
+                                more than 65535 work units (see "Query groups") */
     FFD_ERR_WORKSPACE = 3,   /* workspace missing or smaller than ffd_workspace_bytes() */
     FFD_ERR_HIP = 4          /* the HIP runtime reported an error for a launch */
 } ffd_status;
@@ -104,10 +110,10 @@ ffd_status ffd_quantize_k_append(const ffd_dims* dims, const void* K, int32_t to
  *   out, lse   results; lse may be NULL.
  *   keep_mask  optional (NULL) per-(b, query head, block) selection, written as 0/1.
  *   workspace  caller-owned device memory of at least ffd_workspace_bytes(dims, block) bytes,
- *              prepared once by ffd_workspace_init (for the same dims and block); it holds a
- *              counter per (sequence, kv head), which every call returns to zero, and the
- *              per-split partial softmax states.  Calls that share a workspace must not overlap
- *              in time (run them on one stream).
+ *              prepared once by ffd_workspace_init; it holds a counter per work unit (see
+ *              "Query groups"), which every call returns to zero, and the per-split partial
+ *              softmax states.  Calls that share a workspace must not overlap in time (run them
+ *              on one stream).
  */
 ffd_status ffd_decode_sparse(const ffd_dims* dims, const void* q, const void* K, const void* V,
                              const uint8_t* Kq, const float* scales, float delta, int32_t block,
@@ -276,11 +282,13 @@ size_t ffd_workspace_bytes_window(const ffd_dims* dims, int32_t block, int32_t w
  * environment variable FFD_NUM_SPLITS (a positive integer) overrides. */
 size_t ffd_workspace_bytes(const ffd_dims* dims, int32_t block);
 
-/* Prepares a workspace for the decode calls: zeroes its per-(sequence, kv head) counters (the
- * first 8 * batch * n_kv_heads bytes, rounded up to 256) with a small kernel on `stream` (no
- * memset, so it may be recorded into a graph).  FFD_ERR_WORKSPACE if workspace_bytes is smaller
- * than that region; each decode call checks its own size.  Needed once per new allocation; a
- * completed decode call leaves the workspace prepared. */
+/* Prepares a workspace for the decode calls: zeroes its counter region (the first 524,288
+ * bytes: one 8-byte counter for each of the at most 65535 work units of a call, rounded up to
+ * 256) with a small kernel on `stream` (no memset, so it may be recorded into a graph).
+ * FFD_ERR_WORKSPACE if workspace_bytes is smaller than that region; each decode call checks its
+ * own size.  Needed once per new allocation: every completed decode call returns the counters it
+ * used to zero, so a prepared workspace stays prepared for later calls with any dims and block it
+ * is large enough for (dims and block are validated but do not change what is zeroed). */
 ffd_status ffd_workspace_init(const ffd_dims* dims, int32_t block, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 

@@ -16,8 +16,19 @@ using ffd::kWaves;
 
 // the ranked selection rules sort a row of block scores in LDS (8-byte keys)
 constexpr int kMaxRankedBlocks = 16384;
+// work units per call: a grid dimension of the score kernel, and the workspace's counter slots
+constexpr int64_t kMaxUnits = 65535;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Work units: the G = Hq / Hkv query heads of a kv head are handled G_unit at a time, G_unit
+// being the narrowest kernel width (1, 2, 4, 8) that holds them, or 8 with several units per kv
+// head for groups of more than 8 (each unit then reads the kv head's keys and values itself).
+int group_of(const ffd_dims* d) { return d->n_q_heads / d->n_kv_heads; }
+int64_t n_units(const ffd_dims* d)
+{
+    return (int64_t)d->batch * d->n_kv_heads * ffd::units_per_kv(group_of(d));
+}
 
 // Shape checks shared by every call.  `block` must be known (64/128) for the decode calls.
 ffd_status check_dims(const ffd_dims* d, int32_t block)
@@ -31,10 +42,9 @@ ffd_status check_dims(const ffd_dims* d, int32_t block)
     if (d->head_dim != kHeadDim) return FFD_ERR_UNSUPPORTED;
     if (block != 64 && block != 128) return FFD_ERR_UNSUPPORTED;
     if (d->seq_cap % block) return FFD_ERR_INVALID_ARG;
-    const int G = d->n_q_heads / d->n_kv_heads;
-    if (G != 1 && G != 2 && G != 4 && G != 8) return FFD_ERR_UNSUPPORTED;
-    // grid and table limits: at most kMaxSplits splits of at most kMaxBlocksPerSplit blocks
-    if ((int64_t)d->batch * d->n_kv_heads > 65535) return FFD_ERR_UNSUPPORTED;
+    // grid and table limits: at most 65535 work units (a grid dimension of the score kernel),
+    // at most kMaxSplits splits of at most kMaxBlocksPerSplit blocks
+    if (n_units(d) > kMaxUnits) return FFD_ERR_UNSUPPORTED;
     const int64_t n_blocks = ((int64_t)d->seq_len + block - 1) / block;
     if (n_blocks > (int64_t)kMaxSplits * kMaxBlocksPerSplit) return FFD_ERR_UNSUPPORTED;
     return FFD_OK;
@@ -43,7 +53,7 @@ ffd_status check_dims(const ffd_dims* d, int32_t block)
 int splits_for(const ffd_dims* d, int32_t block, bool sparse)
 {
     const int n_blocks = (d->seq_len + block - 1) / block;
-    const int64_t bh = (int64_t)d->batch * d->n_kv_heads;
+    const int64_t bh = n_units(d);
     const int min_s = (n_blocks + kMaxBlocksPerSplit - 1) / kMaxBlocksPerSplit;
     int64_t s;
     const char* env = getenv("FFD_NUM_SPLITS");
@@ -78,20 +88,24 @@ int splits_for(const ffd_dims* d, int32_t block, bool sparse)
     return (int)s;
 }
 
-// Workspace layout: counters [B*Hkv] u64 | ml [B*Hkv*S*G] float2 | o [B*Hkv*S*G*d] fp32,
-// each region starting on a 256-byte boundary.
+// Workspace layout: counters [kMaxUnits] u64 | ml [units*S*G_unit] float2 |
+// o [units*S*G_unit*d] fp32, each region starting on a 256-byte boundary.  The counter region has
+// a fixed size (one slot for every unit any call may have), so that a workspace prepared once
+// serves every later call whatever its dims: each call returns the slots it used to zero.
 struct WsLayout {
     size_t off_ml, off_o, total;
 };
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr size_t kCounterBytes = ((size_t)kMaxUnits * sizeof(unsigned long long) + 255) & ~(size_t)255;
+
 WsLayout ws_layout(const ffd_dims* d, int S)
 {
-    const size_t bh = (size_t)d->batch * d->n_kv_heads;
-    const size_t rec = bh * (size_t)S * (size_t)(d->n_q_heads / d->n_kv_heads);
+    const size_t bh = (size_t)n_units(d);
+    const size_t rec = bh * (size_t)S * (size_t)ffd::unit_heads(group_of(d));
     WsLayout w;
-    w.off_ml = round256(bh * sizeof(unsigned long long));
+    w.off_ml = kCounterBytes;
     w.off_o = w.off_ml + round256(rec * 2 * sizeof(float));
     w.total = w.off_o + rec * kHeadDim * sizeof(float);
     return w;
@@ -153,7 +167,9 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
     p.B = dims->batch;
     p.Hq = dims->n_q_heads;
     p.Hkv = dims->n_kv_heads;
-    p.G = dims->n_q_heads / dims->n_kv_heads;
+    p.G = group_of(dims);
+    p.GP = ffd::unit_heads(p.G);
+    p.NSUB = ffd::units_per_kv(p.G);
     p.L = dims->seq_len;
     p.cap = dims->seq_cap;
     p.T = block;
@@ -217,11 +233,11 @@ ffd_status ffd_workspace_init(const ffd_dims* dims, int32_t block, void* workspa
     if (st != FFD_OK) return st;
     if (dims->batch == 0) return FFD_OK;
     if (!workspace || !aligned16(workspace)) return FFD_ERR_WORKSPACE;
-    // only the counters are prepared: any workspace holding them qualifies (a decode call checks
-    // its own size requirement, which depends on its split count)
-    if (workspace_bytes < ws_layout(dims, 1).off_ml) return FFD_ERR_WORKSPACE;
+    // only the counters are prepared, all of their fixed region: any workspace holding it
+    // qualifies (a decode call checks its own size requirement, which depends on its dims)
+    if (workspace_bytes < kCounterBytes) return FFD_ERR_WORKSPACE;
     return finish(ffd::launch_zero_counters(static_cast<uint32_t*>(workspace),
-                                            2 * dims->batch * dims->n_kv_heads, stream));
+                                            (int)(kCounterBytes / sizeof(uint32_t)), stream));
 }
 
 int32_t ffd_num_splits(const ffd_dims* dims, int32_t block, int32_t sparse)
@@ -442,7 +458,9 @@ ffd_status ffd_block_scores(const ffd_dims* dims, int32_t kind, const void* q, c
     p.B = dims->batch;
     p.Hq = dims->n_q_heads;
     p.Hkv = dims->n_kv_heads;
-    p.G = dims->n_q_heads / dims->n_kv_heads;
+    p.G = group_of(dims);
+    p.GP = ffd::unit_heads(p.G);
+    p.NSUB = ffd::units_per_kv(p.G);
     p.cap = dims->seq_cap;
     p.T = block;
     p.n_full = dims->seq_len / block;

@@ -13,6 +13,13 @@ constexpr int kHeadDim = 128;
 constexpr int kWaves = 4;                  // waves per work-group of the decode kernels
 constexpr int kMaxBlocksPerSplit = 256;    // LDS sizing of the per-split block tables
 constexpr int kMaxSplits = 256;            // LDS sizing of the final split merge
+constexpr int kMaxUnitHeads = 8;           // query heads per work unit (the kernels' widest group)
+
+// Query heads per work unit for a group of G query heads per kv head: the narrowest kernel width
+// (1, 2, 4 or 8) that holds the group, or 8 for larger groups, which are cut into units of 8
+// heads (each unit reads the kv head's keys and values on its own).
+inline int unit_heads(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : kMaxUnitHeads; }
+inline int units_per_kv(int G) { return (G + kMaxUnitHeads - 1) / kMaxUnitHeads; }
 
 struct DecodeParams {
     const void* q;
@@ -25,12 +32,15 @@ struct DecodeParams {
     float* out;
     float* lse;
     uint8_t* keep_mask;
-    unsigned long long* counters;  // [B*Hkv] finished splits (high half) and, for S <= 32, a
+    unsigned long long* counters;  // [units] finished splits (high half) and, for S <= 32, a
                                    // mask of the splits with a partial (low half); zero between
                                    // calls
-    float2* part_ml;     // [B*Hkv][S][G] per-split (max in log2 units, sum of exp2)
-    float* part_o;       // [B*Hkv][S][G][d] per-split unnormalized output
-    int B, Hq, Hkv, G;
+    float2* part_ml;     // [units][S][GP] per-split (max in log2 units, sum of exp2)
+    float* part_o;       // [units][S][GP][d] per-split unnormalized output
+    int B, Hq, Hkv, G;   // G = Hq / Hkv query heads per kv head (any value)
+    int GP, NSUB;        // query heads per work unit (the kernel's width: 1, 2, 4 or 8; the
+                         // unit's last heads are padding when G is not a multiple) and units per
+                         // kv head; units = B * Hkv * NSUB, counters and partials are per unit
     int L, cap, T;
     int n_full, n_blocks;
     int S, R;       // splits per (b, kv head), blocks per split
@@ -90,6 +100,7 @@ struct ScoreParams {
     const void* kmax;
     float* scores;  // [B][Hq][n_full]
     int B, Hq, Hkv, G, cap, T, n_full;
+    int GP, NSUB;      // as DecodeParams
     float kappa;       // as DecodeParams
     float inv_sqrt_d;  // (float)(1 / sqrt(d))
 };

@@ -719,22 +719,28 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
     const int w = threadIdx.x >> 6;
     const int col = lane & 15, kg = lane >> 4;
 
-    // work-group -> (b, kv head, split).  Sparse: the S splits of one (b, g) are consecutive
-    // work-groups, which the dispatcher deals round-robin to the XCDs, so every XCD holds
-    // splits of every (b, g) and the exact work of a (b, g) that keeps many blocks is spread
-    // over all of them.  Ranks 0 and 1 are the splits holding the sink (0) and the local block
-    // (S-1), which always carry exact work; the ranks of (b, g) start at work-group offset
-    // S - bg mod S, so that these forced splits of different (b, g) fall on different XCDs.
-    // Dense (the same work in every split): all splits of one (b, g) share blockIdx.x mod
-    // (B*Hkv), one XCD when B*Hkv is a multiple of 8.  Each layout measured faster than the
-    // other for its kernel.
-    const int bh = p.B * p.Hkv;
+    // work-group -> (unit, split).  A unit is G query heads (the kernel's width) of one (b, kv
+    // head): the whole group, its padded form, or one of several slices of a group wider than
+    // the kernel.  Sparse: the S splits of one unit are consecutive work-groups, which the
+    // dispatcher deals round-robin to the XCDs, so every XCD holds splits of every unit and the
+    // exact work of a unit that keeps many blocks is spread over all of them.  Ranks 0 and 1
+    // are the splits holding the sink (0) and the local block (S-1), which always carry exact
+    // work; the ranks of a unit start at work-group offset S - unit mod S, so that these forced
+    // splits of different units fall on different XCDs.  Dense (the same work in every split):
+    // all splits of one unit share blockIdx.x mod units, one XCD when the unit count is a
+    // multiple of 8.  Each layout measured faster than the other for its kernel.
+    const int n_units = p.B * p.Hkv * p.NSUB;
     const int id = blockIdx.x;
-    const int bg = SPARSE ? id / p.S : id % bh;
-    const int rank = SPARSE ? (id % p.S + bg) % p.S : id / bh;
+    const int unit = SPARSE ? id / p.S : id % n_units;
+    const int rank = SPARSE ? (id % p.S + unit) % p.S : id / n_units;
     int split = rank;
     if (SPARSE && p.S > 1) split = rank == 0 ? 0 : (rank == 1 ? p.S - 1 : rank - 1);
+    const int bg = unit / p.NSUB;  // (b, kv head) whose keys and values the unit reads
+    const int sub = unit % p.NSUB;
     const int b = bg / p.Hkv, g = bg % p.Hkv;
+    // real query heads of the unit: the first nh of its G; the others are padding, with a zero
+    // query in the exact stage, never kept and never written
+    const int nh = min(G, p.G - sub * G);
     // this sequence's length: the common one, or (decode loops) its own from device memory
     int L_b = p.L;
     if (p.seq_lens) L_b = min(max(p.seq_lens[b], 0), p.L);
@@ -747,21 +753,24 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
     const size_t kv_off = (size_t)bg * p.cap * D;
     const char* Kbg = p.K ? static_cast<const char*>(p.K) + kv_off * esz : nullptr;
     const char* Vbg = static_cast<const char*>(p.V) + kv_off * esz;
-    const int h0 = b * p.Hq + g * G;  // first query row of the group
+    const int h0 = b * p.Hq + g * p.G + sub * G;  // first query row of the unit
 
     WaveScratch<G>& ws = sh.wave[w];
     constexpr int NT = T / 16;
     int n_kept;
 
-    // the group's G query rows (at most 16 bytes per thread), copied to LDS once the first scan
-    // loads are in flight; the load is unconditional (clamped index) so that it is issued
-    // before them and the copy waits only for itself
-    constexpr int kQ16 = (int)(G * D * (BF16 ? 2 : 4) / 16);
+    // the unit's query rows (at most 16 bytes per thread), copied to LDS once the first scan
+    // loads are in flight; the load is unconditional (clamped index, inside the real rows) so
+    // that it is issued before them and the copy waits only for itself; padding rows are zero
+    constexpr int kRow16 = (int)(D * (BF16 ? 2 : 4) / 16);
+    constexpr int kQ16 = G * kRow16;
     static_assert(kQ16 <= NW * 64, "query rows exceed one 16-byte load per thread");
+    const int q16_real = nh * kRow16;
     const float4 qcopy = reinterpret_cast<const float4*>(
-        static_cast<const char*>(p.q) + (size_t)h0 * D * esz)[min((int)threadIdx.x, kQ16 - 1)];
+        static_cast<const char*>(p.q) + (size_t)h0 * D * esz)[min((int)threadIdx.x, q16_real - 1)];
     auto publish_q = [&]() {
-        if ((int)threadIdx.x < kQ16) sh.q[threadIdx.x] = qcopy;
+        if ((int)threadIdx.x < kQ16)
+            sh.q[threadIdx.x] = (int)threadIdx.x < q16_real ? qcopy : make_float4(0.f, 0.f, 0.f, 0.f);
     };
 
     if constexpr (SPARSE) {
@@ -771,7 +780,7 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
     #pragma unroll
             for (int k = 0; k < HPL; ++k) {
                 const int h = (G >= 4) ? (kg + 4 * k) : (kg % G);
-                const int hq = h0 + h;
+                const int hq = h0 + min(h, nh - 1);  // a padding head scans a real head's row
                 if constexpr (BF16) {
                     const uint4 x = *reinterpret_cast<const uint4*>(
                         static_cast<const __bf16*>(p.q) + (size_t)hq * D + col * 8);
@@ -791,7 +800,7 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
             const uint8_t* kq_bg = p.Kq + (size_t)bg * p.cap * (D * BITS / 8);
             const float* sc_bg = p.scales + (size_t)bg * (p.cap / T) * D;
             const int nf = nf_b;
-            const u32 all_heads = (1u << G) - 1u;
+            const u32 all_heads = (1u << nh) - 1u;
             // Forced blocks of the split (sink 0, the local block nf-1 and a partial tail) are kept
             // for every head; every other block of the split is a scan item of exactly one wave.
             if (w == 0) {
@@ -800,8 +809,7 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
                     if (j == 0 || j >= nf - 1) {
                         sh.kbits[t] = (uint8_t)all_heads;
                         if (p.keep_mask)
-    #pragma unroll
-                            for (int h = 0; h < G; ++h) p.keep_mask[(size_t)(h0 + h) * p.mask_stride + j] = 1;
+                            for (int h = 0; h < nh; ++h) p.keep_mask[(size_t)(h0 + h) * p.mask_stride + j] = 1;
                     } else if (p.running) {
                         sh.kbits[t] = 0;  // decided after the scan
                     }
@@ -841,10 +849,10 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
                     } else {
                         // selection, Eq. 1 with the pseudo-max: shat >= mtilde - delta
                         const int j = block_of(k);
-                        const bool keep = lane < G && shat >= theta;
+                        const bool keep = lane < nh && shat >= theta;
                         const u32 bits = (u32)__ballot(keep) & all_heads;
                         if (lane == 0) sh.kbits[j - jb] = (uint8_t)bits;
-                        if (p.keep_mask && lane < G)
+                        if (p.keep_mask && lane < nh)
                             p.keep_mask[(size_t)(h0 + lane) * p.mask_stride + j] = keep ? 1 : 0;
                     }
                 };
@@ -883,8 +891,7 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
             // the caller's keep mask; nothing is scanned
             for (int t = threadIdx.x; t < je - jb; t += NW * 64) {
                 u32 bits = 0;
-#pragma unroll
-                for (int h = 0; h < G; ++h)
+                for (int h = 0; h < nh; ++h)
                     bits |= (p.ext_mask[(size_t)(h0 + h) * p.mask_stride + jb + t] != 0 ? 1u : 0u)
                             << h;
                 sh.kbits[t] = (uint8_t)bits;
@@ -899,7 +906,7 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
             // estimates of the split's earlier scanned blocks.  One wave per head, 64 blocks at a
             // time: an exclusive prefix maximum over the lanes plus the earlier chunks' maximum.
             const int nf = nf_b;
-            for (int h = w; h < G; h += NW) {
+            for (int h = w; h < nh; h += NW) {
                 float carry = sh.u.run.mt[h];
                 for (int base = 0; base < je - jb; base += 64) {
                     const int t = base + lane;
@@ -979,7 +986,7 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
                     kb = sh.kbits[off];
                 } else {
                     off = kk;
-                    kb = 0xFFu;
+                    kb = (1u << nh) - 1u;
                 }
                 t0 = (jb + off) * T + (it % NT) * 16;
             };
@@ -1058,13 +1065,13 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
         }
     }
     __syncthreads();
-    const size_t rec0 = ((size_t)bg * p.S + split) * G;
+    const size_t rec0 = ((size_t)unit * p.S + split) * G;
     const bool fast = p.S <= 32;  // the counter word can carry a mask of the non-empty splits
     if (n_kept > 0) {
-        // one 16-byte store per four channels of a head, (m, l) with the first four
+        // one 16-byte store per four channels of a real head, (m, l) with the first four
         const rsrc_t ro = dev_rsrc(p.part_o + rec0 * D, G * D * 4);
         const rsrc_t rml = dev_rsrc(p.part_ml + rec0, G * 8);
-        for (int e = threadIdx.x; e < G * (D / 4); e += NW * 64) {
+        for (int e = threadIdx.x; e < nh * (D / 4); e += NW * 64) {
             const int h = e / (D / 4), c = (e % (D / 4)) * 4;
             float M = kNegInf;
 #pragma unroll
@@ -1083,7 +1090,7 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
             st_dev16(ro, e * 16, o);
             if (c == 0) st_dev8(rml, h * 8, M, l);
         }
-    } else if (!fast && threadIdx.x < G) {
+    } else if (!fast && (int)threadIdx.x < nh) {
         st_dev2(&p.part_ml[rec0 + threadIdx.x], kNegInf, 0.0f);
     }
 
@@ -1099,16 +1106,16 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
         const unsigned long long add =
             (1ull << 32) | ((fast && n_kept > 0) ? (1ull << split) : 0ull);
         const unsigned long long old = __hip_atomic_fetch_add(
-            &p.counters[bg], add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            &p.counters[unit], add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sh.is_last = (u32)(old >> 32) == (u32)(p.S - 1);
         sh.mask = (u32)(old | add);
     }
     __syncthreads();
     if (!sh.is_last) return;
     if (threadIdx.x == 0)  // ready for the next call
-        __hip_atomic_store(&p.counters[bg], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.counters[unit], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-    const size_t base = (size_t)bg * p.S * G;
+    const size_t base = (size_t)unit * p.S * G;
     if (fast) {
         // Thread (part, e) merges four channels e of one head over a share of the non-empty
         // splits: those of rank part, part + P, ... among them, in increasing split order, read
@@ -1121,7 +1128,8 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
         constexpr int kMB = P == 1 ? 16 : 8;
         const int e = (int)threadIdx.x % NE4, part = (int)threadIdx.x / NE4;
         const int h = e / (D / 4), c = (e % (D / 4)) * 4;
-        u32 mine = sh.mask;
+        const bool real = h < nh;  // padding heads read and write nothing
+        u32 mine = real ? sh.mask : 0u;
         if constexpr (P > 1) {
             u32 rest = mine;
             mine = 0u;
@@ -1203,6 +1211,7 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
             }
             M = Mb;
         }
+        if (!real) return;
         // an empty sequence (length 0) has no softmax: out = 0, lse = -inf
         v4f r;
 #pragma unroll
@@ -1214,7 +1223,7 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
     }
 
     // general path: (m, l) of every split first, then o of the non-empty ones
-    for (int h = w; h < G; h += NW) {
+    for (int h = w; h < nh; h += NW) {
         float M = kNegInf;
         for (int s = lane; s < p.S; s += 64)
             M = fmaxf(M, ld_dev2(&p.part_ml[base + (size_t)s * G + h]).x);
@@ -1248,7 +1257,7 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
         }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < G * D; e += NW * 64) {
+    for (int e = threadIdx.x; e < nh * D; e += NW * 64) {
         const int h = e / D, c = e % D;
         const int n = sh.u.fin.cnt[h];
         float acc = 0.0f;
@@ -1559,7 +1568,7 @@ __global__ __launch_bounds__(256) void quantize_res_kernel(QuantParams p)
 template <int T, int G, bool BF16>
 hipError_t launch_decode_t(const DecodeParams& p, bool sparse, hipStream_t stream)
 {
-    const dim3 grid(p.B * p.Hkv * p.S), block(kWaves * 64);
+    const dim3 grid(p.B * p.Hkv * p.NSUB * p.S), block(kWaves * 64);
     if (sparse)
         hipLaunchKernelGGL((decode_kernel<T, G, BF16, true, 4, false>), grid, block, 0, stream, p);
     else
@@ -1570,7 +1579,7 @@ hipError_t launch_decode_t(const DecodeParams& p, bool sparse, hipStream_t strea
 template <int T, bool BF16>
 hipError_t launch_decode_g(const DecodeParams& p, bool sparse, hipStream_t stream)
 {
-    switch (p.G) {
+    switch (p.GP) {
     case 1: return launch_decode_t<T, 1, BF16>(p, sparse, stream);
     case 2: return launch_decode_t<T, 2, BF16>(p, sparse, stream);
     case 4: return launch_decode_t<T, 4, BF16>(p, sparse, stream);
@@ -1582,8 +1591,8 @@ hipError_t launch_decode_g(const DecodeParams& p, bool sparse, hipStream_t strea
 template <int T, int BITS>
 hipError_t launch_res_g(const DecodeParams& p, hipStream_t stream)
 {
-    const dim3 grid(p.B * p.Hkv * p.S), block(kResWaves * 64);
-    switch (p.G) {
+    const dim3 grid(p.B * p.Hkv * p.NSUB * p.S), block(kResWaves * 64);
+    switch (p.GP) {
     case 1: hipLaunchKernelGGL((decode_kernel<T, 1, true, true, BITS, true>), grid, block, 0, stream, p); break;
     case 2: hipLaunchKernelGGL((decode_kernel<T, 2, true, true, BITS, true>), grid, block, 0, stream, p); break;
     case 4: hipLaunchKernelGGL((decode_kernel<T, 4, true, true, BITS, true>), grid, block, 0, stream, p); break;
@@ -1653,17 +1662,23 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(ScoreParams p)
     __shared__ float4 qs[G * D * (BF16 ? 2 : 4) / 16];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int col = lane & 15, kg = lane >> 4;
-    const int bg = blockIdx.y;
+    // blockIdx.y = work unit: G query heads (the kernel's width) of one (b, kv head), the last
+    // ones padding when the group is narrower (as in decode_kernel)
+    const int unit = blockIdx.y;
+    const int bg = unit / p.NSUB, sub = unit % p.NSUB;
     const int b = bg / p.Hkv, g = bg % p.Hkv;
-    const int h0 = b * p.Hq + g * G;
+    const int h0 = b * p.Hq + g * p.G + sub * G;
+    const int nh = min(G, p.G - sub * G);  // real heads of the unit
     const int j0 = blockIdx.x * kChunk;
     const int j1 = min(p.n_full, j0 + kChunk);
     const size_t esz = BF16 ? 2 : 4;
     if constexpr (KIND == 2) {
-        constexpr int kQ16 = G * D * (BF16 ? 2 : 4) / 16;
+        constexpr int kRow16 = D * (BF16 ? 2 : 4) / 16;
+        constexpr int kQ16 = G * kRow16;
         const float4* src =
             reinterpret_cast<const float4*>(static_cast<const char*>(p.q) + (size_t)h0 * D * esz);
-        for (int i = threadIdx.x; i < kQ16; i += kWaves * 64) qs[i] = src[i];
+        for (int i = threadIdx.x; i < kQ16; i += kWaves * 64)
+            qs[i] = i < nh * kRow16 ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
         __syncthreads();
     }
     if constexpr (KIND == 0) {
@@ -1671,7 +1686,7 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(ScoreParams p)
         float qw[HPL][8];
 #pragma unroll
         for (int k = 0; k < HPL; ++k) {
-            const int h = (G >= 4) ? (kg + 4 * k) : (kg % G);
+            const int h = min((G >= 4) ? (kg + 4 * k) : (kg % G), nh - 1);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 qw[k][i] = elem(p.q, (size_t)(h0 + h) * D + col * 8 + i, BF16);
@@ -1682,7 +1697,7 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(ScoreParams p)
             ScanRegs<T, 4> r;
             scan_load<T, 4>(r, kq_bg + (size_t)j * T * (D / 2), sc_bg + (size_t)j * D, lane);
             const float shat = scan_compute<T, G, 4>(r, qw, p.kappa, wsh[w], lane);
-            if (lane < G) p.scores[(size_t)(h0 + lane) * p.n_full + j] = shat;
+            if (lane < nh) p.scores[(size_t)(h0 + lane) * p.n_full + j] = shat;
         }
     } else if constexpr (KIND == 1) {
         const size_t mrow = (size_t)bg * (p.cap / T);
@@ -1692,7 +1707,7 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(ScoreParams p)
             const float mn1 = elem(p.kmin, mo + 2 * lane + 1, BF16);
             const float mx0 = elem(p.kmax, mo + 2 * lane, BF16);
             const float mx1 = elem(p.kmax, mo + 2 * lane + 1, BF16);
-            for (int h = 0; h < G; ++h) {
+            for (int h = 0; h < nh; ++h) {
                 const float q0 = elem(p.q, (size_t)(h0 + h) * D + 2 * lane, BF16);
                 const float q1 = elem(p.q, (size_t)(h0 + h) * D + 2 * lane + 1, BF16);
                 float x = fmaxf(__fmul_rn(q0, mn0), __fmul_rn(q0, mx0)) +
@@ -1733,7 +1748,7 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(ScoreParams p)
                 m = fmaxf(m, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
             }
             m = fmax32(fmax16(m));  // over the four token groups: column col = head col % G
-            if (kg == 0 && col < G) p.scores[(size_t)(h0 + col) * p.n_full + j] = m * p.inv_sqrt_d;
+            if (kg == 0 && col < nh) p.scores[(size_t)(h0 + col) * p.n_full + j] = m * p.inv_sqrt_d;
         }
     }
 }
@@ -2038,7 +2053,7 @@ namespace {
 template <int T, int G, bool BF16>
 void launch_scores_k(const ScoreParams& p, int kind, hipStream_t stream)
 {
-    const dim3 grid((p.n_full + 15) / 16, p.B * p.Hkv), block(kWaves * 64);
+    const dim3 grid((p.n_full + 15) / 16, p.B * p.Hkv * p.NSUB), block(kWaves * 64);
     if (kind == 0) hipLaunchKernelGGL((score_kernel<T, G, BF16, 0>), grid, block, 0, stream, p);
     else if (kind == 1) hipLaunchKernelGGL((score_kernel<T, G, BF16, 1>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((score_kernel<T, G, BF16, 2>), grid, block, 0, stream, p);
@@ -2046,7 +2061,7 @@ void launch_scores_k(const ScoreParams& p, int kind, hipStream_t stream)
 template <int T, bool BF16>
 hipError_t launch_scores_g(const ScoreParams& p, int kind, hipStream_t stream)
 {
-    switch (p.G) {
+    switch (p.GP) {
     case 1: launch_scores_k<T, 1, BF16>(p, kind, stream); break;
     case 2: launch_scores_k<T, 2, BF16>(p, kind, stream); break;
     case 4: launch_scores_k<T, 4, BF16>(p, kind, stream); break;

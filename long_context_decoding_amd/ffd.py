@@ -12,6 +12,7 @@ Names follow the C ABI: ``quantize_k_append``, ``decode_sparse``, ``decode_dense
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 from pathlib import Path
@@ -138,6 +139,13 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Context in which temporary buffers of a call on `stream` are allocated: torch's caching
+    allocator then ties them to that stream, so that their memory is not handed to other work
+    before the call's kernels on `stream` are done with it."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _need(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -160,29 +168,34 @@ def num_splits(dims: Dims, block: int, sparse: bool = True) -> int:
 
 
 def workspace_init(dims: Dims, block: int, workspace: torch.Tensor, stream=None) -> None:
-    """Prepare a workspace (zero its counters) on the current stream."""
+    """Prepare a workspace (zero its counters) on `stream` (default: the current stream)."""
     _need(workspace, "workspace", torch.uint8)
     _check(lib().ffd_workspace_init(ctypes.byref(dims), block, _ptr(workspace),
                                     workspace.numel(), _stream(stream)))
 
 
-def alloc_workspace(dims: Dims, block: int, device) -> torch.Tensor:
-    """A prepared workspace for decode calls with these dims and block."""
+def alloc_workspace(dims: Dims, block: int, device, stream=None) -> torch.Tensor:
+    """A workspace for decode calls with these dims and block, allocated for and prepared on
+    `stream` (default: the current stream)."""
     n = workspace_bytes(dims, block)
     if n == 0:
         raise FFDError(FFD_ERR_INVALID_ARG, "invalid dims for workspace")
-    ws = torch.empty(n, dtype=torch.uint8, device=device)
-    workspace_init(dims, block, ws)
+    with _on(stream):
+        ws = torch.empty(n, dtype=torch.uint8, device=device)
+        workspace_init(dims, block, ws)
     return ws
 
 
-def alloc_workspace_window(dims: Dims, block: int, window: int, device) -> torch.Tensor:
-    """A prepared workspace for decode_sparse_running with this window."""
+def alloc_workspace_window(dims: Dims, block: int, window: int, device,
+                           stream=None) -> torch.Tensor:
+    """A workspace for decode_sparse_running with this window, allocated for and prepared on
+    `stream`."""
     n = lib().ffd_workspace_bytes_window(ctypes.byref(dims), block, window)
     if n == 0:
         raise FFDError(FFD_ERR_UNSUPPORTED, "invalid dims or window for workspace")
-    ws = torch.empty(n, dtype=torch.uint8, device=device)
-    workspace_init(dims, block, ws)
+    with _on(stream):
+        ws = torch.empty(n, dtype=torch.uint8, device=device)
+        workspace_init(dims, block, ws)
     return ws
 
 
@@ -208,13 +221,15 @@ def quantize_k_append(K: torch.Tensor, tok_begin: int, tok_end: int, block: int,
                                        _ptr(Kq), _ptr(scales), _stream(stream)))
 
 
-def _decode_outputs(q, out, lse, want_lse):
+def _decode_outputs(q, out, lse, want_lse, stream=None):
     B, Hq, d = q.shape
     if out is None:
-        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        with _on(stream):
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.float32, (B, Hq, d), q.device)
     if lse is None and want_lse:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        with _on(stream):
+            lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     if lse is not None:
         _need(lse, "lse", torch.float32, (B, Hq), q.device)
     return out, lse
@@ -234,12 +249,12 @@ def decode_sparse(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, Kq: torch.T
     _need(Kq, "Kq", torch.uint8, (B, Hkv, cap, d // 2), K.device)
     _need(scales, "scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d),
           K.device)
-    out, lse = _decode_outputs(q, out, lse, want_lse)
+    out, lse = _decode_outputs(q, out, lse, want_lse, stream)
     if keep_mask is not None:
         _need(keep_mask, "keep_mask", torch.uint8,
               (q.shape[0], q.shape[1], math.ceil(seq_len / block)), q.device)
     if workspace is None:
-        workspace = alloc_workspace(dims, block, q.device)
+        workspace = alloc_workspace(dims, block, q.device, stream)
     _need(workspace, "workspace", torch.uint8, None, q.device)
     _check(lib().ffd_decode_sparse(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V), _ptr(Kq),
                                    _ptr(scales), float(delta), block, _ptr(out), _ptr(lse),
@@ -264,12 +279,12 @@ def decode_sparse_running(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, Kq:
     _need(Kq, "Kq", torch.uint8, (B, Hkv, cap, d // 2), K.device)
     _need(scales, "scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d),
           K.device)
-    out, lse = _decode_outputs(q, out, lse, want_lse)
+    out, lse = _decode_outputs(q, out, lse, want_lse, stream)
     if keep_mask is not None:
         _need(keep_mask, "keep_mask", torch.uint8,
               (q.shape[0], q.shape[1], math.ceil(seq_len / block)), q.device)
     if workspace is None:
-        workspace = alloc_workspace_window(dims, block, window, q.device)
+        workspace = alloc_workspace_window(dims, block, window, q.device, stream)
     _need(workspace, "workspace", torch.uint8, None, q.device)
     _check(lib().ffd_decode_sparse_running(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V),
                                            _ptr(Kq), _ptr(scales), float(delta), block,
@@ -286,9 +301,9 @@ def decode_dense(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, block: int, 
     for name, t in (("q", q), ("K", K), ("V", V)):
         _need(t, name, K.dtype, None, K.device)
     _need(V, "V", K.dtype, K.shape, K.device)
-    out, lse = _decode_outputs(q, out, lse, want_lse)
+    out, lse = _decode_outputs(q, out, lse, want_lse, stream)
     if workspace is None:
-        workspace = alloc_workspace(dims, block, q.device)
+        workspace = alloc_workspace(dims, block, q.device, stream)
     _need(workspace, "workspace", torch.uint8, None, q.device)
     _check(lib().ffd_decode_dense(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V), block,
                                   _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
@@ -346,12 +361,12 @@ def decode_sparse_residual(q: torch.Tensor, K_tail: torch.Tensor | None, V: torc
         _need(K_tail, "K_tail", torch.bfloat16, V.shape, V.device)
     Kc, sc, Kr, sr = kres
     _need_kres(V.shape, block, bits, Kc, sc, Kr, sr, V.device)
-    out, lse = _decode_outputs(q, out, lse, want_lse)
+    out, lse = _decode_outputs(q, out, lse, want_lse, stream)
     if keep_mask is not None:
         _need(keep_mask, "keep_mask", torch.uint8,
               (q.shape[0], q.shape[1], math.ceil(seq_len / block)), q.device)
     if workspace is None:
-        workspace = alloc_workspace(dims, block, q.device)
+        workspace = alloc_workspace(dims, block, q.device, stream)
     _need(workspace, "workspace", torch.uint8, None, q.device)
     _check(lib().ffd_decode_sparse_residual(ctypes.byref(dims), _ptr(q), _ptr(K_tail), _ptr(V),
                                             _ptr(Kc), _ptr(sc), _ptr(Kr), _ptr(sr), bits,
@@ -395,12 +410,12 @@ def decode_sparse_varlen(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, Kq: 
     _need(scales, "scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d),
           K.device)
     _need(seq_lens, "seq_lens", torch.int32, (B,), K.device)
-    out, lse = _decode_outputs(q, out, lse, want_lse)
+    out, lse = _decode_outputs(q, out, lse, want_lse, stream)
     if keep_mask is not None:
         _need(keep_mask, "keep_mask", torch.uint8,
               (q.shape[0], q.shape[1], math.ceil(max_len / block)), q.device)
     if workspace is None:
-        workspace = alloc_workspace(dims, block, q.device)
+        workspace = alloc_workspace(dims, block, q.device, stream)
     _need(workspace, "workspace", torch.uint8, None, q.device)
     _check(lib().ffd_decode_sparse_varlen(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V), _ptr(Kq),
                                           _ptr(scales), _ptr(seq_lens), float(delta), block,
@@ -420,9 +435,9 @@ def decode_dense_varlen(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_l
     _need(V, "V", K.dtype, K.shape, K.device)
     _need(q, "q", K.dtype, None, K.device)
     _need(seq_lens, "seq_lens", torch.int32, (B,), K.device)
-    out, lse = _decode_outputs(q, out, lse, want_lse)
+    out, lse = _decode_outputs(q, out, lse, want_lse, stream)
     if workspace is None:
-        workspace = alloc_workspace(dims, block, q.device)
+        workspace = alloc_workspace(dims, block, q.device, stream)
     _need(workspace, "workspace", torch.uint8, None, q.device)
     _check(lib().ffd_decode_dense_varlen(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V),
                                          _ptr(seq_lens), block, _ptr(out), _ptr(lse),
@@ -464,7 +479,8 @@ def block_scores(kind: int, q: torch.Tensor, K: torch.Tensor, block: int, seq_le
     _need(q, "q", K.dtype, None, K.device)
     nf = seq_len // block
     if out is None:
-        out = torch.empty((B, Hq, nf), dtype=torch.float32, device=q.device)
+        with _on(stream):
+            out = torch.empty((B, Hq, nf), dtype=torch.float32, device=q.device)
     _need(out, "scores", torch.float32, (B, Hq, nf), q.device)
     _check(lib().ffd_block_scores(ctypes.byref(dims), kind, _ptr(q), _ptr(K), _ptr(Kq),
                                   _ptr(scales), _ptr(kmin), _ptr(kmax), block, _ptr(out),
@@ -480,7 +496,8 @@ def select_blocks(rule: int, scores: torch.Tensor, param: float, block: int, seq
     _need(scores, "scores", torch.float32, None, scores.device)
     n_blocks = math.ceil(seq_len / block)
     if keep_mask is None:
-        keep_mask = torch.empty((B, Hq, n_blocks), dtype=torch.uint8, device=scores.device)
+        with _on(stream):
+            keep_mask = torch.empty((B, Hq, n_blocks), dtype=torch.uint8, device=scores.device)
     _need(keep_mask, "keep_mask", torch.uint8, (B, Hq, n_blocks), scores.device)
     if pseudo_max is not None:
         _need(pseudo_max, "pseudo_max", torch.float32, (B, Hq), scores.device)
@@ -501,9 +518,9 @@ def decode_masked(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, keep_mask: 
     _need(q, "q", K.dtype, None, K.device)
     _need(keep_mask, "keep_mask", torch.uint8,
           (q.shape[0], q.shape[1], math.ceil(seq_len / block)), q.device)
-    out, lse = _decode_outputs(q, out, lse, want_lse)
+    out, lse = _decode_outputs(q, out, lse, want_lse, stream)
     if workspace is None:
-        workspace = alloc_workspace(dims, block, q.device)
+        workspace = alloc_workspace(dims, block, q.device, stream)
     _need(workspace, "workspace", torch.uint8, None, q.device)
     _check(lib().ffd_decode_masked(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V),
                                    _ptr(keep_mask), block, _ptr(out), _ptr(lse), _ptr(workspace),

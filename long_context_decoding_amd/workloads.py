@@ -116,6 +116,20 @@ WORKLOADS = {
 }
 
 
+# Further shapes the paper runs the method on (Sec. 4.5 and App. F: Qwen2.5 with grouped-query
+# attention); parity cases, not benchmark lines.
+EXTRA_WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("gqa7_32k_sink_needles", B=1, Hq=28, Hkv=4, L=32768, T=64, deltas=(5.0,),
+                 plant="needles", n_needles=round(0.01 * 512), needle_a=6.0, sink_a=10.0,
+                 seed=20260906,
+                 description="Qwen2.5-7B-shaped layer (28 query / 4 kv heads), 32K, sink block + "
+                             "1% needle blocks"),
+    ]
+}
+
+
 def _gen(seed: int, *stream: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, *stream])))
 

@@ -15,6 +15,7 @@ HEADER = ROOT / "include" / "ffd.h"
 # fake, 16-byte aligned device addresses: validation must fail before anything dereferences them
 A = ctypes.c_void_p(0x10000)
 MISALIGNED = ctypes.c_void_p(0x10008)
+COUNTER_BYTES = 524288  # fixed counter region: one 8-byte slot per work unit, 65535 units
 
 
 def declared_functions():
@@ -61,13 +62,16 @@ def sparse_call(L, d, block=64, delta=5.0, q=A, ws=A, ws_bytes=1 << 30, K=A, kee
                                ws_bytes, None)
 
 
+
+
+
 def test_workspace_and_splits(L):
     d = dims()
     S = ffd.num_splits(d, 64)
     assert S >= 1
-    rec = 1 * 8 * S * 4                       # (b, kv head, split, query head of the group)
+    rec = 1 * 8 * S * 4                       # (unit, split, query head of the unit)
     r256 = lambda x: -(-x // 256) * 256
-    assert ffd.workspace_bytes(d, 64) == r256(8 * 8) + r256(rec * 8) + rec * 128 * 4
+    assert ffd.workspace_bytes(d, 64) == COUNTER_BYTES + r256(rec * 8) + rec * 128 * 4
     big = dims(B=8, seq_len=131072, seq_cap=131072)
     S = ffd.num_splits(big, 64)
     assert -(-2048 // S) <= 256
@@ -75,16 +79,47 @@ def test_workspace_and_splits(L):
     Sd = ffd.num_splits(big, 64, sparse=False)
     assert Sd == 131072 // 8192 and Sd > S
     rec = 8 * 8 * Sd * 4
-    assert ffd.workspace_bytes(big, 64) == r256(8 * 8 * 8) + r256(rec * 8) + rec * 128 * 4
+    assert ffd.workspace_bytes(big, 64) == COUNTER_BYTES + r256(rec * 8) + rec * 128 * 4
     long1 = dims(seq_len=262144, seq_cap=262144)
     assert ffd.num_splits(long1, 128, sparse=False) == ffd.num_splits(long1, 128) == 32
     assert ffd.workspace_bytes(dims(head_dim=64), 64) == 0
     assert ffd.workspace_bytes(d, 96) == 0
 
 
+@pytest.mark.parametrize("Hq,Hkv,units,width", [
+    (24, 8, 8, 4),     # G = 3: one unit of 4 heads per kv head, the last one padding
+    (28, 4, 4, 8),     # G = 7 (Qwen2.5-7B's 28 query / 4 kv heads): padded to 8
+    (40, 8, 8, 8),     # G = 5
+    (12, 2, 2, 8),     # G = 6
+    (64, 4, 8, 8),     # G = 16: two units of 8 per kv head
+    (48, 4, 8, 8),     # G = 12: units of 8 and of 4 (+4 padding)
+    (9, 1, 2, 8),      # G = 9
+])
+def test_group_sizes_and_units(L, Hq, Hkv, units, width):
+    """Every group size is accepted; the workspace holds one partial per (unit, split, head of
+    the unit), the unit being the kernel width that holds the group (or 8 heads)."""
+    d = dims(Hq=Hq, Hkv=Hkv)
+    S = ffd.num_splits(d, 64)
+    Sd = ffd.num_splits(d, 64, sparse=False)
+    assert S >= 1 and Sd >= 1
+    # one work-group per CU: the split count follows the unit count (4096 tokens: 64 blocks,
+    # so at most 32 splits of two blocks each)
+    assert S == min(-(-256 // units), 32)
+    rec = units * max(S, Sd) * width
+    r256 = lambda x: -(-x // 256) * 256
+    assert ffd.workspace_bytes(d, 64) == COUNTER_BYTES + r256(rec * 8) + rec * 128 * 4
+    assert sparse_call(L, d, ws_bytes=ffd.workspace_bytes(d, 64) - 1) == ffd.FFD_ERR_WORKSPACE
+
+
+def test_too_many_units_unsupported(L):
+    # 65535 units at most: 4096 sequences x 8 kv heads x 2 units (G = 16) is 65536
+    assert sparse_call(L, dims(B=4096, Hq=128, Hkv=8)) == ffd.FFD_ERR_UNSUPPORTED
+    assert ffd.workspace_bytes(dims(B=4096, Hq=128, Hkv=8), 64) == 0
+    assert ffd.workspace_bytes(dims(B=4095, Hq=128, Hkv=8), 64) > 0
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=64), ffd.FFD_ERR_UNSUPPORTED),
-    (dict(Hq=24, Hkv=8), ffd.FFD_ERR_UNSUPPORTED),      # G = 3
     (dict(Hq=30, Hkv=8), ffd.FFD_ERR_INVALID_ARG),      # not a multiple
     (dict(seq_len=0), ffd.FFD_ERR_INVALID_ARG),
     (dict(seq_cap=4000), ffd.FFD_ERR_INVALID_ARG),      # < seq_len
@@ -132,10 +167,10 @@ def test_workspace_init_validation(L):
     wi = L.ffd_workspace_init
     assert wi(ctypes.byref(d), 64, None, n, None) == ffd.FFD_ERR_WORKSPACE
     assert wi(ctypes.byref(d), 64, MISALIGNED, n, None) == ffd.FFD_ERR_WORKSPACE
-    # only the counters need to fit: 8 bytes per (sequence, kv head), rounded up to 256
-    assert wi(ctypes.byref(d), 64, A, 255, None) == ffd.FFD_ERR_WORKSPACE
-    big = dims(B=40)  # 320 counters = 2560 bytes
-    assert wi(ctypes.byref(big), 64, A, 2559, None) == ffd.FFD_ERR_WORKSPACE
+    # only the counter region needs to fit: its fixed size, whatever the dims
+    assert wi(ctypes.byref(d), 64, A, COUNTER_BYTES - 1, None) == ffd.FFD_ERR_WORKSPACE
+    big = dims(B=40)
+    assert wi(ctypes.byref(big), 64, A, COUNTER_BYTES - 1, None) == ffd.FFD_ERR_WORKSPACE
     assert wi(ctypes.byref(d), 96, A, n, None) == ffd.FFD_ERR_UNSUPPORTED
     assert wi(ctypes.byref(dims(B=0)), 64, None, 0, None) == ffd.FFD_OK
 

@@ -29,7 +29,7 @@ def bf16(x: np.ndarray) -> np.ndarray:
     return W.f32_to_bf16_bits(x.astype(np.float32))
 
 
-@pytest.mark.parametrize("T,G", [(64, 4), (128, 1), (64, 8), (128, 2)])
+@pytest.mark.parametrize("T,G", [(64, 4), (128, 1), (64, 8), (128, 2), (64, 7), (128, 6), (64, 16)])
 def test_varlen_matches_oracle_per_sequence(T, G):
     Hkv = 2 if G <= 4 else 1
     cap = 12 * T

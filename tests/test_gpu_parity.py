@@ -16,7 +16,7 @@ import torch
 import oracle
 from conftest import log
 from helpers import (DEV, TOL, assert_close, gpu_dense, gpu_quantize, gpu_sparse, oracle_attend,
-                     oracle_masks, sample_heads, upload)
+                     oracle_masks, upload)
 from long_context_decoding_amd import ffd
 from long_context_decoding_amd import workloads as W
 
@@ -25,16 +25,29 @@ pytestmark = pytest.mark.gpu
 INF = float("inf")
 DELTAS = (0.0, 0.5, 2.0, 5.0, INF)
 
-CASES = [(dt, G, T, L)
-         for dt in ("bf16", "f32")
-         for G in (1, 2, 4, 8)
-         for T in (64, 128)
-         for L in (T, 2 * T, 3 * T + 17, 20 * T + 5)]
+CASES = ([(dt, G, T, L)
+          for dt in ("bf16", "f32")
+          for G in (1, 2, 4, 8)
+          for T in (64, 128)
+          for L in (T, 2 * T, 3 * T + 17, 20 * T + 5)]
+         # group sizes the kernels run padded (3 as 4; 5, 6, 7 as 8)
+         + [(dt, G, T, L)
+            for dt in ("bf16", "f32")
+            for G in (3, 5, 6, 7)
+            for T in (64, 128)
+            for L in (T, 3 * T + 17, 20 * T + 5)]
+         # groups wider than the kernel: cut into units of 8 heads (9 = 8 + 1, 12 = 8 + 4,
+         # 16 = 8 + 8)
+         + [(dt, G, T, L)
+            for dt in ("bf16", "f32")
+            for G in (9, 12, 16)
+            for T in (64, 128)
+            for L in (3 * T + 17, 20 * T + 5)])
 
 
 def small_case(dt, G, T, L):
     B = 2 if (G + L) % 2 == 0 else 1
-    Hkv = 2 if G <= 4 else 1
+    Hkv = 2 if G <= 4 or G % 3 == 0 else 1
     plant = "powerlaw" if (L // T) % 2 == 0 else "needles"
     seed = 1000 * G + 7 * T + L + (0 if dt == "bf16" else 1)
     return W.small(f"case_{dt}_G{G}_T{T}_L{L}", B=B, Hq=G * Hkv, Hkv=Hkv, L=L, T=T, dtype=dt,
@@ -97,9 +110,11 @@ def oracle_quantize_threaded(w, K, slices):
     return Kq, sc
 
 
-@pytest.mark.parametrize("name", list(W.WORKLOADS))
+@pytest.mark.parametrize("name", list(W.WORKLOADS) + list(W.EXTRA_WORKLOADS))
 def test_named_workload_full_size(name):
-    w = W.WORKLOADS[name]
+    """Full size, in the benchmark's launch configuration: Kq and scales byte-exact, masks of
+    every head bit-exact, out and lse of every head within the tolerance, sparse and dense."""
+    w = W.WORKLOADS.get(name) or W.EXTRA_WORKLOADS[name]
     log(f"[gpu] full-size {name}: generating")
     q, K, V, info = W.make_inputs(w)
     all_slices = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
@@ -111,7 +126,7 @@ def test_named_workload_full_size(name):
     torch.cuda.synchronize()
     assert torch.equal(Kq_d.cpu(), torch.from_numpy(Kq)), "Kq bytes differ"
     assert torch.equal(sc_d.cpu(), torch.from_numpy(sc)), "scales differ"
-    heads = sample_heads(w, 12, seed=w.seed)
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
     tol = TOL[w.dtype]
     for delta in w.deltas:
         log(f"[gpu] full-size {name}: sparse delta={delta}")
@@ -179,6 +194,29 @@ def test_split_invariance(mid_case, splits, monkeypatch):
     assert_close(lse, lse0, 1e-5, "lse vs default split")
     d, dl = gpu_dense(w, qd, Kd, Vd)
     assert_close(d, d0, 1e-5, "dense out vs default split")
+
+
+def test_side_stream_without_workspace(mid_case):
+    """A call on a non-default stream with no workspace given: the binding allocates and
+    prepares the temporary workspace on that stream, so the result equals the oracle's."""
+    w, (q, K, V), (qd, Kd, Vd, Kq_d, sc_d) = mid_case
+    Kq, sc = oracle.quantize_k(K, w.T, 0, w.L)
+    ref = oracle.decode(q, K, V, w.L, w.T, delta=5.0, Kq=Kq, scales=sc)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for i in range(3):
+        keep = torch.full((w.B, w.Hq, w.n_blocks), 7, dtype=torch.uint8, device=DEV)
+        side.wait_stream(torch.cuda.current_stream())
+        out, lse = ffd.decode_sparse(qd, Kd, Vd, Kq_d, sc_d, 5.0, w.T, w.L, keep_mask=keep,
+                                     stream=side)
+        # other work on the current stream meanwhile allocates and fills fresh memory
+        junk = torch.full((1 << 20,), float("nan"), device=DEV)
+        del junk
+        side.synchronize()
+        np.testing.assert_array_equal(keep.cpu().numpy(), ref["keep"])
+        assert_close(out.cpu().numpy(), ref["out"], TOL[w.dtype], f"out call {i}")
+        assert_close(lse.cpu().numpy(), ref["lse"], TOL[w.dtype], f"lse call {i}")
+    torch.cuda.synchronize()
 
 
 def test_deterministic(mid_case):

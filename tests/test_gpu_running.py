@@ -25,7 +25,9 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"bf16": 2e-3, "f32": 1e-5}
 CASES = [("bf16", 4, 64, 20 * 64 + 5, 2), ("bf16", 1, 128, 9 * 128, 1), ("f32", 2, 64, 12 * 64 + 33, 2),
-         ("bf16", 8, 64, 7 * 64 + 1, 1)]
+         ("bf16", 8, 64, 7 * 64 + 1, 1),
+         # padded groups and a group cut into two units of 8
+         ("bf16", 5, 64, 17 * 64 + 3, 2), ("f32", 3, 128, 8 * 128 + 1, 1), ("bf16", 16, 64, 9 * 64, 1)]
 
 
 @pytest.mark.parametrize("dtype,G,T,L,Hkv", CASES)

@@ -24,11 +24,13 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"bf16": 2e-3, "f32": 1e-5}
 CASES = [("bf16", 4, 64, 20 * 64 + 5), ("bf16", 1, 128, 9 * 128), ("f32", 2, 64, 12 * 64 + 33),
-         ("bf16", 8, 64, 7 * 64 + 1)]
+         ("bf16", 8, 64, 7 * 64 + 1),
+         # padded groups and a group cut into two units of 8
+         ("bf16", 3, 128, 11 * 128 + 7), ("f32", 7, 64, 13 * 64 + 9), ("bf16", 12, 64, 10 * 64)]
 
 
 def setup(dtype, G, T, L, seed):
-    Hkv = 2 if G <= 4 else 1
+    Hkv = 2 if G <= 4 or G == 12 else 1
     w = W.small(f"sel_{dtype}_G{G}_T{T}_L{L}", B=2, Hq=G * Hkv, Hkv=Hkv, L=L, T=T, dtype=dtype,
                 seed=seed, plant="powerlaw" if seed % 2 else "needles")
     q, K, V, _ = W.make_inputs(w)
