@@ -274,6 +274,27 @@ ffd_status ffd_decode_sparse_running(const ffd_dims* dims, const void* q, const 
                                      float* lse, uint8_t* keep_mask, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, serving loops or
+ * harnesses that forbid hipMalloc): ffd_decode_sparse with the library's own fixed scratch area
+ * in place of a caller's workspace.  Same arguments (minus the workspace), same kernels, same
+ * results as ffd_decode_sparse.
+ *   - The scratch area is a file-scope device array of FFD_NOALLOC_SCRATCH_BYTES (16 MiB) per
+ *     GPU, held from the first call on that GPU until the process ends.  A call whose dims need
+ *     more (ffd_workspace_bytes is an upper bound of the need) returns FFD_ERR_WORKSPACE and
+ *     launches nothing.
+ *   - The first call on a device (the current device) looks up the area's address and zeroes its
+ *     counters with a kernel on `stream`; it should not be the call under graph capture.  Nothing
+ *     is allocated, then or later (no hipMalloc, hipFree or allocating library routine).
+ *   - Every call on a GPU shares that GPU's area: calls that overlap in time on one GPU (other
+ *     streams, other threads) race and give wrong results.  Serialize them (one stream).
+ */
+#define FFD_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+ffd_status ffd_decode_sparse_noalloc(const ffd_dims* dims, const void* q, const void* K,
+                                     const void* V, const uint8_t* Kq, const float* scales,
+                                     float delta, int32_t block, float* out, float* lse,
+                                     uint8_t* keep_mask, hipStream_t stream);
+
 /* Workspace bytes of ffd_decode_sparse_running for this window; 0 for invalid arguments. */
 size_t ffd_workspace_bytes_window(const ffd_dims* dims, int32_t block, int32_t window);
 

@@ -13,7 +13,7 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libffd.so"
-SOURCES = [CSRC / "ffd_kernels.hip", CSRC / "ffd_api.cpp"]
+SOURCES = [CSRC / "ffd_kernels.hip", CSRC / "ffd_scratch.hip", CSRC / "ffd_api.cpp"]
 HEADERS = [CSRC / "ffd_internal.h", ROOT / "include" / "ffd.h"]
 PROBE_LIB = PKG / "libffd_probe.so"
 PROBE_SOURCES = [CSRC / "probe.hip"]

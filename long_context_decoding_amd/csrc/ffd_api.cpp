@@ -99,6 +99,7 @@ struct WsLayout {
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr size_t kCounterBytes = ((size_t)kMaxUnits * sizeof(unsigned long long) + 255) & ~(size_t)255;
+static_assert(FFD_NOALLOC_SCRATCH_BYTES == ffd::kScratchBytes, "header and library disagree");
 
 WsLayout ws_layout(const ffd_dims* d, int S)
 {
@@ -119,7 +120,8 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
                          size_t workspace_bytes, hipStream_t stream, bool sparse,
                          const int8_t* Kr = nullptr, const float* res_scales = nullptr,
                          int bits = 0, const int32_t* seq_lens = nullptr,
-                         const uint8_t* ext_mask = nullptr, int window = 0)
+                         const uint8_t* ext_mask = nullptr, int window = 0,
+                         bool noalloc = false)
 {
     const bool res = bits != 0;
     ffd_status st = check_dims(dims, block);
@@ -146,6 +148,14 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
         return FFD_ERR_UNSUPPORTED;
     const int S = window != 0 ? (n_blk + window - 1) / window : splits_for(dims, block, sparse);
     const WsLayout lay = ws_layout(dims, S);
+    if (noalloc) {
+        // the library's fixed scratch area in place of a caller's workspace: sizes beyond it are
+        // rejected before any HIP call; its address is looked up (and its counters zeroed) at
+        // the first call on the device
+        if (lay.total > ffd::kScratchBytes) return FFD_ERR_WORKSPACE;
+        if (ffd::scratch_area(kCounterBytes, stream, &workspace) != hipSuccess) return FFD_ERR_HIP;
+        workspace_bytes = ffd::kScratchBytes;
+    }
     if (!workspace || !aligned16(workspace)) return FFD_ERR_WORKSPACE;
     if (workspace_bytes < lay.total) return FFD_ERR_WORKSPACE;
 
@@ -280,6 +290,15 @@ ffd_status ffd_decode_sparse(const ffd_dims* dims, const void* q, const void* K,
 {
     return decode_common(dims, q, K, V, Kq, scales, delta, block, out, lse, keep_mask, workspace,
                          workspace_bytes, stream, true);
+}
+
+ffd_status ffd_decode_sparse_noalloc(const ffd_dims* dims, const void* q, const void* K,
+                                     const void* V, const uint8_t* Kq, const float* scales,
+                                     float delta, int32_t block, float* out, float* lse,
+                                     uint8_t* keep_mask, hipStream_t stream)
+{
+    return decode_common(dims, q, K, V, Kq, scales, delta, block, out, lse, keep_mask, nullptr, 0,
+                         stream, true, nullptr, nullptr, 0, nullptr, nullptr, 0, true);
 }
 
 ffd_status ffd_quantize_k_residual_append(const ffd_dims* dims, const void* K, int32_t tok_begin,

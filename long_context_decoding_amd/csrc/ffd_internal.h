@@ -14,6 +14,8 @@ constexpr int kWaves = 4;                  // waves per work-group of the decode
 constexpr int kMaxBlocksPerSplit = 256;    // LDS sizing of the per-split block tables
 constexpr int kMaxSplits = 256;            // LDS sizing of the final split merge
 constexpr int kMaxUnitHeads = 8;           // query heads per work unit (the kernels' widest group)
+constexpr size_t kScratchBytes = (size_t)16 << 20;  // the fixed scratch area of the no-allocation
+                                                    // entry point, per device
 
 // Query heads per work unit for a group of G query heads per kv head: the narrowest kernel width
 // (1, 2, 4 or 8) that holds the group, or 8 for larger groups, which are cut into units of 8
@@ -124,5 +126,10 @@ hipError_t launch_quantize(const QuantParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_decode_res(const DecodeParams& p, int bits, hipStream_t stream);
 hipError_t launch_quantize_res(const QuantParams& p, int bits, hipStream_t stream);
 hipError_t launch_zero_counters(uint32_t* counters, int n, hipStream_t stream);
+
+// The current device's fixed scratch area (kScratchBytes, 256-byte aligned; ffd_scratch.hip):
+// its device address, looked up at the first call on the device, when its first counter_bytes
+// bytes are also zeroed on `stream`.  No allocation.
+hipError_t scratch_area(size_t counter_bytes, hipStream_t stream, void** ptr);
 
 }  // namespace ffd

@@ -89,6 +89,8 @@ def lib():
         L.ffd_decode_sparse_running.restype = i32
         L.ffd_workspace_bytes_window.argtypes = [D, i32, i32]
         L.ffd_workspace_bytes_window.restype = sz
+        L.ffd_decode_sparse_noalloc.argtypes = [D, P, P, P, P, P, f32, i32, P, P, P, P]
+        L.ffd_decode_sparse_noalloc.restype = i32
         _lib = L
     return _lib
 
@@ -260,6 +262,35 @@ def decode_sparse(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, Kq: torch.T
                                    _ptr(scales), float(delta), block, _ptr(out), _ptr(lse),
                                    _ptr(keep_mask), _ptr(workspace), workspace.numel(),
                                    _stream(stream)))
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # FFD_NOALLOC_SCRATCH_BYTES
+
+
+def decode_sparse_noalloc(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, Kq: torch.Tensor,
+                          scales: torch.Tensor, delta: float, block: int, seq_len: int,
+                          out: torch.Tensor, lse: torch.Tensor | None = None,
+                          keep_mask: torch.Tensor | None = None, stream=None):
+    """Sparse decode step on the library's fixed scratch area (no workspace, nothing
+    allocated: `out` and `lse` are the caller's).  Calls that overlap on one GPU race."""
+    dims = dims_of(q, K, seq_len)
+    for name, t in (("q", q), ("K", K), ("V", V)):
+        _need(t, name, K.dtype, None, K.device)
+    _need(V, "V", K.dtype, K.shape, K.device)
+    B, Hkv, cap, d = K.shape
+    _need(Kq, "Kq", torch.uint8, (B, Hkv, cap, d // 2), K.device)
+    _need(scales, "scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d),
+          K.device)
+    _need(out, "out", torch.float32, (q.shape[0], q.shape[1], d), q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (q.shape[0], q.shape[1]), q.device)
+    if keep_mask is not None:
+        _need(keep_mask, "keep_mask", torch.uint8,
+              (q.shape[0], q.shape[1], math.ceil(seq_len / block)), q.device)
+    _check(lib().ffd_decode_sparse_noalloc(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V),
+                                           _ptr(Kq), _ptr(scales), float(delta), block, _ptr(out),
+                                           _ptr(lse), _ptr(keep_mask), _stream(stream)))
     return out, lse
 
 
