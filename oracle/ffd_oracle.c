@@ -203,32 +203,40 @@ void ffdo_scan_head(const float* qh, const uint8_t* Kq, const float* scales, int
 }
 
 /* ------------------------------------------------------------------------------------------ */
-/* O5-O7: pseudo-max, threshold and block mask for one query head.                             */
+/* O5-O7: relative threshold and block mask of one query head (Eq. 1 with Eq. 3).              */
 /* ------------------------------------------------------------------------------------------ */
 /*
- * n_full full blocks, n_blocks = ceil(L/T) blocks in total (the last one may be a partial tail).
- * keep[n_blocks] receives 0/1.  mtilde/theta receive the pseudo-max and threshold (NaN when
- * n_full == 0: then every block is kept).
+ * Eq. 1 keeps a block when its largest score is no more than delta below the largest score of
+ * the whole attention row.  That maximum is unknown before every block has been scored, so Eq. 3
+ * stands a reference in for it: the largest score over a few anchor blocks on which attention
+ * concentrates, the sink at the start of the sequence and the most recent tokens.  Here the
+ * scores are the scan estimates, the anchors are block 0 and the last full block, and the
+ * anchors, together with a partial tail block (which has no low-bit copy), are kept with no test.
+ *
+ * est[n_full] are the estimates of the full blocks; keep[n_blocks] receives 0/1, n_blocks =
+ * ceil(L/T).  ref_out and cut_out (may be NULL) receive the reference and the cut RN(ref - delta);
+ * both are NaN when there is no full block, and then every block is kept.
  */
-void ffdo_select_head(const float* shat_block, int n_full, int n_blocks, float delta,
-                      uint8_t* keep, float* mtilde_out, float* theta_out)
+static int anchor_or_tail(int j, int n_full) { return j == 0 || j >= n_full - 1; }
+
+void ffdo_select_head(const float* est, int n_full, int n_blocks, float delta, uint8_t* keep,
+                      float* ref_out, float* cut_out)
 {
     if (n_full == 0) {
-        for (int j = 0; j < n_blocks; ++j) keep[j] = 1;
-        if (mtilde_out) *mtilde_out = NAN;
-        if (theta_out) *theta_out = NAN;
+        memset(keep, 1, (size_t)n_blocks);
+        if (ref_out) *ref_out = NAN;
+        if (cut_out) *cut_out = NAN;
         return;
     }
-    const float s_global = shat_block[0];          /* sink block */
-    const float s_local = shat_block[n_full - 1];  /* last full block */
-    const float mtilde = s_global > s_local ? s_global : s_local;
-    const float theta = mtilde - delta;            /* delta = +inf gives -inf */
-    for (int j = 0; j < n_blocks; ++j) {
-        if (j == 0 || j >= n_full - 1) keep[j] = 1; /* sink, local, tail */
-        else keep[j] = shat_block[j] >= theta ? 1 : 0;
-    }
-    if (mtilde_out) *mtilde_out = mtilde;
-    if (theta_out) *theta_out = theta;
+    const int anchors[2] = {0, n_full - 1};
+    float ref = -INFINITY;
+    for (int a = 0; a < 2; ++a)
+        if (est[anchors[a]] > ref) ref = est[anchors[a]];
+    const float cut = ref - delta; /* one binary32 subtraction; delta = +inf gives -inf */
+    for (int j = 0; j < n_blocks; ++j)
+        keep[j] = (uint8_t)(anchor_or_tail(j, n_full) || est[j] >= cut);
+    if (ref_out) *ref_out = ref;
+    if (cut_out) *cut_out = cut;
 }
 
 /* ------------------------------------------------------------------------------------------ */
