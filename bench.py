@@ -461,11 +461,35 @@ def run_workload(w, delta: float, steps: int, warmup: int, min_rotation_mib: int
 # ------------------------------------------------------------------------------------------
 # CPU baseline: the oracle, unchanged, on the host cores
 # ------------------------------------------------------------------------------------------
+def cpu_model() -> str | None:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def host_threads() -> tuple[int, str]:
+    """Threads for the CPU oracle: the host's CPU share for this process -- OMP_NUM_THREADS when
+    the environment sets it (a machine shared by several GPUs gives each GPU's jobs that many),
+    else every core in the process's affinity set -- and where the figure came from."""
+    affinity = max(1, len(os.sched_getaffinity(0)))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) >= 1:
+        return min(int(env), affinity), "OMP_NUM_THREADS (the host's CPU share for this job)"
+    return affinity, "sched_getaffinity (every core this process may run on)"
+
+
 def cpu_baseline(w, delta: float, host, budget_s: float = 12.0) -> dict:
+    """The oracle, unchanged, on the host's cores (OpenMP over the (b, query head) rows: 32 rows
+    at 256K, so more than 32 threads would idle)."""
     import oracle
 
     q, K, V = host
-    nthreads = min(16, max(1, len(os.sched_getaffinity(0))))
+    affinity = len(os.sched_getaffinity(0))
+    nthreads, source = host_threads()
     t0 = time.time()
     Kq, sc = oracle.quantize_k(K, w.T, 0, w.L)
     quant_s = time.time() - t0
@@ -477,7 +501,8 @@ def cpu_baseline(w, delta: float, host, budget_s: float = 12.0) -> dict:
         times.append(time.perf_counter() - t0)
     med = float(np.median(times[1:])) if len(times) > 1 else times[0]
     return {"value": med * 1e6, "unit": "µs/decode step", "cores": nthreads,
-            "kind": "oracle",
+            "kind": "oracle", "threads": nthreads, "threads_from": source, "rows": w.B * w.Hq,
+            "nproc": affinity, "cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
             "sample": (f"whole sparse decode step of {w.name} (all {w.B * w.Hq} query heads: "
                        f"integer scan, select, fp64 exact attention over kept blocks), "
                        f"{len(times)} runs, median of runs 2..; oracle quantize of the cache "
