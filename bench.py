@@ -651,6 +651,53 @@ def running_leg(names=("h1_4k_f32_needles", "gqa4_32k_sink_needles")) -> dict:
     return res
 
 
+SWEEP_LENGTHS = (4096, 8192, 16384, 32768, 65536, 131072, 262144)
+
+
+def sweep_workload(L: int):
+    """The headline workload's shape and structure at context L (the pages' Fig. 3 sweeps one
+    layer shape over 4K-256K): B = 1, 32 query / 8 kv heads, blocks of 128, a sink block and
+    0.5% needle blocks (at least one)."""
+    from long_context_decoding_amd import workloads as W
+
+    base = W.WORKLOADS[PRIMARY]
+    if L == base.L:
+        return base
+    nb = L // base.T
+    return base.with_(name=f"ctx{L // 1024}k_gqa4_sink_needles", L=L,
+                      n_needles=max(1, round(0.005 * nb)), seed=base.seed + L)
+
+
+def context_sweep(prim: dict, prim_probe: dict, steps: int, warmup: int, rotation_mib: int,
+                  graphs: bool) -> list:
+    """Sparse and dense step time against context length at one shape (Fig. 3 analogue): per
+    length, the graph-replayed step over rotated cache copies, the speedup over dense, the
+    algorithmic bytes and their rate, and the streaming-read probe at the same byte count."""
+    rows = []
+    for L in SWEEP_LENGTHS:
+        w = sweep_workload(L)
+        if w.name == prim["workload"]:
+            r, prb = prim, prim_probe
+        else:
+            r, _ = run_workload(w, 5.0, steps, warmup, rotation_mib, graphs=graphs)
+            prb = probe_leg(r["bytes_read_sparse"], steps, groups=(1024,))
+        row = {"L": L, "workload": r["workload"], "splits": r["splits"],
+               "sparse_us": round(r["sparse_us"], 3), "dense_us": round(r["dense_us"], 3),
+               "speedup_vs_dense": round(r["speedup_vs_dense"], 3),
+               "bytes_sparse": r["bytes_read_sparse"], "bytes_dense": r["bytes_read_dense"],
+               "sparse_GBps": round(r["sparse_GBps"], 1),
+               "sparse_hbm_frac": round(r["sparse_hbm_frac"], 4),
+               "dense_hbm_frac": round(r["dense_hbm_frac"], 4),
+               "probe_GBps": round(prb["GBps"], 1),
+               "sparse_frac_of_probe": round(r["sparse_GBps"] / prb["GBps"], 4),
+               "union_keep": round(r["union_keep"], 5)}
+        log(f"sweep L={L}: sparse {row['sparse_us']:.1f} us, dense {row['dense_us']:.1f} us, "
+            f"{row['speedup_vs_dense']:.2f}x, {row['sparse_GBps']:.0f} GB/s "
+            f"({row['sparse_frac_of_probe']:.0%} of the probe's {row['probe_GBps']:.0f})")
+        rows.append(row)
+    return rows
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -670,6 +717,8 @@ def main() -> int:
                     help="skip the decode-loop leg (append + decode with device-side lengths)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (no graph capture), e.g. under counter tools")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the context-length sweep (4K-256K at the headline shape)")
     ap.add_argument("--rotation-mib", type=int, default=1024,
                     help="minimum bytes read by one rotation over the cache copies")
     args = ap.parse_args()
@@ -739,6 +788,10 @@ def main() -> int:
     log(f"streaming-read probe over {prb['bytes'] / 1e6:.1f} MB: {prb['GBps']:.0f} GB/s "
         f"({prb['GBps'] / HBM_PEAK_GBPS:.1%} of {HBM_PEAK_GBPS:.0f}); the sparse step reaches "
         f"{prim['sparse_GBps'] / prb['GBps']:.1%} of it")
+    sweep = None
+    if not args.no_sweep and args.workload == PRIMARY:
+        sweep = context_sweep(prim, prb, args.steps, args.warmup, args.rotation_mib,
+                              graphs=not args.eager)
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
@@ -796,6 +849,7 @@ def main() -> int:
             "frac_of_probe": round(sec["frac_of_probe"], 4) if sec.get("frac_of_probe") else None,
         },
         "probe": prb,
+        "context_sweep": sweep,
         "cpu_baseline": cpu,
         "primary": prim,
         "secondary": sec,
