@@ -355,11 +355,26 @@ __device__ __forceinline__ void tile_load(TileRegs<BF16>& r, const void* __restr
     }
 }
 
+// Online-softmax state of one lane.  m and l belong to head col % G (the lane's score column).
+// The unnormalized output o depends on how P.V is computed:
+//   bf16 values (MF): on the MFMA, o[j] is the 16 x 16 accumulator of channels 8 r + j (r = 16
+//     rows) against the 16 columns (heads col % G, replicated): lane (kg, col) holds channels
+//     32 kg + 8 v + j, v = 0..3, of head col, summed over every token;
+//   fp32 values: on the VALU, o[h][c] is channel 8 col + c of head h, summed over this lane's
+//     tokens (4 kg + v), to be summed over kg at the end.
+template <int G, bool MF>
+struct SoftState;
 template <int G>
-struct SoftState {
-    float o[G][8];  // unnormalized output, channels 8*col.., summed over this lane's tokens
-    float m;        // running max (log2 units) of head col % G
-    float l;        // running sum of exp2(s - m) of head col % G
+struct SoftState<G, true> {
+    v4f o[8];
+    float m;
+    float l;
+};
+template <int G>
+struct SoftState<G, false> {
+    float o[G][8];
+    float m;
+    float l;
 };
 
 // Scores S[token t0 + 4 kg + v][head col % G] of a 16-token tile with stored keys.  B operand:
@@ -394,8 +409,8 @@ __device__ __forceinline__ v4f tile_scores(const TileRegs<BF16>& r, const void* 
 // Online softmax (base 2) of a tile's scores and P.V into the lane's running state.  r.v holds
 // the tile's values: 4 x uint4 of bf16 (token 4*kg + i, channels 8*col ..) or 8 x float4.
 template <int G, bool VBF16, typename TR>
-__device__ __forceinline__ void softmax_pv(v4f acc, const TR& r, SoftState<G>& st, int t0, int L,
-                                           u32 kbits, float c_log2, int lane)
+__device__ __forceinline__ void softmax_pv(v4f acc, const TR& r, SoftState<G, VBF16>& st, int t0,
+                                           int L, u32 kbits, float c_log2, int lane)
 {
     const int col = lane & 15, kg = lane >> 4;
     const bool head_keep = (kbits >> (col % G)) & 1u;
@@ -421,6 +436,43 @@ __device__ __forceinline__ void softmax_pv(v4f acc, const TR& r, SoftState<G>& s
     st.l = st.l * alpha + psum;
     st.m = m_new;
 
+    if constexpr (VBF16) {
+        // P.V on the bf16 MFMA, O^T[channel][head] += V^T[channel][token] P^T[token][head], one
+        // 16x16x32 product per 16 channels 8 r + j (r = 0..15) and j = 0..7.  The K dimension holds
+        // every token twice: k = 8 kg + i is token 4 kg + (i % 4), with the bf16 high part of its
+        // probability for i < 4 and the low part p - hi for i >= 4, so the fp32 probabilities
+        // enter to within 2^-17 relative and the sum over tokens needs no cross-lane step.
+        // B: this lane's own probabilities (column col = head col % G, tokens 4 kg + v).
+        v8bf bp;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const __bf16 hi = (__bf16)p[v];
+            bp[v] = hi;
+            bp[v + 4] = (__bf16)(p[v] - (float)hi);
+        }
+        // A: row r = col holds channel 8 col + j of tokens 4 kg + i: the j-th bf16 of r.v[i];
+        // rows past the sequence are zeroed (they may hold anything, even NaN)
+        u32 wv[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool in = t0 + 4 * kg + i < L;
+            const uint4 x = r.v[i];
+            wv[i][0] = in ? x.x : 0u;
+            wv[i][1] = in ? x.y : 0u;
+            wv[i][2] = in ? x.z : 0u;
+            wv[i][3] = in ? x.w : 0u;
+        }
+        typedef u32 v4u __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const u32 sel = (j & 1) ? 0x07060302u : 0x05040100u;  // high or low bf16 of each word
+            const u32 d0 = __builtin_amdgcn_perm(wv[1][j >> 1], wv[0][j >> 1], sel);
+            const u32 d1 = __builtin_amdgcn_perm(wv[3][j >> 1], wv[2][j >> 1], sel);
+            const v8bf a = __builtin_bit_cast(v8bf, (v4u){d0, d1, d0, d1});
+            st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bp, st.o[j] * alpha, 0, 0, 0);
+        }
+        return;
+    } else {
     // move probabilities to the PV layout: lane (kg, col) needs p[4 kg + v] of every head h of
     // the group, and its rescale factor, from lane h of its own row (column h of the score tile)
     float pp[G][4];
@@ -460,11 +512,12 @@ __device__ __forceinline__ void softmax_pv(v4f acc, const TR& r, SoftState<G>& s
 #pragma unroll
             for (int c = 0; c < 8; ++c) st.o[h][c] = fmaf(pp[h][v], vv[c], st.o[h][c]);
     }
+    }
 }
 
 template <int G, bool BF16>
 __device__ __forceinline__ void tile_compute(const TileRegs<BF16>& r, const void* __restrict__ qrow,
-                                             const v8bf* qv, SoftState<G>& st, int t0, int L,
+                                             const v8bf* qv, SoftState<G, BF16>& st, int t0, int L,
                                              u32 kbits, float c_log2, int lane)
 {
     softmax_pv<G, BF16>(tile_scores<BF16>(r, qrow, qv, lane), r, st, t0, L, kbits, c_log2, lane);
@@ -584,7 +637,7 @@ __device__ __forceinline__ v4f tile_scores_res(const TileRes& r, const v8bf* qv,
 
 template <int G, int BITS>
 __device__ __forceinline__ void tile_compute_res(const TileRes& r, const v8bf* qv,
-                                                 SoftState<G>& st, WaveScratch<G>& ws, int t0,
+                                                 SoftState<G, true>& st, WaveScratch<G>& ws, int t0,
                                                  int L, u32 kbits, float c_log2, bool tail,
                                                  int lane)
 {
@@ -966,11 +1019,17 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
 
     // exact attention over the kept blocks, 16-token tiles dealt round-robin to the waves,
     // pipelined like the scan (two tiles in flight, no load past the last tile)
-    SoftState<G> st;
+    constexpr bool MF = BF16;  // P.V on the MFMA for 16-bit values (see SoftState)
+    SoftState<G, MF> st;
+    if constexpr (MF) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+        for (int j = 0; j < 8; ++j) st.o[j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    } else {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) st.o[h][c] = 0.0f;
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) st.o[h][c] = 0.0f;
+    }
     st.m = kNegInf;
     st.l = 0.0f;
     {
@@ -1040,19 +1099,35 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
         }
     }
 
-    // sum the four token subsets (kg) of every lane's channels
+    if constexpr (!MF) {
+        // sum the four token subsets (kg) of every lane's channels
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            float x = st.o[h][c];
-            x = fsum32(fsum16(x));
-            st.o[h][c] = x;
-        }
+            for (int c = 0; c < 8; ++c) {
+                float x = st.o[h][c];
+                x = fsum32(fsum16(x));
+                st.o[h][c] = x;
+            }
+    }
 
     // merge the waves' softmax states into this split's partial
     __syncthreads();  // the shat table is reused as the merge buffer
-    if (kg == 0) {
+    if constexpr (MF) {
+        // lane (kg, col < G): channels 32 kg + 8 v + j of head col are st.o[j][v]
+        if (col < G) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float4* dst = reinterpret_cast<float4*>(&sh.u.merge.o[w][col][32 * kg + 8 * v]);
+                dst[0] = make_float4(st.o[0][v], st.o[1][v], st.o[2][v], st.o[3][v]);
+                dst[1] = make_float4(st.o[4][v], st.o[5][v], st.o[6][v], st.o[7][v]);
+            }
+            if (kg == 0) {
+                sh.u.merge.m[w][col] = st.m;
+                sh.u.merge.l[w][col] = st.l;
+            }
+        }
+    } else if (kg == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float4* dst = reinterpret_cast<float4*>(&sh.u.merge.o[w][h][col * 8]);
