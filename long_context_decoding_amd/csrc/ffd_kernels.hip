@@ -14,7 +14,9 @@
 //                      select   pseudo-max over the sink and local blocks (Eq. 3), keep a block
 //                               iff its estimated max >= pseudo-max - delta (Eq. 1)
 //                      exact    bf16/fp32 MFMA for the G x 16 score tile, online softmax with
-//                               fp32 probabilities, PV on the VALU in fp32 (Alg. 1 refinement)
+//                               fp32 probabilities, PV on the bf16 MFMA with each probability
+//                               as a bf16 high/low pair (fp32 values: on the VALU) (Alg. 1
+//                               refinement)
 //                      combine  one partial (o, m, l) per query head; the last work-group of the
 //                               (sequence, kv head) merges the splits' partials with the
 //                               log-sum-exp rule (split-KV decoding, FTF Sec. 2)
