@@ -16,7 +16,7 @@ import torch
 import oracle
 from conftest import log
 from helpers import (DEV, TOL, assert_close, gpu_dense, gpu_quantize, gpu_sparse, oracle_attend,
-                     oracle_masks, upload)
+                     oracle_masks, sample_heads, upload)
 from long_context_decoding_amd import ffd
 from long_context_decoding_amd import workloads as W
 
@@ -352,5 +352,44 @@ def test_largest_block_count():
     for h in range(2):
         assert_close(out[0, h], ref[(0, h)][0], 2e-3, f"out h={h}")
         assert_close(lse[0, h], ref[(0, h)][1], 2e-3, f"lse h={h}")
+    del qd, Kd, Vd, Kq_d, sc_d
+    torch.cuda.empty_cache()
+
+
+def test_most_work_units():
+    """65528 work units, near the 65535 a call supports: 8191 sequences of one kv head with a
+    64-head query group, cut into 8 units of 8 heads each, 5 blocks of 64 tokens (block 0 the
+    sink, block 4 the local block, one needle among blocks 1-3).  Masks are compared for every
+    head of the first and last sequences and for sampled heads elsewhere; sparse and dense
+    outputs for sampled heads."""
+    w = W.Workload("max_units", B=8191, Hq=64, Hkv=1, L=5 * 64, T=64, plant="needles",
+                   n_needles=1, needle_a=6.0, sink_a=10.0, seed=91)
+    log(f"[gpu] {w.name}: generating {w.B} sequences")
+    q, K, V, _ = W.make_inputs(w)
+    qd, Kd, Vd = upload(w, q, K, V)
+    dims = ffd.dims_of(qd, Kd, w.L)
+    assert w.B * w.Hkv * (w.G // 8) == 65528
+    Kq_d, sc_d = gpu_quantize(w, Kd)
+    log(f"[gpu] {w.name}: sparse and dense")
+    out, lse, keep = gpu_sparse(w, qd, Kd, Vd, Kq_d, sc_d, 5.0)
+    out_dn, lse_dn = gpu_dense(w, qd, Kd, Vd)
+    Kq, sc = oracle.quantize_k(K, w.T, 0, w.L)
+    np.testing.assert_array_equal(Kq_d.cpu().numpy(), Kq)
+    np.testing.assert_array_equal(sc_d.cpu().numpy(), sc)
+    out_heads = sample_heads(w, 96, seed=6) + [(w.B - 1, w.Hq - 1)]
+    heads = sorted(set([(0, h) for h in range(w.Hq)] + [(w.B - 1, h) for h in range(w.Hq)]
+                       + sample_heads(w, 1024, seed=5) + out_heads))
+    ref_keep = oracle_masks(w, q, Kq, sc, 5.0, heads=heads)
+    for b, h in heads:
+        np.testing.assert_array_equal(keep[b, h], ref_keep[b, h], err_msg=f"mask b={b} h={h}")
+    # every head keeps its sink and local blocks
+    assert keep[:, :, 0].all() and keep[:, :, 4].all()
+    ref = oracle_attend(w, q, K, V, out_heads, keep=ref_keep)
+    ref_dn = oracle_attend(w, q, K, V, out_heads)
+    for b, h in out_heads:
+        assert_close(out[b, h], ref[(b, h)][0], 2e-3, f"out b={b} h={h}")
+        assert_close(lse[b, h], ref[(b, h)][1], 2e-3, f"lse b={b} h={h}")
+        assert_close(out_dn[b, h], ref_dn[(b, h)][0], 2e-3, f"dense out b={b} h={h}")
+        assert_close(lse_dn[b, h], ref_dn[(b, h)][1], 2e-3, f"dense lse b={b} h={h}")
     del qd, Kd, Vd, Kq_d, sc_d
     torch.cuda.empty_cache()
