@@ -46,6 +46,8 @@ constexpr int kResWaves = 8;  // decode waves per work-group in the residual sto
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef unsigned int u32;
 
 __device__ __forceinline__ float as_f(int x) { return __builtin_bit_cast(float, x); }
@@ -174,7 +176,8 @@ struct __attribute__((aligned(16))) WaveScratch {
     int8_t wB[2][G][4][16];  // scan MFMA B operand: [k-step][head][kg][16 int8]
     float f[G];              // per-head scan factor RN(W * kappa)
     int wsum[G];             // per-head sum of the requantized weights
-    float4 rsc[64];          // residual form: the current block's s (lanes 0-31), s_r (32-63)
+    float4 rsc[96];          // residual form: the current block's s (lanes 0-31), s_r (32-63),
+                             // -half * s (64-95)
 };
 
 // ------------------------------------------------------------------------------------------
@@ -592,9 +595,10 @@ __device__ __forceinline__ u32 byte_of(const uint4& x, int b)
     return (w >> ((b & 3) * 8)) & 255u;
 }
 
-// Scores of a residual-form tile: Dequant k = RN(RN((u - half) s) + RN(r_q s_r)) in fp32 (Alg. 1),
-// split into bf16 k_hi = RN_bf16(k) and k_lo = RN_bf16(k - k_hi) (|k - k_hi - k_lo| <= 2^-16 |k|),
-// so that q.k_quant + q.k_res accumulates on the bf16 MFMA with fp32 sums (Eq. 4).
+// Scores of a residual-form tile: Dequant k = (u - half) s + r_q s_r in fp32 (Alg. 1; two fused
+// multiply-adds, within an ulp or two of the separately rounded products and sum), split into
+// bf16 k_hi = RN_bf16(k) and k_lo = RN_bf16(k - k_hi) (|k - k_hi - k_lo| <= 2^-16 |k|), so that
+// q.k_quant + q.k_res accumulates on the bf16 MFMA with fp32 sums (Eq. 4).
 // qv: the query operand of k-step ks, channels 32 kg + 8 ks .., in registers.
 template <int BITS, int G>
 __device__ __forceinline__ v4f tile_scores_res(const TileRes& r, const v8bf* qv,
@@ -609,26 +613,49 @@ __device__ __forceinline__ v4f tile_scores_res(const TileRes& r, const v8bf* qv,
                                                           acc, 0, 0, 0);
         return acc;
     }
+    constexpr float half = (float)((1 << BITS) - 1) * 0.5f;
     ws.rsc[lane] = __builtin_bit_cast(float4, r.a[3]);
+    if (lane < 32) {
+        const float4 s4 = __builtin_bit_cast(float4, r.a[3]);
+        ws.rsc[64 + lane] = make_float4(-half * s4.x, -half * s4.y, -half * s4.z, -half * s4.w);
+    }
     wave_sync();
     const float* sq = reinterpret_cast<const float*>(ws.rsc) + kg * 32;  // s of my channels
     const float* sr = sq + 128;                                           // s_r of my channels
-    constexpr float half = (float)((1 << BITS) - 1) * 0.5f;
+    const float* nhs = sq + 256;                                          // -half * s
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         v8bf hi, lo;
+        // (u - half) s + r_q s_r evaluated as u s + (r_q s_r - half s) with fused multiply-adds
+        // (the exact stage only has to stay within the output tolerance), then the high/low
+        // split two channels at a time: one packed conversion gives both highs, whose fp32
+        // values are the packed word's halves shifted into place
+        // the codes of a dword, channel c' at bits BITS*c', spread one per byte:
+        // (word >> BITS*m) & mask holds channel (8/BITS) b + m in byte b
+        float k[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int c = 8 * ks + i;  // channel 32*kg + c
-            u32 u;
-            if constexpr (BITS == 4) u = (byte_of(r.a[0], c >> 1) >> ((c & 1) * 4)) & 15u;
-            else u = (byte_of(r.a[0], c >> 2) >> ((c & 3) * 2)) & 3u;
+            constexpr int PER = 32 / BITS;  // channels per dword
+            constexpr int PB = 8 / BITS;    // channels per byte
+            constexpr u32 M = BITS == 4 ? 0x0F0F0F0Fu : 0x03030303u;
+            const int dw = c / PER, cc = c % PER;
+            const u32 wd = dw == 0 ? r.a[0].x : dw == 1 ? r.a[0].y : dw == 2 ? r.a[0].z : r.a[0].w;
+            const u32 spread = (wd >> (BITS * (cc % PB))) & M;
+            const float u = (float)((spread >> (8 * (cc / PB))) & 0xFFu);
             const int rq = (int)(int8_t)byte_of(c < 16 ? r.a[1] : r.a[2], c & 15);
-            const float k = __fadd_rn(__fmul_rn((float)u - half, sq[c]),
-                                      __fmul_rn((float)rq, sr[c]));
-            const __bf16 kh = (__bf16)k;
-            hi[i] = kh;
-            lo[i] = (__bf16)__fsub_rn(k, (float)kh);
+            k[i] = fmaf(u, sq[c], fmaf((float)rq, sr[c], nhs[c]));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+            const v2bf h = __builtin_convertvector((v2f){k[i], k[i + 1]}, v2bf);
+            const u32 hb = __builtin_bit_cast(u32, h);
+            const v2bf l = __builtin_convertvector(
+                (v2f){k[i] - as_f((int)(hb << 16)), k[i + 1] - as_f((int)(hb & 0xFFFF0000u))}, v2bf);
+            hi[i] = h[0];
+            hi[i + 1] = h[1];
+            lo[i] = l[0];
+            lo[i + 1] = l[1];
         }
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, qv[ks], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, qv[ks], acc, 0, 0, 0);
