@@ -6,7 +6,8 @@
 2. The C-ABI layer (long_context_decoding_amd/csrc/ffd_api.cpp: validation, split heuristic,
    workspace layout) is built host-only with g++ and the same sanitizers, its kernel launchers
    replaced by counting stubs (tests/sanitize/launch_stubs.cpp); tests/test_abi.py runs against it,
-   then a set of valid calls that reach the (stub) launchers.
+   then a set of valid calls that reach the (stub) launchers, and every launching entry point
+   once more with its launch made to fail, which must return FFD_ERR_HIP.
 
 Any sanitizer report aborts the subprocess (halt_on_error, no recovery), which fails the test.  A
 negative control checks that the harness does report a planted heap overflow.
@@ -119,6 +120,40 @@ def test_abi_layer_under_sanitizers(tmp_path):
             assert L.ffd_decode_sparse_noalloc(ctypes.byref(d), A, A, A, A, A, 5.0, T, A, A,
                                                None, None) in (0, 3)
             assert n() > before
+        # every launching entry point maps a failed launch (or scratch-area lookup) to
+        # FFD_ERR_HIP, and the failure does not stick to the next call
+        fail = ctypes.CDLL({str(lib)!r}).ffd_stub_fail_next
+        T = 128
+        d = ffd.make_dims(1, 32, 8, 4096, 4096, ffd.FFD_BF16)
+        ws = ffd.workspace_bytes(d, T)
+        D = ctypes.byref(d)
+        calls = {{
+            "decode_sparse": lambda: L.ffd_decode_sparse(D, A, A, A, A, A, 5.0, T, A, A, A, A, ws, None),
+            "decode_dense": lambda: L.ffd_decode_dense(D, A, A, A, T, A, A, A, ws, None),
+            "decode_masked": lambda: L.ffd_decode_masked(D, A, A, A, A, T, A, A, A, ws, None),
+            "decode_sparse_running": lambda: L.ffd_decode_sparse_running(
+                D, A, A, A, A, A, 5.0, T, 8, A, A, None, A, 1 << 40, None),
+            "decode_sparse_noalloc": lambda: L.ffd_decode_sparse_noalloc(
+                D, A, A, A, A, A, 5.0, T, A, A, None, None),
+            "decode_sparse_residual": lambda: L.ffd_decode_sparse_residual(
+                D, A, None, A, A, A, A, A, 2, 5.0, T, A, A, None, A, ws, None),
+            "decode_sparse_varlen": lambda: L.ffd_decode_sparse_varlen(
+                D, A, A, A, A, A, A, 5.0, T, A, A, None, A, ws, None),
+            "decode_dense_varlen": lambda: L.ffd_decode_dense_varlen(D, A, A, A, A, T, A, A, A, ws, None),
+            "quantize_k_append": lambda: L.ffd_quantize_k_append(D, A, 0, 4096, T, A, A, None),
+            "quantize_k_residual_append": lambda: L.ffd_quantize_k_residual_append(
+                D, A, 0, 4096, T, 2, A, A, A, A, None),
+            "append_token": lambda: L.ffd_append_token(D, A, A, A, A, A, T, A, A, None),
+            "workspace_init": lambda: L.ffd_workspace_init(D, T, A, ws, None),
+            "block_bounds": lambda: L.ffd_block_bounds(D, A, 0, 4096, T, A, A, None),
+            "block_scores": lambda: L.ffd_block_scores(D, 0, A, A, A, A, A, A, T, A, None),
+            "select_blocks": lambda: L.ffd_select_blocks(D, 1, A, None, 3.0, T, A, None),
+        }}
+        for name, call in calls.items():
+            assert call() == 0, (name, "with working launches")
+            fail(1)
+            assert call() == 4, (name, "with a failed launch")
+            assert call() == 0, (name, "after a failed launch")
         sys.exit(0)
     """)
     _assert_clean(res)
