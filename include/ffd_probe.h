@@ -16,7 +16,8 @@ extern "C" {
 
 /*
  * Streaming read of `bytes` bytes at `src`, split into n_groups contiguous chunks, one work-group
- * of 256 threads each (16-byte loads, eight in flight per lane).  Work-group g writes the XOR of
+ * of 256 threads each (16-byte loads with the streaming cache policy, eight in flight per lane).
+ * Work-group g writes the XOR of
  * the 16-byte words of its chunk to sink[16 g .. 16 g + 15], so sink holds n_groups * 16 bytes.
  *   src, sink  caller-owned device memory, 16-byte aligned
  *   bytes      a positive multiple of 16

@@ -187,6 +187,7 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
     p.n_blocks = (dims->seq_len + block - 1) / block;
     p.S = S;
     p.R = window != 0 ? window : (p.n_blocks + S - 1) / S;
+    p.stream = p.R >= (sparse ? ffd::kStreamBlocks : ffd::kStreamBlocksDense) ? 1 : 0;
     p.running = window != 0 ? 1 : 0;
     p.seq_lens = seq_lens;
     p.mask_stride = p.n_blocks;

@@ -57,7 +57,18 @@ struct DecodeParams {
                               // sparse kernel then attends over these blocks and scans nothing
     int running;              // sparse: top-delta against the running maximum of each split (the
                               // splits are then the caller's windows of R blocks)
+    int stream;               // the launch uses the kernels whose streamed reads (the scan's codes
+                              // and scales, the exact stage's values, the dense step's keys) take
+                              // the streaming (non-temporal) cache policy: set for long splits
 };
+
+// Splits of at least this many blocks run the streaming-policy kernels.  Measured (alternating
+// builds, graph replay): sparse 128K x 8 (256 blocks per split) 214 -> 193 us, 256K (64 blocks)
+// 33.4 -> 31.3 us, 128K (32 blocks) 22.3 -> 20.8 us; slower on shorter splits, whose steps are
+// bound by latency (32K, 8 blocks: +0.2 us; 4K: +0.6 us).  The dense step gains from 4 blocks per
+// split (32K: 31.5 -> 28.6 us; 256K: 183 -> 155 us) and not on 2 (a 4K-token fp32 head).
+constexpr int kStreamBlocks = 32;
+constexpr int kStreamBlocksDense = 4;
 
 struct QuantParams {
     const void* K;

@@ -48,6 +48,35 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+
+// Loads of data that is read once (the scan's codes and scales, the exact stage's values, the
+// dense step's keys and values) can use the streaming (non-temporal) cache policy, which streams
+// faster on this chip (decode_kernel's STREAM variants, launched for long splits:
+// kStreamBlocks).  The kept keys of the sparse step stay on the default policy (measured slower
+// with streaming loads).
+template <bool B>
+struct Flag {
+    static constexpr bool value = B;
+};
+// 16-byte load (streaming cache policy when NT)
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const void* p)
+{
+    if constexpr (NT) {
+        typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
+        const v4u_t x = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(p));
+        return make_uint4(x[0], x[1], x[2], x[3]);
+    } else {
+        return *reinterpret_cast<const uint4*>(p);
+    }
+}
+template <bool NT>
+__device__ __forceinline__ float4 ld16f(const void* p)
+{
+    const uint4 u = ld16<NT>(p);
+    return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                       __uint_as_float(u.w));
+}
 typedef unsigned int u32;
 
 __device__ __forceinline__ float as_f(int x) { return __builtin_bit_cast(float, x); }
@@ -200,19 +229,27 @@ struct ScanRegs {
     float4 s0, s1;                              // scales of channels 8*col .. 8*col+7
 };
 
-template <int T, int BITS>
+template <int T, int BITS, bool NT>
 __device__ __forceinline__ void scan_load(ScanRegs<T, BITS>& r, const uint8_t* __restrict__ kq_blk,
                                           const float* __restrict__ sc_blk, int lane)
 {
     const int col = lane & 15, kg = lane >> 4;
     constexpr int RB = D * BITS / 8, CB = 32 * BITS / 8;  // bytes per row, per 32 channels
 #pragma unroll
-    for (int i = 0; i < T / 16; ++i)
-        r.kq[i] = *reinterpret_cast<const typename CodeSlice<BITS>::type*>(
-            kq_blk + (size_t)(i * 16 + col) * RB + kg * CB);
-    const float4* sp = reinterpret_cast<const float4*>(sc_blk + col * 8);
-    r.s0 = sp[0];
-    r.s1 = sp[1];
+    for (int i = 0; i < T / 16; ++i) {
+        const uint8_t* a = kq_blk + (size_t)(i * 16 + col) * RB + kg * CB;
+        if constexpr (BITS == 4) {
+            r.kq[i] = ld16<NT>(a);
+        } else if constexpr (NT) {
+            typedef u32 v2u_t __attribute__((ext_vector_type(2)));
+            const v2u_t x = __builtin_nontemporal_load(reinterpret_cast<const v2u_t*>(a));
+            r.kq[i] = make_uint2(x[0], x[1]);
+        } else {
+            r.kq[i] = *reinterpret_cast<const uint2*>(a);
+        }
+    }
+    r.s0 = ld16f<NT>(sc_blk + col * 8);
+    r.s1 = ld16f<NT>(sc_blk + col * 8 + 4);
 }
 
 // Estimated block maximum of every query head of the group.  Requantization lanes: row kg
@@ -333,7 +370,7 @@ struct TileRegs<false> {
     float4 v[8];  // token 4*kg + i/2, channels 8*col + 4*(i%2) ..
 };
 
-template <bool BF16>
+template <bool BF16, bool NTK, bool NTV>
 __device__ __forceinline__ void tile_load(TileRegs<BF16>& r, const void* __restrict__ Kbg,
                                           const void* __restrict__ Vbg, int t0, int lane)
 {
@@ -343,20 +380,20 @@ __device__ __forceinline__ void tile_load(TileRegs<BF16>& r, const void* __restr
         const __bf16* Vp = static_cast<const __bf16*>(Vbg);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-            r.k[ks] = *reinterpret_cast<const uint4*>(Kp + (size_t)(t0 + col) * D + ks * 32 + kg * 8);
+            r.k[ks] = ld16<NTK>(Kp + (size_t)(t0 + col) * D + ks * 32 + kg * 8);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            r.v[i] = *reinterpret_cast<const uint4*>(Vp + (size_t)(t0 + 4 * kg + i) * D + col * 8);
+            r.v[i] = ld16<NTV>(Vp + (size_t)(t0 + 4 * kg + i) * D + col * 8);
     } else {
         const float* Kp = static_cast<const float*>(Kbg);
         const float* Vp = static_cast<const float*>(Vbg);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            r.k[i] = *reinterpret_cast<const float4*>(Kp + (size_t)(t0 + col) * D + kg * 32 + i * 4);
+            r.k[i] = ld16f<NTK>(Kp + (size_t)(t0 + col) * D + kg * 32 + i * 4);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            r.v[i] = *reinterpret_cast<const float4*>(Vp + (size_t)(t0 + 4 * kg + i / 2) * D +
-                                                      col * 8 + (i & 1) * 4);
+            r.v[i] = ld16f<NTV>(Vp + (size_t)(t0 + 4 * kg + i / 2) * D + col * 8 +
+                                        (i & 1) * 4);
     }
 }
 
@@ -542,7 +579,7 @@ struct TileRes {
     uint4 v[4];  // as TileRegs<true>::v
 };
 
-template <int BITS>
+template <int BITS, bool NT>
 __device__ __forceinline__ void tile_load_res(TileRes& r, const uint8_t* __restrict__ kc_bg,
                                               const float* __restrict__ sc_bg,
                                               const int8_t* __restrict__ kr_bg,
@@ -581,12 +618,12 @@ __device__ __forceinline__ void tile_load_res(TileRes& r, const uint8_t* __restr
         const uint2 hi = *reinterpret_cast<const uint2*>(tail ? a0 + 8 : a0);
         r.a[0] = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
-    r.a[1] = *reinterpret_cast<const uint4*>(a1);
-    r.a[2] = *reinterpret_cast<const uint4*>(a2);
+    r.a[1] = ld16<false>(a1);
+    r.a[2] = ld16<false>(a2);
     r.a[3] = *reinterpret_cast<const uint4*>(a3);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        r.v[i] = *reinterpret_cast<const uint4*>(V_bg + (size_t)(t0 + 4 * kg + i) * D + col * 8);
+        r.v[i] = ld16<NT>(V_bg + (size_t)(t0 + 4 * kg + i) * D + col * 8);
 }
 
 __device__ __forceinline__ u32 byte_of(const uint4& x, int b)
@@ -791,7 +828,7 @@ __device__ __forceinline__ float2 ld_dev8(rsrc_t r, int off)
 //      with the log-sum-exp rule into out and lse, and resets the counter.
 // BITS is the width of the scanned codes; RES selects the residual storage form (thumbnail +
 // 8-bit residual instead of stored keys; bf16 values; sparse only).
-template <int T, int G, bool BF16, bool SPARSE, int BITS, bool RES>
+template <int T, int G, bool BF16, bool SPARSE, int BITS, bool RES, bool STREAM>
 __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_kernel(DecodeParams p)
 {
     // waves per work-group: eight in the residual form, whose exact tiles cost more arithmetic
@@ -912,10 +949,10 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
             };
             if (n_items > 0) {
                 float pro0 = 0.0f, theta = 0.0f;  // lanes < G: head = lane
-                auto load = [&](ScanRegs<T, BITS>& r, int k) {
+                auto load = [&](ScanRegs<T, BITS>& r, int k, auto nt) {
                     const int j = block_of(k);
-                    scan_load<T, BITS>(r, kq_bg + (size_t)j * T * (D * BITS / 8), sc_bg + (size_t)j * D,
-                                       lane);
+                    scan_load<T, BITS, decltype(nt)::value>(
+                        r, kq_bg + (size_t)j * T * (D * BITS / 8), sc_bg + (size_t)j * D, lane);
                 };
                 auto process = [&](const ScanRegs<T, BITS>& r, int k) {
                     const float shat = scan_compute<T, G, BITS>(r, qw, p.kappa, ws, lane);
@@ -944,27 +981,30 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
                 // issued before the computation that follows it in program order (otherwise the
                 // scheduler hoists that computation's first use of its buffer above the loads, and
                 // the in-order wait counter then waits for the prefetch too).
-                ScanRegs<T, BITS> ra, rb;
-                load(ra, 0);
-                __builtin_amdgcn_sched_barrier(0);
-                publish_q();
-                int k = 0;
-                for (; k + 2 < n_items; k += 2) {
-                    load(rb, k + 1);
+                auto pipeline = [&](auto nt) {
+                    ScanRegs<T, BITS> ra, rb;
+                    load(ra, 0, nt);
                     __builtin_amdgcn_sched_barrier(0);
-                    process(ra, k);
-                    load(ra, k + 2);
-                    __builtin_amdgcn_sched_barrier(0);
-                    process(rb, k + 1);
-                }
-                if (k + 1 < n_items) {
-                    load(rb, k + 1);
-                    __builtin_amdgcn_sched_barrier(0);
-                    process(ra, k);
-                    process(rb, k + 1);
-                } else {
-                    process(ra, k);
-                }
+                    publish_q();
+                    int k = 0;
+                    for (; k + 2 < n_items; k += 2) {
+                        load(rb, k + 1, nt);
+                        __builtin_amdgcn_sched_barrier(0);
+                        process(ra, k);
+                        load(ra, k + 2, nt);
+                        __builtin_amdgcn_sched_barrier(0);
+                        process(rb, k + 1);
+                    }
+                    if (k + 1 < n_items) {
+                        load(rb, k + 1, nt);
+                        __builtin_amdgcn_sched_barrier(0);
+                        process(ra, k);
+                        process(rb, k + 1);
+                    } else {
+                        process(ra, k);
+                    }
+                };
+                pipeline(Flag<STREAM>{});
             } else {
                 publish_q();
             }
@@ -1082,16 +1122,19 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
             // residual form: tiles of full blocks are rebuilt from thumbnail + residual, the tiles
             // of a partial tail block (no low-bit copy) read the 16-bit keys
             const int full_end = nf_b * T;
-            auto load_tile = [&](TR& r, int t0) {
+            // STREAM: the streaming policy for the values (and, in the dense step, the keys); the
+            // kept keys of the sparse step keep the default policy (measured slower otherwise)
+            auto load_tile = [&](TR& r, int t0, auto nt) {
+                constexpr bool NT = decltype(nt)::value;
                 if constexpr (RES)
-                    tile_load_res<BITS>(
+                    tile_load_res<BITS, NT>(
                         r, p.Kq + (size_t)bg * p.cap * (D * BITS / 8),
                         p.scales + (size_t)bg * (p.cap / T) * D, p.Kr + (size_t)bg * p.cap * D,
                         p.res_scales + (size_t)bg * (p.cap / T) * D,
                         reinterpret_cast<const __bf16*>(Kbg), reinterpret_cast<const __bf16*>(Vbg),
                         t0, T, t0 >= full_end, lane);
                 else
-                    tile_load<BF16>(r, Kbg, Vbg, t0, lane);
+                    tile_load<BF16, NT && !SPARSE, NT>(r, Kbg, Vbg, t0, lane);
             };
             auto compute_tile = [&](const TR& r, int t0, u32 kb) {
                 if constexpr (RES)
@@ -1100,31 +1143,34 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
                 else
                     tile_compute<G, BF16>(r, qrow, qv, st, t0, L_b, kb, p.c_log2, lane);
             };
-            TR ta, tb;
-            int t0a, t0b;
-            u32 kba, kbb;
-            tile_of(0, t0a, kba);
-            load_tile(ta, t0a);
-            int k = 0;
-            for (; k + 2 < n_w; k += 2) {
-                tile_of(k + 1, t0b, kbb);
-                load_tile(tb, t0b);
-                __builtin_amdgcn_sched_barrier(0);
-                compute_tile(ta, t0a, kba);
-                tile_of(k + 2, t0a, kba);
-                load_tile(ta, t0a);
-                __builtin_amdgcn_sched_barrier(0);
-                compute_tile(tb, t0b, kbb);
-            }
-            if (k + 1 < n_w) {
-                tile_of(k + 1, t0b, kbb);
-                load_tile(tb, t0b);
-                __builtin_amdgcn_sched_barrier(0);
-                compute_tile(ta, t0a, kba);
-                compute_tile(tb, t0b, kbb);
-            } else {
-                compute_tile(ta, t0a, kba);
-            }
+            auto pipeline = [&](auto nt) {
+                TR ta, tb;
+                int t0a, t0b;
+                u32 kba, kbb;
+                tile_of(0, t0a, kba);
+                load_tile(ta, t0a, nt);
+                int k = 0;
+                for (; k + 2 < n_w; k += 2) {
+                    tile_of(k + 1, t0b, kbb);
+                    load_tile(tb, t0b, nt);
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute_tile(ta, t0a, kba);
+                    tile_of(k + 2, t0a, kba);
+                    load_tile(ta, t0a, nt);
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute_tile(tb, t0b, kbb);
+                }
+                if (k + 1 < n_w) {
+                    tile_of(k + 1, t0b, kbb);
+                    load_tile(tb, t0b, nt);
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute_tile(ta, t0a, kba);
+                    compute_tile(tb, t0b, kbb);
+                } else {
+                    compute_tile(ta, t0a, kba);
+                }
+            };
+            pipeline(Flag<STREAM>{});
         }
     }
 
@@ -1669,14 +1715,25 @@ __global__ __launch_bounds__(256) void quantize_res_kernel(QuantParams p)
     }
 }
 
+// The streaming-policy kernels (p.stream, set for long splits) exist for 16-bit inputs only.
 template <int T, int G, bool BF16>
 hipError_t launch_decode_t(const DecodeParams& p, bool sparse, hipStream_t stream)
 {
     const dim3 grid(p.B * p.Hkv * p.NSUB * p.S), block(kWaves * 64);
-    if (sparse)
-        hipLaunchKernelGGL((decode_kernel<T, G, BF16, true, 4, false>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((decode_kernel<T, G, BF16, false, 4, false>), grid, block, 0, stream, p);
+    if (BF16 && p.stream) {
+        if (sparse)
+            hipLaunchKernelGGL((decode_kernel<T, G, BF16, true, 4, false, BF16>), grid, block, 0,
+                               stream, p);
+        else
+            hipLaunchKernelGGL((decode_kernel<T, G, BF16, false, 4, false, BF16>), grid, block, 0,
+                               stream, p);
+    } else if (sparse) {
+        hipLaunchKernelGGL((decode_kernel<T, G, BF16, true, 4, false, false>), grid, block, 0,
+                           stream, p);
+    } else {
+        hipLaunchKernelGGL((decode_kernel<T, G, BF16, false, 4, false, false>), grid, block, 0,
+                           stream, p);
+    }
     return hipGetLastError();
 }
 
@@ -1692,18 +1749,23 @@ hipError_t launch_decode_g(const DecodeParams& p, bool sparse, hipStream_t strea
     }
 }
 
-template <int T, int BITS>
-hipError_t launch_res_g(const DecodeParams& p, hipStream_t stream)
+template <int T, int BITS, bool STREAM>
+hipError_t launch_res_s(const DecodeParams& p, hipStream_t stream)
 {
     const dim3 grid(p.B * p.Hkv * p.NSUB * p.S), block(kResWaves * 64);
     switch (p.GP) {
-    case 1: hipLaunchKernelGGL((decode_kernel<T, 1, true, true, BITS, true>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<T, 2, true, true, BITS, true>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<T, 4, true, true, BITS, true>), grid, block, 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<T, 8, true, true, BITS, true>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<T, 1, true, true, BITS, true, STREAM>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<T, 2, true, true, BITS, true, STREAM>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<T, 4, true, true, BITS, true, STREAM>), grid, block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<T, 8, true, true, BITS, true, STREAM>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+template <int T, int BITS>
+hipError_t launch_res_g(const DecodeParams& p, hipStream_t stream)
+{
+    return p.stream ? launch_res_s<T, BITS, true>(p, stream) : launch_res_s<T, BITS, false>(p, stream);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1799,7 +1861,7 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(ScoreParams p)
         const float* sc_bg = p.scales + (size_t)bg * (p.cap / T) * D;
         for (int j = j0 + w; j < j1; j += kWaves) {
             ScanRegs<T, 4> r;
-            scan_load<T, 4>(r, kq_bg + (size_t)j * T * (D / 2), sc_bg + (size_t)j * D, lane);
+            scan_load<T, 4, false>(r, kq_bg + (size_t)j * T * (D / 2), sc_bg + (size_t)j * D, lane);
             const float shat = scan_compute<T, G, 4>(r, qw, p.kappa, wsh[w], lane);
             if (lane < nh) p.scores[(size_t)(h0 + lane) * p.n_full + j] = shat;
         }

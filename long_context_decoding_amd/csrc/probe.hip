@@ -4,7 +4,8 @@
 // the ceiling the decode kernels are compared with beside the vendor peak.  Each work-group
 // reads one contiguous chunk of the buffer with 16-byte loads (eight in flight per lane) and
 // writes the XOR of the 16-byte words it read, so that no load can be optimised away and the
-// result can be checked.
+// result can be checked.  The loads use the streaming (non-temporal) cache policy, which reads
+// faster on this chip than the default one (as the decode kernels' streamed reads do).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,7 +28,13 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __re
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const size_t k = i + (size_t)u * kThreads;
-            v[u] = k < end ? src[k] : make_uint4(0u, 0u, 0u, 0u);
+            if (k < end) {
+                typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
+                const v4u_t x = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(src + k));
+                v[u] = make_uint4(x[0], x[1], x[2], x[3]);
+            } else {
+                v[u] = make_uint4(0u, 0u, 0u, 0u);
+            }
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
