@@ -7,13 +7,18 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libffd.so"
-SOURCES = [CSRC / "ffd_kernels.hip", CSRC / "ffd_scratch.hip", CSRC / "ffd_api.cpp"]
+# ffd_kernels_stream.hip compiles the second half of ffd_kernels.hip (the streaming-policy decode
+# kernels); the translation units compile in parallel
+SOURCES = [CSRC / "ffd_kernels.hip", CSRC / "ffd_kernels_stream.hip", CSRC / "ffd_scratch.hip",
+           CSRC / "ffd_api.cpp"]
 HEADERS = [CSRC / "ffd_internal.h", ROOT / "include" / "ffd.h"]
 PROBE_LIB = PKG / "libffd_probe.so"
 PROBE_SOURCES = [CSRC / "probe.hip"]
@@ -41,9 +46,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(lib: Path, sources, verbose: bool) -> Path:
-    tmp = lib.with_suffix(".so.tmp")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", str(tmp), *map(str, sources)]
+def _run(cmd, verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,6 +56,18 @@ def _compile(lib: Path, sources, verbose: bool) -> Path:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
+
+
+def _compile(lib: Path, sources, verbose: bool) -> Path:
+    """Each source to an object (in parallel), then one shared library."""
+    tmp = lib.with_suffix(".so.tmp")
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="ffd_build_") as td:
+        objs = [str(Path(td) / (Path(src).name + ".o")) for src in sources]
+        with ThreadPoolExecutor(max_workers=len(sources)) as ex:
+            list(ex.map(lambda so: _run([hipcc(), *compile_flags, "-c", "-o", so[1], str(so[0])],
+                                        verbose), zip(sources, objs)))
+        _run([hipcc(), *HIPCC_FLAGS, "-o", str(tmp), *objs], verbose)
     os.replace(tmp, lib)
     return lib
 

@@ -137,6 +137,9 @@ hipError_t launch_quantize(const QuantParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_decode_res(const DecodeParams& p, int bits, hipStream_t stream);
 hipError_t launch_quantize_res(const QuantParams& p, int bits, hipStream_t stream);
 hipError_t launch_zero_counters(uint32_t* counters, int n, hipStream_t stream);
+// the streaming-policy decode kernels (bf16 inputs, p.stream set), in their own translation unit
+hipError_t launch_decode_stream(const DecodeParams& p, bool sparse, hipStream_t stream);
+hipError_t launch_decode_res_stream(const DecodeParams& p, int bits, hipStream_t stream);
 
 // The current device's fixed scratch area (kScratchBytes, 256-byte aligned; ffd_scratch.hip):
 // its device address, looked up at the first call on the device, when its first counter_bytes

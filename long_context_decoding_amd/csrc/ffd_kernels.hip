@@ -36,6 +36,13 @@
 
 #include "ffd_internal.h"
 
+// This file is compiled twice: as itself (FFD_PART 0: every kernel but the streaming-policy decode
+// kernels, and every launcher) and through ffd_kernels_stream.hip (FFD_PART 1: the streaming-policy
+// decode kernels and their launchers), so that the two halves compile in parallel.
+#ifndef FFD_PART
+#define FFD_PART 0
+#endif
+
 namespace ffd {
 namespace {
 
@@ -1430,11 +1437,13 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
     }
 }
 
+#if FFD_PART == 0
 __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ p, int n)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0u;
 }
+#endif
 
 // ------------------------------------------------------------------------------------------
 // App. A quantizer, 16 levels, of key block j of slice bg: one thread per channel c (a
@@ -1716,17 +1725,25 @@ __global__ __launch_bounds__(256) void quantize_res_kernel(QuantParams p)
 }
 
 // The streaming-policy kernels (p.stream, set for long splits) exist for 16-bit inputs only.
+template <int T, int G>
+hipError_t launch_stream_t(const DecodeParams& p, bool sparse, hipStream_t stream)
+{
+    const dim3 grid(p.B * p.Hkv * p.NSUB * p.S), block(kWaves * 64);
+    if (sparse)
+        hipLaunchKernelGGL((decode_kernel<T, G, true, true, 4, false, true>), grid, block, 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((decode_kernel<T, G, true, false, 4, false, true>), grid, block, 0,
+                           stream, p);
+    return hipGetLastError();
+}
+
 template <int T, int G, bool BF16>
 hipError_t launch_decode_t(const DecodeParams& p, bool sparse, hipStream_t stream)
 {
     const dim3 grid(p.B * p.Hkv * p.NSUB * p.S), block(kWaves * 64);
     if (BF16 && p.stream) {
-        if (sparse)
-            hipLaunchKernelGGL((decode_kernel<T, G, BF16, true, 4, false, BF16>), grid, block, 0,
-                               stream, p);
-        else
-            hipLaunchKernelGGL((decode_kernel<T, G, BF16, false, 4, false, BF16>), grid, block, 0,
-                               stream, p);
+        return launch_decode_stream(p, sparse, stream);  // the other half of this file
     } else if (sparse) {
         hipLaunchKernelGGL((decode_kernel<T, G, BF16, true, 4, false, false>), grid, block, 0,
                            stream, p);
@@ -1765,7 +1782,7 @@ hipError_t launch_res_s(const DecodeParams& p, hipStream_t stream)
 template <int T, int BITS>
 hipError_t launch_res_g(const DecodeParams& p, hipStream_t stream)
 {
-    return p.stream ? launch_res_s<T, BITS, true>(p, stream) : launch_res_s<T, BITS, false>(p, stream);
+    return p.stream ? launch_decode_res_stream(p, BITS, stream) : launch_res_s<T, BITS, false>(p, stream);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -2125,6 +2142,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p)
 
 }  // namespace
 
+#if FFD_PART == 0
 hipError_t launch_decode(const DecodeParams& p, bool bf16, bool sparse, hipStream_t stream)
 {
     if (p.T == 64)
@@ -2260,5 +2278,31 @@ hipError_t launch_select(const SelectParams& p, int rule, hipStream_t stream)
         hipLaunchKernelGGL(select_kernel<2>, dim3(p.rows), dim3(256), dyn, stream, p);
     return hipGetLastError();
 }
+
+#else  // FFD_PART == 1
+hipError_t launch_decode_stream(const DecodeParams& p, bool sparse, hipStream_t stream)
+{
+    switch (p.T * 16 + p.GP) {
+    case 64 * 16 + 1: return launch_stream_t<64, 1>(p, sparse, stream);
+    case 64 * 16 + 2: return launch_stream_t<64, 2>(p, sparse, stream);
+    case 64 * 16 + 4: return launch_stream_t<64, 4>(p, sparse, stream);
+    case 64 * 16 + 8: return launch_stream_t<64, 8>(p, sparse, stream);
+    case 128 * 16 + 1: return launch_stream_t<128, 1>(p, sparse, stream);
+    case 128 * 16 + 2: return launch_stream_t<128, 2>(p, sparse, stream);
+    case 128 * 16 + 4: return launch_stream_t<128, 4>(p, sparse, stream);
+    case 128 * 16 + 8: return launch_stream_t<128, 8>(p, sparse, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode_res_stream(const DecodeParams& p, int bits, hipStream_t stream)
+{
+    if (p.T == 64)
+        return bits == 2 ? launch_res_s<64, 2, true>(p, stream) : launch_res_s<64, 4, true>(p, stream);
+    if (p.T == 128)
+        return bits == 2 ? launch_res_s<128, 2, true>(p, stream) : launch_res_s<128, 4, true>(p, stream);
+    return hipErrorInvalidValue;
+}
+#endif
 
 }  // namespace ffd

@@ -30,23 +30,31 @@ pytestmark = pytest.mark.skipif(not shutil.which(B.hipcc()) and not B.Path(B.hip
 
 @pytest.fixture(scope="module")
 def kernels(tmp_path_factory):
-    out = tmp_path_factory.mktemp("isa") / "ffd_kernels.s"
+    # both translation units of the kernels (the default-policy and the streaming-policy halves)
+    td = tmp_path_factory.mktemp("isa")
     flags = [f for f in B.HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
-    res = subprocess.run([B.hipcc(), *flags, "-S", "--offload-device-only", "-o", str(out),
-                          str(B.CSRC / "ffd_kernels.hip")], capture_output=True, text=True)
-    assert res.returncode == 0, res.stderr[-4000:]
-    s = out.read_text()
+    srcs = [B.CSRC / "ffd_kernels.hip", B.CSRC / "ffd_kernels_stream.hip"]
+    procs = [subprocess.Popen([B.hipcc(), *flags, "-S", "--offload-device-only", "-o",
+                               str(td / (src.name + ".s")), str(src)],
+                              stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+             for src in srcs]
+    for pr in procs:
+        _, err = pr.communicate()
+        assert pr.returncode == 0, err[-4000:]
     bodies = {}
-    for m in re.finditer(r"^(_Z\w+):\s*(?:;.*)?$", s, re.M):
-        end = s.find(".Lfunc_end", m.end())
-        bodies[m.group(1)] = [l.strip() for l in s[m.end():end].splitlines()]
+    for src in srcs:
+        s = (td / (src.name + ".s")).read_text()
+        for m in re.finditer(r"^(_Z\w+):\s*(?:;.*)?$", s, re.M):
+            end = s.find(".Lfunc_end", m.end())
+            bodies[m.group(1)] = [l.strip() for l in s[m.end():end].splitlines()]
     return {n: b for n, b in bodies.items() if "decode_kernel" in n}
 
 
 def test_all_decode_kernels_found(kernels):
-    # T in {64, 128} x G in {1, 2, 4, 8} x {bf16, fp32} x {sparse, dense} stored-key kernels plus
-    # T x G x BITS in {2, 4} residual-form kernels
-    assert len(kernels) >= 48, sorted(kernels)
+    # T in {64, 128} x G in {1, 2, 4, 8} x {bf16, fp32} x {sparse, dense} stored-key kernels and
+    # T x G x BITS in {2, 4} residual-form kernels, each with the default cache policy; the bf16
+    # stored-key and residual-form ones also with the streaming policy
+    assert len(kernels) == 80, sorted(kernels)
 
 
 def test_partials_travel_at_device_scope(kernels):
