@@ -10,7 +10,8 @@ numpy arrays.  See that file's header for what each stage computes and which pas
 "Faster Than Flash: Exploiting Attention Sparsity for Efficient Long-Context Decoding" it follows.
 
 Array conventions: bf16 tensors are numpy ``uint16`` arrays holding bf16 bit patterns; fp32
-tensors are ``float32``.
+tensors are ``float32``.  Block scales of the low-bit key copies are stored as bf16 (``uint16``);
+the residual scales of the storage form are ``float32``.
 """
 from __future__ import annotations
 
@@ -54,6 +55,8 @@ def _load():
     i32 = ctypes.c_int
     f32 = ctypes.c_float
     lib.ffdo_version.restype = i32
+    lib.ffdo_round_bf16.argtypes = [P, P, i32]
+    lib.ffdo_round_bf16.restype = None
     lib.ffdo_quantize_channel.argtypes = [P, i32, i32, i32, P, P]
     lib.ffdo_quantize_channel.restype = None
     lib.ffdo_quantize_k.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P]
@@ -100,6 +103,21 @@ def _dtype_code(a: np.ndarray) -> int:
     raise TypeError(f"oracle takes float32 or bf16-bits (uint16) arrays, got {a.dtype}")
 
 
+def _need_bf16(a: np.ndarray, name: str) -> np.ndarray:
+    if a.dtype != np.uint16:
+        raise TypeError(f"{name}: block scales are bf16 bits (uint16), got {a.dtype}")
+    return np.ascontiguousarray(a)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 values rounded to bf16 (nearest, ties to even) -> bf16 bits (uint16), as the
+    block scales are stored."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty(x.shape, dtype=np.uint16)
+    _load().ffdo_round_bf16(_ptr(x), _ptr(y), x.size)
+    return y
+
+
 def to_f32(a: np.ndarray) -> np.ndarray:
     """Values of an fp32 or bf16-bits array as float32."""
     if a.dtype == np.uint16:
@@ -125,7 +143,8 @@ def quantize_channel(x: np.ndarray, bits: int):
 
 def quantize_k(K: np.ndarray, T: int, tok_begin: int = 0, tok_end: int | None = None,
                Kq: np.ndarray | None = None, scales: np.ndarray | None = None):
-    """Quantize the completed blocks of K [B, Hkv, L_cap, d] -> (Kq u8 [..., d/2], scales f32)."""
+    """Quantize the completed blocks of K [B, Hkv, L_cap, d] -> (Kq u8 [..., d/2], scales bf16
+    bits u16 [..., L_cap/T, d])."""
     B, Hkv, L_cap, d = K.shape
     if tok_end is None:
         tok_end = L_cap
@@ -133,7 +152,8 @@ def quantize_k(K: np.ndarray, T: int, tok_begin: int = 0, tok_end: int | None = 
     if Kq is None:
         Kq = np.zeros((B, Hkv, L_cap, d // 2), dtype=np.uint8)
     if scales is None:
-        scales = np.zeros((B, Hkv, L_cap // T, d), dtype=np.float32)
+        scales = np.zeros((B, Hkv, L_cap // T, d), dtype=np.uint16)
+    _need_bf16(scales, "scales")
     lib = _load()
     dt = _dtype_code(K)
     for b in range(B):
@@ -164,7 +184,7 @@ def scan_head(qh: np.ndarray, Kq_slice: np.ndarray, scales_slice: np.ndarray, n_
     qh = np.ascontiguousarray(to_f32(qh))
     d = qh.shape[0]
     Kq_slice = np.ascontiguousarray(Kq_slice)
-    scales_slice = np.ascontiguousarray(scales_slice)
+    scales_slice = _need_bf16(scales_slice, "scales")
     sb = np.empty(max(n_full, 1), dtype=np.float32)
     st = np.empty(max(n_full * T, 1), dtype=np.float32) if per_token else None
     Et = np.empty(max(n_full * T, 1), dtype=np.int32) if per_token else None
@@ -223,7 +243,7 @@ def decode(q, K, V, L: int, T: int, delta: float = float("inf"), Kq=None, scales
         if Kq is None or scales is None:
             raise ValueError("sparse decode needs Kq and scales")
         Kq = np.ascontiguousarray(Kq)
-        scales = np.ascontiguousarray(scales)
+        scales = _need_bf16(scales, "scales")
         keep = np.empty((B, Hq, max(n_blocks, 1)), dtype=np.uint8)
         mtilde = np.empty((B, Hq), dtype=np.float32)
         if want_shat:
@@ -258,17 +278,18 @@ def quantize_residual(r: np.ndarray):
 def quantize_k_res(K: np.ndarray, T: int, bits: int, tok_begin: int = 0, tok_end: int | None = None,
                    out=None):
     """Thumbnail + residual of the completed blocks of K [B, Hkv, L_cap, d] ->
-    (Kc u8 [.., d*bits/8], sc f32 [.., L_cap/T, d], Kr i8 [.., d], sr f32 [.., L_cap/T, d])."""
+    (Kc u8 [.., d*bits/8], sc bf16 bits u16 [.., L_cap/T, d], Kr i8 [.., d], sr f32 [.., L_cap/T, d])."""
     B, Hkv, L_cap, d = K.shape
     if tok_end is None:
         tok_end = L_cap
     K = np.ascontiguousarray(K)
     if out is None:
         out = (np.zeros((B, Hkv, L_cap, d * bits // 8), np.uint8),
-               np.zeros((B, Hkv, L_cap // T, d), np.float32),
+               np.zeros((B, Hkv, L_cap // T, d), np.uint16),
                np.zeros((B, Hkv, L_cap, d), np.int8),
                np.zeros((B, Hkv, L_cap // T, d), np.float32))
     Kc, sc, Kr, sr = out
+    _need_bf16(sc, "sc")
     lib = _load()
     dt = _dtype_code(K)
     for b in range(B):
@@ -284,7 +305,7 @@ def quantize_k_res(K: np.ndarray, T: int, bits: int, tok_begin: int = 0, tok_end
 def dequant(Kc, sc, Kr, sr, T: int, bits: int, t: int, c: int) -> float:
     """Alg. 1 Dequant of key element (t, c) of one slice (double)."""
     d = Kr.shape[-1]
-    return float(_load().ffdo_dequant(_ptr(np.ascontiguousarray(Kc)), _ptr(np.ascontiguousarray(sc)),
+    return float(_load().ffdo_dequant(_ptr(np.ascontiguousarray(Kc)), _ptr(_need_bf16(sc, "sc")),
                                       _ptr(np.ascontiguousarray(Kr)), _ptr(np.ascontiguousarray(sr)),
                                       d, T, bits, t, c))
 
@@ -294,7 +315,7 @@ def scan_head_bits(qh, Kc_slice, sc_slice, n_full: int, T: int, bits: int, per_t
     qh = np.ascontiguousarray(to_f32(qh))
     d = qh.shape[0]
     Kc_slice = np.ascontiguousarray(Kc_slice)
-    sc_slice = np.ascontiguousarray(sc_slice)
+    sc_slice = _need_bf16(sc_slice, "sc")
     sb = np.empty(max(n_full, 1), dtype=np.float32)
     st = np.empty(max(n_full * T, 1), dtype=np.float32) if per_token else None
     Et = np.empty(max(n_full * T, 1), dtype=np.int32) if per_token else None
@@ -314,7 +335,7 @@ def attend_head_res(qh, Kc, sc, Kr, sr, Ktail, V, L: int, T: int, bits: int, kee
     kp = None if keep is None else np.ascontiguousarray(keep, dtype=np.uint8)
     V = np.ascontiguousarray(V)
     _load().ffdo_attend_head_res(_ptr(qv), _ptr(np.ascontiguousarray(Kc)),
-                                 _ptr(np.ascontiguousarray(sc)), _ptr(np.ascontiguousarray(Kr)),
+                                 _ptr(_need_bf16(sc, "sc")), _ptr(np.ascontiguousarray(Kr)),
                                  _ptr(np.ascontiguousarray(sr)),
                                  None if Ktail is None else _ptr(np.ascontiguousarray(Ktail)),
                                  _ptr(V), _dtype_code(V), L, d, T, bits, _ptr(kp), _ptr(out),
@@ -337,6 +358,7 @@ def decode_res(q, Ktail, V, Kc, sc, Kr, sr, L: int, T: int, bits: int, delta: fl
     keep = np.empty((B, Hq, max(n_blocks, 1)), dtype=np.uint8) if sparse else None
     mtilde = np.empty((B, Hq), dtype=np.float32) if sparse else None
     shat = np.empty((B, Hq, max(n_full, 1)), dtype=np.float32) if (sparse and want_shat) else None
+    _need_bf16(sc, "sc")
     arrs = [np.ascontiguousarray(a) for a in (q, V, Kc, sc, Kr, sr)]
     Kt = None if Ktail is None else np.ascontiguousarray(Ktail)
     rc = _load().ffdo_decode_res(B, Hq, Hkv, d, L, L_cap, T, bits, _ptr(arrs[0]), _ptr(Kt),

@@ -34,7 +34,11 @@
  *     nearest codeword (Eq. 7); a value exactly on a bin boundary goes to the upper bin.
  *     amax == 0 gives s = 0 and every code = 2^(bits-1).
  *   - Scale group: one scale per (block of T tokens, channel).
- *   - Scan arithmetic (integer-exact): per (query head, block) w_c = RN(q_c * s_c),
+ *   - Scale storage: each block scale is kept as bf16, the binary32 s rounded to the nearest
+ *     bf16 value (8 significant bits), ties to even.  The codes are those of the binary32
+ *     quantizer above; the scan and Dequant read the stored bf16 scale.
+ *   - Scan arithmetic (integer-exact): per (query head, block) w_c = RN(q_c * s_c) (s_c the
+ *     stored bf16 scale),
  *     W = max_c |w_c|; if W == 0 all estimates are 0; otherwise rho = RN(127/W),
  *     wi_c = rint_even(RN(w_c*rho)) clamped to [-127,127], E_t = sum_c wi_c * (2u_tc - (2^bits-1))
  *     (exact integer), f = RN(W * kappa) with kappa = (float)(0.5 / (127 * sqrt(d))) and the
@@ -71,6 +75,35 @@ static float load_elem(const void* base, int dtype, size_t idx)
     return v;
 }
 
+/*
+ * Storage of a block scale: round-to-nearest-even from binary32 to bf16 (the upper 16 bits of a
+ * binary32 whose lower 16 bits are zero).  Adding 0x7FFF plus the lowest kept bit to the bit
+ * pattern and truncating rounds to nearest with ties to even, also across a binade and up to
+ * infinity; a NaN keeps its sign and becomes a quiet NaN.
+ */
+static uint16_t round_to_bf16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    const uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+static float bf16_value(uint16_t b)
+{
+    const uint32_t u = (uint32_t)b << 16;
+    float v;
+    memcpy(&v, &u, sizeof v);
+    return v;
+}
+
+/* round_to_bf16 over an array (exported so that its rounding can be pinned). */
+void ffdo_round_bf16(const float* x, uint16_t* y, int n)
+{
+    for (int i = 0; i < n; ++i) y[i] = round_to_bf16(x[i]);
+}
+
 /* ------------------------------------------------------------------------------------------ */
 /* O1: App. A quantizer for one channel vector x[0..n) (stride `stride` floats).               */
 /* ------------------------------------------------------------------------------------------ */
@@ -105,11 +138,11 @@ void ffdo_quantize_channel(const float* x, int n, int stride, int bits, uint8_t*
  * O1 for one (batch, kv-head) slice.  K is [L_cap][d] (fp32 or bf16 bits).  Every full block j
  * whose last token index (j+1)*T-1 lies in [tok_begin, tok_end) is quantized:
  *   Kq[t][i] = code(t, 2i) | code(t, 2i+1) << 4      (4-bit codes, two channels per byte)
- *   scales[j][c] = s of channel c of block j.
+ *   scales[j][c] = s of channel c of block j, stored as bf16 bits.
  * Returns the number of blocks written.
  */
 int ffdo_quantize_k(const void* K, int dtype, int L_cap, int d, int T, int tok_begin,
-                    int tok_end, uint8_t* Kq, float* scales)
+                    int tok_end, uint8_t* Kq, uint16_t* scales)
 {
     if (d % 2 || T <= 0 || L_cap % T) return -1;
     const int n_cap_blocks = L_cap / T;
@@ -122,7 +155,9 @@ int ffdo_quantize_k(const void* K, int dtype, int L_cap, int d, int T, int tok_b
         if (last < tok_begin || last >= tok_end) continue;
         for (int c = 0; c < d; ++c) {
             for (int t = 0; t < T; ++t) x[t] = load_elem(K, dtype, (size_t)(j * T + t) * d + c);
-            ffdo_quantize_channel(x, T, 1, 4, col, &scales[(size_t)j * d + c]);
+            float s;
+            ffdo_quantize_channel(x, T, 1, 4, col, &s);
+            scales[(size_t)j * d + c] = round_to_bf16(s);
             for (int t = 0; t < T; ++t) codes[(size_t)t * d + c] = col[t];
         }
         for (int t = 0; t < T; ++t) {
@@ -170,20 +205,28 @@ float ffdo_requant(const float* qh, const float* s, int d, int32_t* wi)
     return W * ffdo_kappa(d);
 }
 
+/* The stored bf16 scales of one block as binary32 values. */
+static void block_scales(const uint16_t* scales, int j, int d, float* s)
+{
+    for (int c = 0; c < d; ++c) s[c] = bf16_value(scales[(size_t)j * d + c]);
+}
+
 /*
  * Scan of one query head over the full blocks of its kv-head slice.
  *   qh[d]                      query (fp32 values)
  *   Kq[n_full*T][d/2]          packed 4-bit codes
- *   scales[n_full][d]
+ *   scales[n_full][d]          bf16 bits
  * Outputs: shat_block[n_full] (block estimate = max over its tokens) and, if non-NULL,
  * shat_tok[n_full*T] and E_tok[n_full*T] (the exact integer sums).
  */
-void ffdo_scan_head(const float* qh, const uint8_t* Kq, const float* scales, int n_full, int T,
-                    int d, float* shat_block, float* shat_tok, int32_t* E_tok)
+void ffdo_scan_head(const float* qh, const uint8_t* Kq, const uint16_t* scales, int n_full,
+                    int T, int d, float* shat_block, float* shat_tok, int32_t* E_tok)
 {
     int32_t* wi = (int32_t*)malloc(sizeof(int32_t) * (size_t)d);
+    float* sf = (float*)malloc(sizeof(float) * (size_t)d);
     for (int j = 0; j < n_full; ++j) {
-        const float f = ffdo_requant(qh, scales + (size_t)j * d, d, wi);
+        block_scales(scales, j, d, sf);
+        const float f = ffdo_requant(qh, sf, d, wi);
         float best = -INFINITY;
         for (int t = 0; t < T; ++t) {
             const uint8_t* row = Kq + (size_t)(j * T + t) * (d / 2);
@@ -200,6 +243,7 @@ void ffdo_scan_head(const float* qh, const uint8_t* Kq, const float* scales, int
         shat_block[j] = best;
     }
     free(wi);
+    free(sf);
 }
 
 /* ------------------------------------------------------------------------------------------ */
@@ -282,7 +326,7 @@ void ffdo_attend_head(const float* qh, const void* K, const void* V, int dtype, 
  * q       [B][Hq][d]              fp32 or bf16 bits
  * K, V    [B][Hkv][L_cap][d]      fp32 or bf16 bits
  * Kq      [B][Hkv][L_cap][d/2]    packed codes      (sparse mode only)
- * scales  [B][Hkv][L_cap/T][d]                      (sparse mode only)
+ * scales  [B][Hkv][L_cap/T][d]    bf16 bits         (sparse mode only)
  * sparse  1: O2-O8, 0: O9 (dense)
  * out     [B][Hq][d] double, lse [B][Hq] double
  * keep    [B][Hq][ceil(L/T)] (sparse, may be NULL)
@@ -292,7 +336,7 @@ void ffdo_attend_head(const float* qh, const void* K, const void* V, int dtype, 
  */
 int ffdo_decode(int B, int Hq, int Hkv, int d, int L, int L_cap, int T, int dtype,
                 const void* q, const void* K, const void* V, const uint8_t* Kq,
-                const float* scales, float delta, int sparse, double* out, double* lse,
+                const uint16_t* scales, float delta, int sparse, double* out, double* lse,
                 uint8_t* keep, float* shat, float* mtilde, int n_threads)
 {
     if (Hkv <= 0 || Hq % Hkv || d % 2 || T <= 0 || L < 0 || L > L_cap || L_cap % T) return -1;
@@ -312,7 +356,7 @@ int ffdo_decode(int B, int Hq, int Hkv, int d, int L, int L_cap, int T, int dtyp
         uint8_t* kp = NULL;
         if (sparse) {
             const uint8_t* Kq_bg = Kq + ((size_t)b * Hkv + g) * (size_t)L_cap * (d / 2);
-            const float* sc_bg = scales + ((size_t)b * Hkv + g) * (size_t)(L_cap / T) * d;
+            const uint16_t* sc_bg = scales + ((size_t)b * Hkv + g) * (size_t)(L_cap / T) * d;
             float* sb = (float*)malloc(sizeof(float) * (size_t)(n_full > 0 ? n_full : 1));
             kp = (uint8_t*)malloc((size_t)(n_blocks > 0 ? n_blocks : 1));
             ffdo_scan_head(qh, Kq_bg, sc_bg, n_full, T, d, sb, NULL, NULL);
@@ -339,7 +383,8 @@ int ffdo_decode(int B, int Hq, int Hkv, int d, int L, int L_cap, int T, int dtyp
 /*   - thumbnail: the App. A quantizer with 2^bits levels, bits = 2 (App. A exactly) or 4;     */
 /*     codes packed little-endian in bytes, channel c at bit (c % (8/bits)) * bits of byte     */
 /*     c / (8/bits) of its token row;                                                          */
-/*   - residual of a key element: r = RN(x - RN((u - half) * s)) in fp32;                      */
+/*   - the thumbnail scale s is stored as bf16 (as in the 4-bit key copy), and the residual    */
+/*     is taken against the stored value: r = RN(x - RN((u - half) * s)) in fp32;             */
 /*   - residual quantizer: symmetric 8-bit per (block, channel): s_r = RN(max|r| / 127),       */
 /*     r_q = clamp(rint(RN(r * RN(127 / max|r|))), -127, 127); max|r| = 0 gives s_r = 0, r_q=0;*/
 /*   - Dequant: k = (u - half) * s + r_q * s_r (evaluated in double here);                     */
@@ -379,12 +424,12 @@ void ffdo_quantize_residual(const float* r, int n, int8_t* rq, float* scale_out)
 /*
  * Thumbnail + residual of the completed blocks of one (batch, kv-head) slice K [L_cap][d]
  * (fp32 or bf16 bits); blocks whose last token lies in [tok_begin, tok_end) are written:
- *   Kc [L_cap][d*bits/8] packed codes, sc [L_cap/T][d] thumbnail scales,
+ *   Kc [L_cap][d*bits/8] packed codes, sc [L_cap/T][d] thumbnail scales (bf16 bits),
  *   Kr [L_cap][d] int8 residual codes, sr [L_cap/T][d] residual scales.
  * Returns the number of blocks written (or -1 for bad sizes).
  */
 int ffdo_quantize_k_res(const void* K, int dtype, int L_cap, int d, int T, int bits,
-                        int tok_begin, int tok_end, uint8_t* Kc, float* sc, int8_t* Kr,
+                        int tok_begin, int tok_end, uint8_t* Kc, uint16_t* sc, int8_t* Kr,
                         float* sr)
 {
     if ((bits != 2 && bits != 4) || d % (8 / bits) || T <= 0 || L_cap % T) return -1;
@@ -402,15 +447,17 @@ int ffdo_quantize_k_res(const void* K, int dtype, int L_cap, int d, int T, int b
         for (int t = 0; t < T; ++t) memset(Kc + (size_t)(j * T + t) * row_bytes, 0, (size_t)row_bytes);
         for (int c = 0; c < d; ++c) {
             for (int t = 0; t < T; ++t) x[t] = load_elem(K, dtype, (size_t)(j * T + t) * d + c);
-            float s;
-            ffdo_quantize_channel(x, T, 1, bits, codes, &s);
+            float s32;
+            ffdo_quantize_channel(x, T, 1, bits, codes, &s32);
+            const uint16_t s16 = round_to_bf16(s32);
+            const float s = bf16_value(s16);
             for (int t = 0; t < T; ++t) {
                 const float xh = ((float)codes[t] - half) * s;
                 r[t] = x[t] - xh;
             }
             float s_r;
             ffdo_quantize_residual(r, T, rq, &s_r);
-            sc[(size_t)j * d + c] = s;
+            sc[(size_t)j * d + c] = s16;
             sr[(size_t)j * d + c] = s_r;
             for (int t = 0; t < T; ++t) {
                 uint8_t* row = Kc + (size_t)(j * T + t) * row_bytes;
@@ -428,29 +475,32 @@ int ffdo_quantize_k_res(const void* K, int dtype, int L_cap, int d, int T, int b
 }
 
 /* Alg. 1 Dequant of key element (t, c) of a slice, in double. */
-double ffdo_dequant(const uint8_t* Kc, const float* sc, const int8_t* Kr, const float* sr,
+double ffdo_dequant(const uint8_t* Kc, const uint16_t* sc, const int8_t* Kr, const float* sr,
                     int d, int T, int bits, int t, int c)
 {
     const int row_bytes = d * bits / 8;
     const int u = code_at(Kc + (size_t)t * row_bytes, c, bits);
     const double half = (double)((1 << bits) - 1) * 0.5;
     const size_t sidx = (size_t)(t / T) * d + c;
-    return ((double)u - half) * (double)sc[sidx] + (double)Kr[(size_t)t * d + c] * (double)sr[sidx];
+    return ((double)u - half) * (double)bf16_value(sc[sidx]) +
+           (double)Kr[(size_t)t * d + c] * (double)sr[sidx];
 }
 
 /*
  * Integer-exact scan of one query head over the thumbnail codes (bits = 2 or 4); the same
  * arithmetic as ffdo_scan_head with E_t = sum_c wi_c * (2 u_tc - (2^bits - 1)).
  */
-void ffdo_scan_head_bits(const float* qh, const uint8_t* Kc, const float* scales, int n_full,
-                         int T, int d, int bits, float* shat_block, float* shat_tok,
+void ffdo_scan_head_bits(const float* qh, const uint8_t* Kc, const uint16_t* scales,
+                         int n_full, int T, int d, int bits, float* shat_block, float* shat_tok,
                          int32_t* E_tok)
 {
     const int row_bytes = d * bits / 8;
     const int top = (1 << bits) - 1;
     int32_t* wi = (int32_t*)malloc(sizeof(int32_t) * (size_t)d);
+    float* sf = (float*)malloc(sizeof(float) * (size_t)d);
     for (int j = 0; j < n_full; ++j) {
-        const float f = ffdo_requant(qh, scales + (size_t)j * d, d, wi);
+        block_scales(scales, j, d, sf);
+        const float f = ffdo_requant(qh, sf, d, wi);
         float best = -INFINITY;
         for (int t = 0; t < T; ++t) {
             const uint8_t* row = Kc + (size_t)(j * T + t) * row_bytes;
@@ -465,6 +515,7 @@ void ffdo_scan_head_bits(const float* qh, const uint8_t* Kc, const float* scales
         shat_block[j] = best;
     }
     free(wi);
+    free(sf);
 }
 
 /*
@@ -472,7 +523,7 @@ void ffdo_scan_head_bits(const float* qh, const uint8_t* Kc, const float* scales
  * 16-bit tail keys Ktail [L_cap][d] (bf16 bits; rows n_full*T .. L-1 are read, may be NULL when
  * L % T == 0).  V [L_cap][d] in `dtype`.  keep = NULL for all blocks.
  */
-void ffdo_attend_head_res(const float* qh, const uint8_t* Kc, const float* sc, const int8_t* Kr,
+void ffdo_attend_head_res(const float* qh, const uint8_t* Kc, const uint16_t* sc, const int8_t* Kr,
                           const float* sr, const void* Ktail, const void* V, int dtype, int L,
                           int d, int T, int bits, const uint8_t* keep, double* out, double* lse)
 {
@@ -512,7 +563,7 @@ void ffdo_attend_head_res(const float* qh, const uint8_t* Kc, const float* sc, c
  */
 int ffdo_decode_res(int B, int Hq, int Hkv, int d, int L, int L_cap, int T, int bits,
                     const void* q, const void* Ktail, const void* V, const uint8_t* Kc,
-                    const float* sc, const int8_t* Kr, const float* sr, float delta, int sparse,
+                    const uint16_t* sc, const int8_t* Kr, const float* sr, float delta, int sparse,
                     double* out, double* lse, uint8_t* keep, float* shat, float* mtilde,
                     int n_threads)
 {
@@ -532,7 +583,7 @@ int ffdo_decode_res(int B, int Hq, int Hkv, int d, int L, int L_cap, int T, int 
         float* qh = (float*)malloc(sizeof(float) * (size_t)d);
         for (int c = 0; c < d; ++c) qh[c] = load_elem(q, FFDO_DTYPE_BF16, (size_t)r * d + c);
         const uint8_t* Kc_bg = Kc + bg * (size_t)L_cap * row_bytes;
-        const float* sc_bg = sc + bg * (size_t)(L_cap / T) * d;
+        const uint16_t* sc_bg = sc + bg * (size_t)(L_cap / T) * d;
         const int8_t* Kr_bg = Kr + bg * (size_t)L_cap * d;
         const float* sr_bg = sr + bg * (size_t)(L_cap / T) * d;
         const char* Kt_bg = Ktail ? (const char*)Ktail + bg * (size_t)L_cap * d * 2 : NULL;

@@ -10,6 +10,7 @@ from pathlib import Path
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from long_context_decoding_amd import workloads as W
@@ -104,8 +105,36 @@ def test_closed_forms(bits):
     assert (cb[c1][interior] == -cb[c2][interior]).all()
 
 
+def torch_bf16_bits(x):
+    """bf16 bit patterns of float32 values by torch's CPU conversion (round to nearest, ties to
+    even): an independent implementation of the scales' storage rounding."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_scale_storage_rounding():
+    """The block scales are stored as bf16, rounded to nearest with ties to even."""
+    rng = np.random.default_rng(11)
+    x = np.concatenate([
+        rng.standard_normal(4096).astype(np.float32) * np.float32(3.0),
+        np.exp(rng.uniform(-80, 80, 4096)).astype(np.float32),
+        # exact ties between two bf16 values (lower 16 bits 0x8000), both parities of the kept
+        # bit, a tie that carries into the next binade, the largest finite value (rounds to
+        # infinity), subnormals, zero and infinity
+        np.array([0x3F808000, 0x3F818000, 0x3FFF8000, 0x7F7FFFFF, 0x7F7F7FFF, 0x00000001,
+                  0x00018000, 0x00028000, 0x00000000, 0x7F800000],
+                 dtype=np.uint32).view(np.float32),
+    ])
+    got = oracle.round_bf16(x)
+    assert (got == torch_bf16_bits(x)).all()
+    assert got[-10:].tolist() == [0x3F80, 0x3F82, 0x4000, 0x7F80, 0x7F7F, 0x0000, 0x0002,
+                                  0x0002, 0x0000, 0x7F80]
+    nan = oracle.round_bf16(np.array([np.nan], np.float32))[0]
+    assert (nan & 0x7F80) == 0x7F80 and (nan & 0x007F) != 0
+
+
 def test_quantize_k_packing_and_blocks():
-    """Kq nibble order, per-(block, channel) scales and the append window."""
+    """Kq nibble order, per-(block, channel) scales (stored as bf16) and the append window."""
     rng = np.random.default_rng(3)
     T, d, L_cap = 64, 128, 5 * 64
     K32 = rng.standard_normal((1, 2, L_cap, d)).astype(np.float32)
@@ -116,13 +145,13 @@ def test_quantize_k_packing_and_blocks():
         for j in range(L_cap // T):
             for c in (0, 1, 2, 77, 127):
                 codes, s = oracle.quantize_channel(Kv[0, g, j * T:(j + 1) * T, c], 4)
-                assert sc[0, g, j, c] == s
+                assert sc[0, g, j, c] == torch_bf16_bits(np.array([s]))[0]
                 byte = Kq[0, g, j * T:(j + 1) * T, c // 2]
                 got = (byte >> 4) if c % 2 else (byte & 15)
                 assert (got == codes).all()
     # append window: only blocks whose last token lies in [tok_begin, tok_end)
     Kq2 = np.full_like(Kq, 0xAB)
-    sc2 = np.full_like(sc, -1.0)
+    sc2 = np.full_like(sc, 0xFFFF)
     oracle.quantize_k(K, T, tok_begin=2 * T - 1, tok_end=4 * T - 1, Kq=Kq2, scales=sc2)
     for j in range(L_cap // T):
         written = j in (1, 2)

@@ -76,7 +76,9 @@ def test_two_bit_thumbnail_is_app_a(T):
     for j in range(n):
         blk = x[j * T:(j + 1) * T]
         s = (np.abs(blk).max(axis=0).astype(np.float32) / np.float32(1.5)).astype(np.float32)
-        np.testing.assert_array_equal(sc[0, 0, j], s)
+        # stored as bf16 (nearest, ties to even; torch's conversion as the independent check)
+        s16 = torch.from_numpy(s).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        np.testing.assert_array_equal(sc[0, 0, j], s16)
         dist = np.abs((blk / s.astype(np.float64))[:, :, None] - cb[None, None, :])
         near = dist <= dist.min(axis=2, keepdims=True) + 1e-6
         got = codes[j * T:(j + 1) * T]
@@ -185,7 +187,8 @@ def test_two_bit_scan_one_hot_query(c):
     q[c] = 2.5
     _, st, _ = oracle.scan_head_bits(q, Kc[0, 0], sc[0, 0], n, T, 2, per_token=True)
     codes = unpack_bits(Kc[0, 0], 2, d)[:, c]
-    expect = (codes - 1.5) * np.repeat(sc[0, 0, :, c], T).astype(np.float64) * 2.5 / math.sqrt(d)
+    expect = (codes - 1.5) * np.repeat(oracle.to_f32(sc[0, 0, :, c]), T).astype(np.float64) * \
+        2.5 / math.sqrt(d)
     np.testing.assert_allclose(st, expect, rtol=4 * 2.0 ** -24, atol=0)
 
 
@@ -198,7 +201,7 @@ def test_two_bit_scan_integer_sums():
     _, st, Et = oracle.scan_head_bits(q, Kc[0, 0], sc[0, 0], n, T, 2, per_token=True)
     codes = unpack_bits(Kc[0, 0], 2, d)
     for j in range(n):
-        wi, f = oracle.requant(q, sc[0, 0, j])
+        wi, f = oracle.requant(q, oracle.to_f32(sc[0, 0, j]))
         E = (codes[j * T:(j + 1) * T] * 2 - 3) @ wi.astype(np.int64)
         np.testing.assert_array_equal(Et[j * T:(j + 1) * T], E)
 

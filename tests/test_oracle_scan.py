@@ -46,7 +46,7 @@ def test_scan_exact_on_grid(seed):
     K = x[None, None]
     Kq, sc = oracle.quantize_k(K, T)
     assert (unpack(Kq[0, 0]) == u).all(), "quantizer must recover grid codes exactly"
-    assert (sc[0, 0] == (2.0 ** exps)[:, None]).all()
+    assert (oracle.to_f32(sc[0, 0]) == (2.0 ** exps)[:, None]).all()
     q = rng.integers(-127, 128, size=d).astype(np.float32)
     q[rng.integers(d)] = 127.0 * (1 if rng.random() < 0.5 else -1)
     sb, st, Et = oracle.scan_head(q, Kq[0, 0], sc[0, 0], n, T, per_token=True)
@@ -68,7 +68,7 @@ def test_scan_one_hot_query(c):
     q[c] = alpha
     sb, st, _ = oracle.scan_head(q, Kq[0, 0], sc[0, 0], n, T, per_token=True)
     codes = unpack(Kq[0, 0])[:, c]
-    s_c = np.repeat(sc[0, 0, :, c], T).astype(np.float64)
+    s_c = np.repeat(oracle.to_f32(sc[0, 0, :, c]), T).astype(np.float64)
     expect = (codes - 7.5) * s_c * alpha / math.sqrt(d)
     np.testing.assert_allclose(st, expect, rtol=4 * 2.0 ** -24, atol=0)
 
@@ -82,9 +82,10 @@ def test_integer_sums_recomputed_int64():
     _, st, Et = oracle.scan_head(q, Kq[0, 0], sc[0, 0], n, T, per_token=True)
     codes = unpack(Kq[0, 0])
     for j in range(n):
-        wi, f = oracle.requant(q, sc[0, 0, j])
+        s_j = oracle.to_f32(sc[0, 0, j])
+        wi, f = oracle.requant(q, s_j)
         # requantization: max |wi| is 127 and wi * W/127 is within half a step of q (.) s
-        w = q.astype(np.float64) * sc[0, 0, j].astype(np.float64)
+        w = q.astype(np.float64) * s_j.astype(np.float64)
         Wmax = np.abs(w).max()
         assert np.abs(wi).max() == 127
         assert (np.abs(wi * Wmax / 127 - w) <= Wmax / 127 * (0.5 + 2 ** -18)).all()
@@ -122,11 +123,13 @@ def test_power_of_two_scaling():
 
 def error_bound(q, x, codes, s_tok, sigma_tok, shat, d):
     """Deterministic bound on |shat_t - s_t| (App. B, Eq. 8, with worst-case instead of
-    sub-Gaussian noise): key quantization error <= s/2 per channel, requantization error of
-    q (.) s <= sigma/2 per channel (sigma = W/127), a few float roundings."""
+    sub-Gaussian noise): key quantization error <= s/2 per channel plus |u - 7.5| times the
+    storage rounding of the scale (s is the stored bf16 value, within 2^-9 of the binary32 scale
+    the codes were chosen with), requantization error of q (.) s <= sigma/2 per channel
+    (sigma = W/127), a few float roundings."""
     qa = np.abs(q.astype(np.float64))
     cu = np.abs(codes - 7.5)
-    key_term = (qa[None, :] * s_tok / 2).sum(axis=1)
+    key_term = (qa[None, :] * s_tok * (0.5 + cu * 2.0 ** -9)).sum(axis=1) * (1 + 2.0 ** -8)
     req_term = sigma_tok[:, 0] / 2 * cu.sum(axis=1)
     w_round = (qa[None, :] * s_tok * cu).sum(axis=1) * 2.0 ** -23
     return (key_term + req_term) * (1 + 2 ** -14) / math.sqrt(d) + w_round / math.sqrt(d) + \
@@ -145,9 +148,9 @@ def test_error_bound_on_workload_slices(name, T):
         qh = W.bf16_bits_to_f32(q[0, h])
         _, st, _ = oracle.scan_head(qh, Kq[0, 0], sc[0, 0], n, T, per_token=True)
         exact = x[: n * T] @ qh.astype(np.float64) / math.sqrt(w.d)
-        s_tok = np.repeat(sc[0, 0, :n].astype(np.float64), T, axis=0)
-        sig = np.repeat(np.abs(qh[None, :] * sc[0, 0, :n]).max(axis=1, keepdims=True) / 127, T,
-                        axis=0)
+        s_n = oracle.to_f32(sc[0, 0, :n])
+        s_tok = np.repeat(s_n.astype(np.float64), T, axis=0)
+        sig = np.repeat(np.abs(qh[None, :] * s_n).max(axis=1, keepdims=True) / 127, T, axis=0)
         bound = error_bound(qh, x, codes[: n * T], s_tok, sig, st, w.d)
         err = np.abs(st - exact)
         assert (err <= bound).all(), (h, (err / bound).max())
