@@ -9,7 +9,7 @@ events around one replay of a HIP graph holding `--steps` consecutive steps that
 copies of the KV cache (as consecutive layers of a model would), so that every input is resident
 in HBM and none is in the 256 MiB Infinity Cache when its step starts.  Eager back-to-back
 launches and same-cache (warm) figures are reported beside it.
-The bytes behind the bandwidth figures are algorithmic: packed int4 keys and their scales for
+The bytes behind the bandwidth figures are algorithmic: packed int4 keys and their bf16 scales for
 every full block, bf16 K and V for every block that some query head of its group keeps, and q.
 """
 from __future__ import annotations
@@ -33,7 +33,10 @@ METRIC = ("µs/decode step + effective HBM GB/s (% peak) at 128K/256K; speedup v
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E vendor peak
 PRIMARY = "gqa4_256k_sink_needles"
 SECONDARY = "b8_gqa4_128k_powerlaw"
-KERNEL_SRC = ROOT / "long_context_decoding_amd" / "csrc" / "ffd_kernels.hip"
+# the sources the decode kernels compile from; counter figures apply only to the build they were
+# taken on
+KERNEL_SRCS = [ROOT / "long_context_decoding_amd" / "csrc" / f
+               for f in ("ffd_kernels.hip", "ffd_kernels_stream.hip", "ffd_internal.h")]
 TRAFFIC_FILE = ROOT / "profiles" / "traffic_decode_sparse.json"
 
 
@@ -43,7 +46,10 @@ def log(msg: str) -> None:
 
 def kernel_hash() -> str | None:
     try:
-        return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()[:16]
+        h = hashlib.sha256()
+        for f in KERNEL_SRCS:
+            h.update(f.read_bytes())
+        return h.hexdigest()[:16]
     except OSError:  # a tree with the built library but not its source: no counter figure applies
         return None
 
@@ -54,7 +60,7 @@ def kernel_hash() -> str | None:
 def bytes_sparse(w, keep: np.ndarray) -> dict:
     """Algorithmic bytes read by one sparse step, from the kept-block mask [B, Hq, n_blocks]."""
     e, d, T = w.elem_bytes, w.d, w.T
-    scan = w.B * w.Hkv * w.n_full * (T * d // 2 + 4 * d)
+    scan = w.B * w.Hkv * w.n_full * (T * d // 2 + 2 * d)  # int4 codes, bf16 scales
     union = keep.reshape(w.B, w.Hkv, w.G, w.n_blocks).max(axis=2)       # [B, Hkv, n_blocks]
     tokens = np.full(w.n_blocks, T, dtype=np.int64)
     if w.L % T:
@@ -69,13 +75,13 @@ def bytes_sparse(w, keep: np.ndarray) -> dict:
 def bytes_residual(w, keep: np.ndarray, bits: int) -> dict:
     """Algorithmic bytes of one sparse step in the residual storage form: thumbnail codes and
     scales of every full block; for every union-kept block its codes, 8-bit residual codes, both
-    scale rows and bf16 values; q."""
+    scale rows (bf16 s, fp32 s_r) and bf16 values; q."""
     d, T = w.d, w.T
     code_b = T * d * bits // 8
-    scan = w.B * w.Hkv * w.n_full * (code_b + 4 * d)
+    scan = w.B * w.Hkv * w.n_full * (code_b + 2 * d)
     union = keep.reshape(w.B, w.Hkv, w.G, w.n_blocks).max(axis=2)
     U = int(union.sum())
-    exact = U * (code_b + T * d + 2 * 4 * d + 2 * T * d)
+    exact = U * (code_b + T * d + (2 + 4) * d + 2 * T * d)
     qb = w.B * w.Hq * d * 2
     return {"scan": scan, "exact": exact, "q": qb, "total": scan + exact + qb,
             "union_keep": float(union.mean())}

@@ -21,7 +21,9 @@
  *         K, V     [B, Hkv, seq_cap, d]   dims.dtype
  *         Kq       [B, Hkv, seq_cap, d/2] uint8: byte i of a token row holds the 4-bit code of
  *                                         channel 2i in bits 0-3 and of channel 2i+1 in bits 4-7
- *         scales   [B, Hkv, seq_cap/T, d] fp32: one scale per (block, channel)
+ *         scales   [B, Hkv, seq_cap/T, d] bf16 bit patterns (uint16): one scale per (block,
+ *                                         channel), the binary32 s = RN(max|x| / 7.5) of App. A
+ *                                         rounded to nearest bf16 (ties to even)
  *         out      [B, Hq, d]             fp32
  *         lse      [B, Hq]                fp32, natural log of the softmax denominator
  *         keep_mask[B, Hq, ceil(L/T)]     uint8, 1 = block used for that query head
@@ -63,7 +65,7 @@
 extern "C" {
 #endif
 
-#define FFD_ABI_VERSION 1
+#define FFD_ABI_VERSION 2
 #define FFD_BITS 4          /* bits per key channel in the scanned copy */
 #define FFD_SINK_BLOCKS 1   /* S_global of Eq. 3: block 0 */
 #define FFD_LOCAL_BLOCKS 1  /* S_local of Eq. 3: the last full block */
@@ -99,7 +101,7 @@ typedef struct {
  * quantizes a whole cache; calling it once per appended token gives the same bytes.
  */
 ffd_status ffd_quantize_k_append(const ffd_dims* dims, const void* K, int32_t tok_begin,
-                                 int32_t tok_end, int32_t block, uint8_t* Kq, float* scales,
+                                 int32_t tok_end, int32_t block, uint8_t* Kq, uint16_t* scales,
                                  hipStream_t stream);
 
 /*
@@ -116,7 +118,7 @@ ffd_status ffd_quantize_k_append(const ffd_dims* dims, const void* K, int32_t to
  *              on one stream).
  */
 ffd_status ffd_decode_sparse(const ffd_dims* dims, const void* q, const void* K, const void* V,
-                             const uint8_t* Kq, const float* scales, float delta, int32_t block,
+                             const uint8_t* Kq, const uint16_t* scales, float delta, int32_t block,
                              float* out, float* lse, uint8_t* keep_mask, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
 
@@ -138,7 +140,9 @@ ffd_status ffd_decode_dense(const ffd_dims* dims, const void* q, const void* K, 
  *   Kc         [B, Hkv, seq_cap, d*bits/8] uint8: thumbnail codes, channel c at bit
  *              (c % (8/bits)) * bits of byte c / (8/bits) of the token row (App. A quantizer
  *              with 2^bits levels: value (u - (2^bits-1)/2) * s; bits = 2 is App. A exactly)
- *   scales     [B, Hkv, seq_cap/T, d] fp32: thumbnail scale s = RN(max|x| / ((2^bits-1)/2))
+ *   scales     [B, Hkv, seq_cap/T, d] bf16 bits: thumbnail scale, the binary32
+ *              RN(max|x| / ((2^bits-1)/2)) rounded to nearest bf16 (ties to even); the codes use
+ *              the binary32 reciprocal RN(((2^bits-1)/2) / max|x|), the residual the stored s
  *   Kr         [B, Hkv, seq_cap, d] int8: residual code of r = RN(x - RN((u - half) s)),
  *              clamp(rint(RN(r * RN(127 / max|r|))), -127, 127), max over the block's T tokens
  *   res_scales [B, Hkv, seq_cap/T, d] fp32: s_r = RN(max|r| / 127) (0 when max|r| = 0)
@@ -147,7 +151,7 @@ ffd_status ffd_decode_dense(const ffd_dims* dims, const void* q, const void* K, 
  */
 ffd_status ffd_quantize_k_residual_append(const ffd_dims* dims, const void* K, int32_t tok_begin,
                                           int32_t tok_end, int32_t block, int32_t bits,
-                                          uint8_t* Kc, float* scales, int8_t* Kr,
+                                          uint8_t* Kc, uint16_t* scales, int8_t* Kr,
                                           float* res_scales, hipStream_t stream);
 
 /*
@@ -158,7 +162,7 @@ ffd_status ffd_quantize_k_residual_append(const ffd_dims* dims, const void* K, i
  * Same outputs, workspace and errors as ffd_decode_sparse; q and V bf16 only.
  */
 ffd_status ffd_decode_sparse_residual(const ffd_dims* dims, const void* q, const void* K_tail,
-                                      const void* V, const uint8_t* Kc, const float* scales,
+                                      const void* V, const uint8_t* Kc, const uint16_t* scales,
                                       const int8_t* Kr, const float* res_scales, int32_t bits,
                                       float delta, int32_t block, float* out, float* lse,
                                       uint8_t* keep_mask, void* workspace, size_t workspace_bytes,
@@ -182,7 +186,7 @@ ffd_status ffd_decode_sparse_residual(const ffd_dims* dims, const void* q, const
  */
 ffd_status ffd_append_token(const ffd_dims* dims, const void* k_new, const void* v_new, void* K,
                             void* V, int32_t* seq_lens, int32_t block, uint8_t* Kq,
-                            float* scales, hipStream_t stream);
+                            uint16_t* scales, hipStream_t stream);
 
 /*
  * Sparse (and dense) decode step with per-sequence lengths read from device memory: sequence b
@@ -193,7 +197,7 @@ ffd_status ffd_append_token(const ffd_dims* dims, const void* k_new, const void*
  * and lse = -inf.
  */
 ffd_status ffd_decode_sparse_varlen(const ffd_dims* dims, const void* q, const void* K,
-                                    const void* V, const uint8_t* Kq, const float* scales,
+                                    const void* V, const uint8_t* Kq, const uint16_t* scales,
                                     const int32_t* seq_lens, float delta, int32_t block,
                                     float* out, float* lse, uint8_t* keep_mask, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream);
@@ -236,7 +240,7 @@ ffd_status ffd_block_bounds(const ffd_dims* dims, const void* K, int32_t tok_beg
  * kernel's estimates), FFD_SCORE_BOUNDS kmin and kmax, FFD_SCORE_EXACT K; the other inputs may
  * be NULL.  q is [B, Hq, d] in dims->dtype. */
 ffd_status ffd_block_scores(const ffd_dims* dims, int32_t kind, const void* q, const void* K,
-                            const uint8_t* Kq, const float* scales, const void* kmin,
+                            const uint8_t* Kq, const uint16_t* scales, const void* kmin,
                             const void* kmax, int32_t block, float* scores, hipStream_t stream);
 
 /* One selection rule over every row of scores [B, Hq, nf] -> keep_mask [B, Hq, ceil(seq_len /
@@ -269,7 +273,7 @@ ffd_status ffd_decode_masked(const ffd_dims* dims, const void* q, const void* K,
  *              (else FFD_ERR_UNSUPPORTED)
  *   workspace  at least ffd_workspace_bytes_window(dims, block, window) bytes. */
 ffd_status ffd_decode_sparse_running(const ffd_dims* dims, const void* q, const void* K,
-                                     const void* V, const uint8_t* Kq, const float* scales,
+                                     const void* V, const uint8_t* Kq, const uint16_t* scales,
                                      float delta, int32_t block, int32_t window, float* out,
                                      float* lse, uint8_t* keep_mask, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream);
@@ -291,7 +295,7 @@ ffd_status ffd_decode_sparse_running(const ffd_dims* dims, const void* q, const 
  */
 #define FFD_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
 ffd_status ffd_decode_sparse_noalloc(const ffd_dims* dims, const void* q, const void* K,
-                                     const void* V, const uint8_t* Kq, const float* scales,
+                                     const void* V, const uint8_t* Kq, const uint16_t* scales,
                                      float delta, int32_t block, float* out, float* lse,
                                      uint8_t* keep_mask, hipStream_t stream);
 

@@ -115,7 +115,7 @@ WsLayout ws_layout(const ffd_dims* d, int S)
 ffd_status finish(hipError_t e) { return e == hipSuccess ? FFD_OK : FFD_ERR_HIP; }
 
 ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, const void* V,
-                         const uint8_t* Kq, const float* scales, float delta, int32_t block,
+                         const uint8_t* Kq, const uint16_t* scales, float delta, int32_t block,
                          float* out, float* lse, uint8_t* keep_mask, void* workspace,
                          size_t workspace_bytes, hipStream_t stream, bool sparse,
                          const int8_t* Kr = nullptr, const float* res_scales = nullptr,
@@ -258,7 +258,7 @@ int32_t ffd_num_splits(const ffd_dims* dims, int32_t block, int32_t sparse)
 }
 
 ffd_status ffd_quantize_k_append(const ffd_dims* dims, const void* K, int32_t tok_begin,
-                                 int32_t tok_end, int32_t block, uint8_t* Kq, float* scales,
+                                 int32_t tok_end, int32_t block, uint8_t* Kq, uint16_t* scales,
                                  hipStream_t stream)
 {
     ffd_status st = check_dims(dims, block);
@@ -285,7 +285,7 @@ ffd_status ffd_quantize_k_append(const ffd_dims* dims, const void* K, int32_t to
 }
 
 ffd_status ffd_decode_sparse(const ffd_dims* dims, const void* q, const void* K, const void* V,
-                             const uint8_t* Kq, const float* scales, float delta, int32_t block,
+                             const uint8_t* Kq, const uint16_t* scales, float delta, int32_t block,
                              float* out, float* lse, uint8_t* keep_mask, void* workspace,
                              size_t workspace_bytes, hipStream_t stream)
 {
@@ -294,7 +294,7 @@ ffd_status ffd_decode_sparse(const ffd_dims* dims, const void* q, const void* K,
 }
 
 ffd_status ffd_decode_sparse_noalloc(const ffd_dims* dims, const void* q, const void* K,
-                                     const void* V, const uint8_t* Kq, const float* scales,
+                                     const void* V, const uint8_t* Kq, const uint16_t* scales,
                                      float delta, int32_t block, float* out, float* lse,
                                      uint8_t* keep_mask, hipStream_t stream)
 {
@@ -304,7 +304,7 @@ ffd_status ffd_decode_sparse_noalloc(const ffd_dims* dims, const void* q, const 
 
 ffd_status ffd_quantize_k_residual_append(const ffd_dims* dims, const void* K, int32_t tok_begin,
                                           int32_t tok_end, int32_t block, int32_t bits,
-                                          uint8_t* Kc, float* scales, int8_t* Kr,
+                                          uint8_t* Kc, uint16_t* scales, int8_t* Kr,
                                           float* res_scales, hipStream_t stream)
 {
     int j_first, j_last;
@@ -332,7 +332,7 @@ ffd_status ffd_quantize_k_residual_append(const ffd_dims* dims, const void* K, i
 }
 
 ffd_status ffd_decode_sparse_residual(const ffd_dims* dims, const void* q, const void* K_tail,
-                                      const void* V, const uint8_t* Kc, const float* scales,
+                                      const void* V, const uint8_t* Kc, const uint16_t* scales,
                                       const int8_t* Kr, const float* res_scales, int32_t bits,
                                       float delta, int32_t block, float* out, float* lse,
                                       uint8_t* keep_mask, void* workspace, size_t workspace_bytes,
@@ -352,7 +352,7 @@ ffd_status ffd_decode_dense(const ffd_dims* dims, const void* q, const void* K, 
 }
 
 ffd_status ffd_decode_sparse_varlen(const ffd_dims* dims, const void* q, const void* K,
-                                    const void* V, const uint8_t* Kq, const float* scales,
+                                    const void* V, const uint8_t* Kq, const uint16_t* scales,
                                     const int32_t* seq_lens, float delta, int32_t block,
                                     float* out, float* lse, uint8_t* keep_mask, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream)
@@ -363,7 +363,7 @@ ffd_status ffd_decode_sparse_varlen(const ffd_dims* dims, const void* q, const v
 }
 
 ffd_status ffd_decode_sparse_running(const ffd_dims* dims, const void* q, const void* K,
-                                     const void* V, const uint8_t* Kq, const float* scales,
+                                     const void* V, const uint8_t* Kq, const uint16_t* scales,
                                      float delta, int32_t block, int32_t window, float* out,
                                      float* lse, uint8_t* keep_mask, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream)
@@ -396,7 +396,7 @@ ffd_status ffd_decode_dense_varlen(const ffd_dims* dims, const void* q, const vo
 
 ffd_status ffd_append_token(const ffd_dims* dims, const void* k_new, const void* v_new, void* K,
                             void* V, int32_t* seq_lens, int32_t block, uint8_t* Kq,
-                            float* scales, hipStream_t stream)
+                            uint16_t* scales, hipStream_t stream)
 {
     ffd_status st = check_dims(dims, block);
     if (st != FFD_OK) return st;
@@ -454,7 +454,7 @@ ffd_status ffd_block_bounds(const ffd_dims* dims, const void* K, int32_t tok_beg
 }
 
 ffd_status ffd_block_scores(const ffd_dims* dims, int32_t kind, const void* q, const void* K,
-                            const uint8_t* Kq, const float* scales, const void* kmin,
+                            const uint8_t* Kq, const uint16_t* scales, const void* kmin,
                             const void* kmax, int32_t block, float* scores, hipStream_t stream)
 {
     ffd_status st = check_dims(dims, block);

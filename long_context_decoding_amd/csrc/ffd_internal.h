@@ -28,7 +28,7 @@ struct DecodeParams {
     const void* K;
     const void* V;
     const uint8_t* Kq;      // scanned codes (4 bits; 2 or 4 bits in the residual form)
-    const float* scales;
+    const uint16_t* scales;  // their block scales, bf16 bits [B*Hkv][cap/T][d]
     const int8_t* Kr;       // residual form: 8-bit residual codes [B*Hkv][cap][d]
     const float* res_scales;  // residual form: residual scales [B*Hkv][cap/T][d]
     float* out;
@@ -73,7 +73,7 @@ constexpr int kStreamBlocksDense = 4;
 struct QuantParams {
     const void* K;
     uint8_t* Kq;
-    float* scales;
+    uint16_t* scales;   // bf16 bits
     int8_t* Kr;         // residual form only
     float* res_scales;  // residual form only
     int B, Hkv, cap, T;
@@ -89,7 +89,7 @@ struct AppendParams {
     void* V;
     int32_t* seq_lens;  // [B], device
     uint8_t* Kq;
-    float* scales;
+    uint16_t* scales;   // bf16 bits
     int B, Hkv, cap, T;
 };
 
@@ -108,7 +108,7 @@ struct ScoreParams {
     const void* q;
     const void* K;
     const uint8_t* Kq;
-    const float* scales;
+    const uint16_t* scales;  // bf16 bits
     const void* kmin;
     const void* kmax;
     float* scores;  // [B][Hq][n_full]

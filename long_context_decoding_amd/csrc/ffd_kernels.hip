@@ -204,6 +204,17 @@ struct pick<false, A, B> {
 __device__ __forceinline__ float bf16_lo(u32 x) { return as_f((int)(x << 16)); }
 __device__ __forceinline__ float bf16_hi(u32 x) { return as_f((int)(x & 0xFFFF0000u)); }
 
+// Block scales are kept as bf16: the binary32 value rounded to nearest, ties to even (adding
+// 0x7FFF plus the lowest kept bit, then truncating, also carries correctly into the next binade
+// and to infinity); a NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t scale_bits(float x)
+{
+    const u32 u = (u32)as_i(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ float scale_value(uint16_t b) { return as_f((int)((u32)b << 16)); }
+
 // ------------------------------------------------------------------------------------------
 // Per-wave LDS scratch
 // ------------------------------------------------------------------------------------------
@@ -212,8 +223,8 @@ struct __attribute__((aligned(16))) WaveScratch {
     int8_t wB[2][G][4][16];  // scan MFMA B operand: [k-step][head][kg][16 int8]
     float f[G];              // per-head scan factor RN(W * kappa)
     int wsum[G];             // per-head sum of the requantized weights
-    float4 rsc[96];          // residual form: the current block's s (lanes 0-31), s_r (32-63),
-                             // -half * s (64-95)
+    float4 rsc[96];          // residual form, four channels an entry: the current block's s
+                             // (0-31), s_r (32-63), -half * s (64-95)
 };
 
 // ------------------------------------------------------------------------------------------
@@ -233,12 +244,12 @@ struct CodeSlice<2> {
 template <int T, int BITS>
 struct ScanRegs {
     typename CodeSlice<BITS>::type kq[T / 16];  // token row (16*i + col), channels 32*kg .. +31
-    float4 s0, s1;                              // scales of channels 8*col .. 8*col+7
+    uint4 s;                                    // bf16 scales of channels 8*col .. 8*col+7
 };
 
 template <int T, int BITS, bool NT>
 __device__ __forceinline__ void scan_load(ScanRegs<T, BITS>& r, const uint8_t* __restrict__ kq_blk,
-                                          const float* __restrict__ sc_blk, int lane)
+                                          const uint16_t* __restrict__ sc_blk, int lane)
 {
     const int col = lane & 15, kg = lane >> 4;
     constexpr int RB = D * BITS / 8, CB = 32 * BITS / 8;  // bytes per row, per 32 channels
@@ -255,8 +266,7 @@ __device__ __forceinline__ void scan_load(ScanRegs<T, BITS>& r, const uint8_t* _
             r.kq[i] = *reinterpret_cast<const uint2*>(a);
         }
     }
-    r.s0 = ld16f<NT>(sc_blk + col * 8);
-    r.s1 = ld16f<NT>(sc_blk + col * 8 + 4);
+    r.s = ld16<NT>(sc_blk + col * 8);
 }
 
 // Estimated block maximum of every query head of the group.  Requantization lanes: row kg
@@ -277,7 +287,8 @@ __device__ __forceinline__ float scan_compute(const ScanRegs<T, BITS>& r,
 {
     constexpr int HPL = (G + 3) / 4;
     const int col = lane & 15, kg = lane >> 4;
-    const float s[8] = {r.s0.x, r.s0.y, r.s0.z, r.s0.w, r.s1.x, r.s1.y, r.s1.z, r.s1.w};
+    const float s[8] = {bf16_lo(r.s.x), bf16_hi(r.s.x), bf16_lo(r.s.y), bf16_hi(r.s.y),
+                        bf16_lo(r.s.z), bf16_hi(r.s.z), bf16_lo(r.s.w), bf16_hi(r.s.w)};
 #pragma unroll
     for (int k = 0; k < HPL; ++k) {
         const int h = kg + 4 * k;
@@ -579,16 +590,16 @@ __device__ __forceinline__ void tile_compute(const TileRegs<BF16>& r, const void
 // ------------------------------------------------------------------------------------------
 struct TileRes {
     // full block: a[0] = the 32 channels' codes (16 B at 4 bits, 8 B + 8 unused at 2 bits),
-    // a[1..2] = their 8-bit residual codes, a[3] = 16 B of the block's scales (lanes 0-31: s of
-    // channels 4*lane .., lanes 32-63: s_r of channels 4*(lane-32) ..).  Tail block (no low-bit
-    // copy): a[0..3] = the 32 channels' 16-bit keys.
+    // a[1..2] = their 8-bit residual codes, a[3] = 16 B of the block's scales (lanes 0-31: the
+    // bf16 s of channels 8*(lane%16) .., lanes 32-63: the fp32 s_r of channels 4*(lane-32) ..).
+    // Tail block (no low-bit copy): a[0..3] = the 32 channels' 16-bit keys.
     uint4 a[4];
     uint4 v[4];  // as TileRegs<true>::v
 };
 
 template <int BITS, bool NT>
 __device__ __forceinline__ void tile_load_res(TileRes& r, const uint8_t* __restrict__ kc_bg,
-                                              const float* __restrict__ sc_bg,
+                                              const uint16_t* __restrict__ sc_bg,
                                               const int8_t* __restrict__ kr_bg,
                                               const float* __restrict__ sr_bg,
                                               const __bf16* __restrict__ kt_bg,
@@ -615,8 +626,8 @@ __device__ __forceinline__ void tile_load_res(TileRes& r, const uint8_t* __restr
         a0 = reinterpret_cast<const char*>(kc_bg + row * RB + kg * CB);
         a1 = reinterpret_cast<const char*>(kr_bg + row * D + kg * 32);
         a2 = a1 + 16;
-        a3 = reinterpret_cast<const char*>(lane < 32 ? sc_bg + blk * D + lane * 4
-                                                     : sr_bg + blk * D + (lane - 32) * 4);
+        a3 = lane < 32 ? reinterpret_cast<const char*>(sc_bg + blk * D + (lane & 15) * 8)
+                       : reinterpret_cast<const char*>(sr_bg + blk * D + (lane - 32) * 4);
     }
     if constexpr (BITS == 4) {
         r.a[0] = *reinterpret_cast<const uint4*>(a0);
@@ -658,10 +669,16 @@ __device__ __forceinline__ v4f tile_scores_res(const TileRes& r, const v8bf* qv,
         return acc;
     }
     constexpr float half = (float)((1 << BITS) - 1) * 0.5f;
-    ws.rsc[lane] = __builtin_bit_cast(float4, r.a[3]);
-    if (lane < 32) {
-        const float4 s4 = __builtin_bit_cast(float4, r.a[3]);
-        ws.rsc[64 + lane] = make_float4(-half * s4.x, -half * s4.y, -half * s4.z, -half * s4.w);
+    if (lane >= 32) {
+        ws.rsc[lane] = __builtin_bit_cast(float4, r.a[3]);  // s_r
+    } else if (lane < 16) {
+        const uint4 b = r.a[3];  // the bf16 s of channels 8*lane .. 8*lane+7
+        const float4 s0 = make_float4(bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y));
+        const float4 s1 = make_float4(bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w));
+        ws.rsc[2 * lane] = s0;
+        ws.rsc[2 * lane + 1] = s1;
+        ws.rsc[64 + 2 * lane] = make_float4(-half * s0.x, -half * s0.y, -half * s0.z, -half * s0.w);
+        ws.rsc[65 + 2 * lane] = make_float4(-half * s1.x, -half * s1.y, -half * s1.z, -half * s1.w);
     }
     wave_sync();
     const float* sq = reinterpret_cast<const float*>(ws.rsc) + kg * 32;  // s of my channels
@@ -924,7 +941,7 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
             }
 
             const uint8_t* kq_bg = p.Kq + (size_t)bg * p.cap * (D * BITS / 8);
-            const float* sc_bg = p.scales + (size_t)bg * (p.cap / T) * D;
+            const uint16_t* sc_bg = p.scales + (size_t)bg * (p.cap / T) * D;
             const int nf = nf_b;
             const u32 all_heads = (1u << nh) - 1u;
             // Forced blocks of the split (sink 0, the local block nf-1 and a partial tail) are kept
@@ -1471,7 +1488,7 @@ __device__ __forceinline__ void quantize_block(QuantParams p, int bg, int j, int
         s = __fdiv_rn(amax, 7.5f);
         inv = __fdiv_rn(7.5f, amax);
     }
-    p.scales[((size_t)bg * (p.cap / T) + j) * D + c] = s;
+    p.scales[((size_t)bg * (p.cap / T) + j) * D + c] = scale_bits(s);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         int u = 8;
@@ -1535,7 +1552,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p)
             s = __fdiv_rn(amax, 7.5f);
             inv = __fdiv_rn(7.5f, amax);
         }
-        p.scales[((size_t)bg * (p.cap / T) + j) * D + t] = s;
+        p.scales[((size_t)bg * (p.cap / T) + j) * D + t] = scale_bits(s);
         inv_s[t] = inv;
     }
     __syncthreads();
@@ -1654,8 +1671,11 @@ __global__ __launch_bounds__(256) void quantize_res_kernel(QuantParams p)
             sv = __fdiv_rn(amax, half);
             inv = __fdiv_rn(half, amax);
         }
-        p.scales[srow + t] = sv;
-        sc_s[t] = sv;
+        // the codes use the binary32 reciprocal; the residual is taken against the stored
+        // (bf16) scale, which Dequant reads
+        const uint16_t sb = scale_bits(sv);
+        p.scales[srow + t] = sb;
+        sc_s[t] = scale_value(sb);
         sc_inv[t] = inv;
     }
     __syncthreads();
@@ -1875,7 +1895,7 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(ScoreParams p)
                 qw[k][i] = elem(p.q, (size_t)(h0 + h) * D + col * 8 + i, BF16);
         }
         const uint8_t* kq_bg = p.Kq + (size_t)bg * p.cap * (D / 2);
-        const float* sc_bg = p.scales + (size_t)bg * (p.cap / T) * D;
+        const uint16_t* sc_bg = p.scales + (size_t)bg * (p.cap / T) * D;
         for (int j = j0 + w; j < j1; j += kWaves) {
             ScanRegs<T, 4> r;
             scan_load<T, 4, false>(r, kq_bg + (size_t)j * T * (D / 2), sc_bg + (size_t)j * D, lane);

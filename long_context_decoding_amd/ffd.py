@@ -38,6 +38,7 @@ class Dims(ctypes.Structure):
 
 
 _lib = None
+ABI_VERSION = 2  # include/ffd.h FFD_ABI_VERSION (2: bf16 block scales)
 
 
 def lib():
@@ -51,6 +52,10 @@ def lib():
         P, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
         D = ctypes.POINTER(Dims)
         L.ffd_abi_version.restype = i32
+        if L.ffd_abi_version() != ABI_VERSION:
+            raise RuntimeError(
+                f"{LIB_PATH} has ABI version {L.ffd_abi_version()}, this binding expects "
+                f"{ABI_VERSION}; rebuild with `python -m long_context_decoding_amd.build`")
         L.ffd_status_string.argtypes = [i32]
         L.ffd_status_string.restype = ctypes.c_char_p
         L.ffd_workspace_bytes.argtypes = [D, i32]
@@ -202,10 +207,10 @@ def alloc_workspace_window(dims: Dims, block: int, window: int, device,
 
 
 def alloc_kq(K: torch.Tensor, block: int):
-    """Zero-filled Kq [B, Hkv, seq_cap, d/2] u8 and scales [B, Hkv, seq_cap/block, d] fp32."""
+    """Zero-filled Kq [B, Hkv, seq_cap, d/2] u8 and scales [B, Hkv, seq_cap/block, d] bf16."""
     B, Hkv, cap, d = K.shape
     Kq = torch.zeros((B, Hkv, cap, d // 2), dtype=torch.uint8, device=K.device)
-    sc = torch.zeros((B, Hkv, cap // block, d), dtype=torch.float32, device=K.device)
+    sc = torch.zeros((B, Hkv, cap // block, d), dtype=torch.bfloat16, device=K.device)
     return Kq, sc
 
 
@@ -216,7 +221,7 @@ def quantize_k_append(K: torch.Tensor, tok_begin: int, tok_end: int, block: int,
     B, Hkv, cap, d = K.shape
     _need(K, "K")
     _need(Kq, "Kq", torch.uint8, (B, Hkv, cap, d // 2), K.device)
-    _need(scales, "scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d),
+    _need(scales, "scales", torch.bfloat16, (B, Hkv, cap // block if block > 0 else 0, d),
           K.device)
     dims = make_dims(B, Hkv, Hkv, seq_len if seq_len is not None else cap, cap, _dtype_code(K), d)
     _check(lib().ffd_quantize_k_append(ctypes.byref(dims), _ptr(K), tok_begin, tok_end, block,
@@ -249,7 +254,7 @@ def decode_sparse(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, Kq: torch.T
     _need(V, "V", K.dtype, K.shape, K.device)
     B, Hkv, cap, d = K.shape
     _need(Kq, "Kq", torch.uint8, (B, Hkv, cap, d // 2), K.device)
-    _need(scales, "scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d),
+    _need(scales, "scales", torch.bfloat16, (B, Hkv, cap // block if block > 0 else 0, d),
           K.device)
     out, lse = _decode_outputs(q, out, lse, want_lse, stream)
     if keep_mask is not None:
@@ -280,7 +285,7 @@ def decode_sparse_noalloc(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, Kq:
     _need(V, "V", K.dtype, K.shape, K.device)
     B, Hkv, cap, d = K.shape
     _need(Kq, "Kq", torch.uint8, (B, Hkv, cap, d // 2), K.device)
-    _need(scales, "scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d),
+    _need(scales, "scales", torch.bfloat16, (B, Hkv, cap // block if block > 0 else 0, d),
           K.device)
     _need(out, "out", torch.float32, (q.shape[0], q.shape[1], d), q.device)
     if lse is not None:
@@ -308,7 +313,7 @@ def decode_sparse_running(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, Kq:
     _need(V, "V", K.dtype, K.shape, K.device)
     B, Hkv, cap, d = K.shape
     _need(Kq, "Kq", torch.uint8, (B, Hkv, cap, d // 2), K.device)
-    _need(scales, "scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d),
+    _need(scales, "scales", torch.bfloat16, (B, Hkv, cap // block if block > 0 else 0, d),
           K.device)
     out, lse = _decode_outputs(q, out, lse, want_lse, stream)
     if keep_mask is not None:
@@ -346,12 +351,12 @@ def decode_dense(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, block: int, 
 # Residual storage form: low-bit thumbnail + 8-bit residual instead of 16-bit keys
 # ------------------------------------------------------------------------------------------
 def alloc_kres(K: torch.Tensor, block: int, bits: int):
-    """Zero-filled (Kc u8 [B,Hkv,cap,d*bits/8], scales f32 [B,Hkv,cap/block,d],
+    """Zero-filled (Kc u8 [B,Hkv,cap,d*bits/8], scales bf16 [B,Hkv,cap/block,d],
     Kr int8 [B,Hkv,cap,d], res_scales f32 [B,Hkv,cap/block,d])."""
     B, Hkv, cap, d = K.shape
     dev = K.device
     return (torch.zeros((B, Hkv, cap, d * bits // 8), dtype=torch.uint8, device=dev),
-            torch.zeros((B, Hkv, cap // block, d), dtype=torch.float32, device=dev),
+            torch.zeros((B, Hkv, cap // block, d), dtype=torch.bfloat16, device=dev),
             torch.zeros((B, Hkv, cap, d), dtype=torch.int8, device=dev),
             torch.zeros((B, Hkv, cap // block, d), dtype=torch.float32, device=dev))
 
@@ -359,7 +364,7 @@ def alloc_kres(K: torch.Tensor, block: int, bits: int):
 def _need_kres(K_shape, block, bits, Kc, sc, Kr, sr, device):
     B, Hkv, cap, d = K_shape
     _need(Kc, "Kc", torch.uint8, (B, Hkv, cap, d * bits // 8), device)
-    _need(sc, "scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d), device)
+    _need(sc, "scales", torch.bfloat16, (B, Hkv, cap // block if block > 0 else 0, d), device)
     _need(Kr, "Kr", torch.int8, (B, Hkv, cap, d), device)
     _need(sr, "res_scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d), device)
 
@@ -418,7 +423,7 @@ def append_token(k_new: torch.Tensor, v_new: torch.Tensor, K: torch.Tensor, V: t
     _need(V, "V", K.dtype, K.shape, K.device)
     _need(seq_lens, "seq_lens", torch.int32, (B,), K.device)
     _need(Kq, "Kq", torch.uint8, (B, Hkv, cap, d // 2), K.device)
-    _need(scales, "scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d), K.device)
+    _need(scales, "scales", torch.bfloat16, (B, Hkv, cap // block if block > 0 else 0, d), K.device)
     dims = make_dims(B, Hkv, Hkv, cap, cap, _dtype_code(K), d)
     _check(lib().ffd_append_token(ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _ptr(K), _ptr(V),
                                   _ptr(seq_lens), block, _ptr(Kq), _ptr(scales), _stream(stream)))
@@ -438,7 +443,7 @@ def decode_sparse_varlen(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, Kq: 
     _need(V, "V", K.dtype, K.shape, K.device)
     _need(q, "q", K.dtype, None, K.device)
     _need(Kq, "Kq", torch.uint8, (B, Hkv, cap, d // 2), K.device)
-    _need(scales, "scales", torch.float32, (B, Hkv, cap // block if block > 0 else 0, d),
+    _need(scales, "scales", torch.bfloat16, (B, Hkv, cap // block if block > 0 else 0, d),
           K.device)
     _need(seq_lens, "seq_lens", torch.int32, (B,), K.device)
     out, lse = _decode_outputs(q, out, lse, want_lse, stream)
@@ -513,6 +518,12 @@ def block_scores(kind: int, q: torch.Tensor, K: torch.Tensor, block: int, seq_le
         with _on(stream):
             out = torch.empty((B, Hq, nf), dtype=torch.float32, device=q.device)
     _need(out, "scores", torch.float32, (B, Hq, nf), q.device)
+    Hkv, cap = K.shape[1], K.shape[2]
+    if Kq is not None:
+        _need(Kq, "Kq", torch.uint8, (B, Hkv, cap, d // 2), K.device)
+    if scales is not None:
+        _need(scales, "scales", torch.bfloat16, (B, Hkv, cap // block if block > 0 else 0, d),
+              K.device)
     _check(lib().ffd_block_scores(ctypes.byref(dims), kind, _ptr(q), _ptr(K), _ptr(Kq),
                                   _ptr(scales), _ptr(kmin), _ptr(kmax), block, _ptr(out),
                                   _stream(stream)))

@@ -21,6 +21,13 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
+def to_host(t: torch.Tensor) -> np.ndarray:
+    """A device tensor as numpy; bf16 as its bit patterns (uint16), the oracle's convention."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
 def upload(w: W.Workload, q, K, V):
     return to_dev(q), to_dev(K), to_dev(V)
 

@@ -44,7 +44,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert ffd.abi_version() == 1
+    assert ffd.abi_version() == 2
     for s in range(5):
         assert ffd.status_string(s)
     assert ffd.status_string(99) == "unknown status"

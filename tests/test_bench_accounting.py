@@ -1,7 +1,7 @@
 """Host logic of the benchmark: the algorithmic byte counts behind its GB/s and roofline figures,
 and the lookup of the counter-measured traffic.  No GPU is used.
 
-Bytes of one sparse step: the packed 4-bit keys (T*d/2 bytes) and fp32 scales (4*d bytes) of every
+Bytes of one sparse step: the packed 4-bit keys (T*d/2 bytes) and bf16 scales (2*d bytes) of every
 full block, for every (sequence, kv head); the 16-bit keys and values (2*d*e bytes per token) of
 every block that at least one query head of the group keeps, a partial tail block counted at its
 real length; and the query rows.
@@ -23,7 +23,7 @@ def test_sparse_bytes_on_a_hand_built_mask():
     keep[0, 1, 2] = 1               # head 1 keeps block 2 again (counted once for the group)
     keep[0, 3, [1, 3]] = 1          # group 1: head 3 keeps block 1 and the 17-token tail
     b = bench.bytes_sparse(w, keep)
-    assert b["scan"] == 1 * 2 * 3 * (T * d // 2 + 4 * d)
+    assert b["scan"] == 1 * 2 * 3 * (T * d // 2 + 2 * d)
     assert b["exact"] == (2 * T + (T + 17)) * 2 * d * 2
     assert b["q"] == 4 * d * 2
     assert b["total"] == b["scan"] + b["exact"] + b["q"]
@@ -31,8 +31,8 @@ def test_sparse_bytes_on_a_hand_built_mask():
 
 
 def test_headline_bytes_of_the_256k_step():
-    # 8 kv heads x 2048 full blocks of 128 tokens scanned (8,704 bytes each), 96 union-kept
-    # blocks of bf16 keys and values (64 KiB each), 32 query rows: 148,905,984 bytes
+    # 8 kv heads x 2048 full blocks of 128 tokens scanned (8,448 bytes each), 96 union-kept
+    # blocks of bf16 keys and values (64 KiB each), 32 query rows: 144,711,680 bytes
     w = W.WORKLOADS["gqa4_256k_sink_needles"]
     keep = np.zeros((w.B, w.Hq, w.n_blocks), np.uint8)
     rng = np.random.default_rng(0)
@@ -41,8 +41,8 @@ def test_headline_bytes_of_the_256k_step():
         for i, j in enumerate(blocks):
             keep[0, g * w.G + i % w.G, j] = 1
     b = bench.bytes_sparse(w, keep)
-    assert b["scan"] == 142_606_336 and b["exact"] == 96 * 65_536 and b["q"] == 8_192
-    assert b["total"] == 148_905_984
+    assert b["scan"] == 138_412_032 and b["exact"] == 96 * 65_536 and b["q"] == 8_192
+    assert b["total"] == 144_711_680
 
 
 def test_dense_and_residual_bytes():
@@ -55,8 +55,9 @@ def test_dense_and_residual_bytes():
     for bits in (2, 4):
         r = bench.bytes_residual(w, keep, bits)
         code = T * d * bits // 8
-        assert r["scan"] == 2 * 2 * 5 * (code + 4 * d)
-        assert r["exact"] == 2 * (code + T * d + 2 * 4 * d + 2 * T * d)
+        # bf16 thumbnail scales (2 d bytes per block), fp32 residual scales (4 d)
+        assert r["scan"] == 2 * 2 * 5 * (code + 2 * d)
+        assert r["exact"] == 2 * (code + T * d + 2 * d + 4 * d + 2 * T * d)
         assert r["total"] == r["scan"] + r["exact"] + 2 * 8 * d * 2
 
 

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from conftest import log
-from helpers import DEV, assert_close, to_dev
+from helpers import DEV, assert_close, to_dev, to_host
 from long_context_decoding_amd import ffd
 from long_context_decoding_amd import workloads as W
 
@@ -162,7 +162,7 @@ def test_graph_replayed_decode_loop():
     np.testing.assert_array_equal(K_dev, K_host)
     np.testing.assert_array_equal(V_dev, V_host)
     Kq_o, sc_o = oracle.quantize_k(K_host, T)
-    Kq_d, sc_d = Kq.cpu().numpy(), sc.cpu().numpy()
+    Kq_d, sc_d = Kq.cpu().numpy(), to_host(sc)
     for b in range(B):
         nf = lens[b] // T
         np.testing.assert_array_equal(Kq_d[b, :, :nf * T], Kq_o[b, :, :nf * T], err_msg=f"Kq b={b}")
@@ -189,4 +189,4 @@ def test_append_at_capacity_is_a_noop():
     np.testing.assert_array_equal(K_dev, expect)
     Kq_o, sc_o = oracle.quantize_k(expect, T)
     np.testing.assert_array_equal(Kq.cpu().numpy()[1], Kq_o[1])
-    np.testing.assert_array_equal(sc.cpu().numpy()[1], sc_o[1])
+    np.testing.assert_array_equal(to_host(sc)[1], sc_o[1])

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from conftest import log
-from helpers import DEV, assert_close, oracle_attend, to_dev, upload
+from helpers import DEV, assert_close, oracle_attend, to_dev, to_host, upload
 from long_context_decoding_amd import ffd
 from long_context_decoding_amd import workloads as W
 
@@ -48,7 +48,7 @@ def gpu_sparse_res(w, qd, Kd, Vd, kres, bits, delta, pass_tail=True):
 def check_kres(kres_d, kres_o, n_rows):
     names = ("Kc", "scales", "Kr", "res_scales")
     for name, a, b in zip(names, kres_d, kres_o):
-        a = a.cpu().numpy()
+        a = to_host(a)
         if name in ("Kc", "Kr"):
             a, b = a[:, :, :n_rows], b[:, :, :n_rows]
         np.testing.assert_array_equal(a, b, err_msg=name)
@@ -114,8 +114,9 @@ def test_named_workload_residual(name, bits):
     kres_d = gpu_kres(w, Kd, bits)
     torch.cuda.synchronize()
     log(f"[gpu] residual {name}: oracle quantize")
-    kres_o = tuple(np.zeros(t.shape, dtype={torch.uint8: np.uint8, torch.float32: np.float32,
-                                            torch.int8: np.int8}[t.dtype]) for t in kres_d)
+    np_of = {torch.uint8: np.uint8, torch.float32: np.float32, torch.bfloat16: np.uint16,
+             torch.int8: np.int8}
+    kres_o = tuple(np.zeros(t.shape, dtype=np_of[t.dtype]) for t in kres_d)
     from concurrent.futures import ThreadPoolExecutor
 
     def one(bg):
