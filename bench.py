@@ -352,13 +352,14 @@ def run_workload(w, delta: float, steps: int, warmup: int, min_rotation_mib: int
     if decode_loop and R >= 2:
         # Decode loop: one step appends the new token's key and value on the device (quantizing
         # the key block it completes) and runs the sparse decode with device-side lengths, as a
-        # generation loop replays it.  It runs on the cache copies other than the first (which
-        # it modifies), each sequence starting a few tokens below the capacity so that no
-        # replay reaches it.
+        # generation loop replays it: as two calls (append_token, decode_sparse_varlen) and as
+        # the fused one-launch step (decode_sparse_append).  It runs on the cache copies other
+        # than the first (which it modifies), each sequence starting a few tokens below the
+        # capacity so that no replay of either form reaches it.
         loop_reps = reps[1:]
         RL = len(loop_reps)
         cap = Kd.shape[2]
-        start = max(0, cap - (2 * math.ceil(steps / RL) + 2 * math.ceil(warmup / RL) + 8))
+        start = max(0, cap - (4 * math.ceil(steps / RL) + 4 * math.ceil(warmup / RL) + 16))
         lens_l = [torch.full((w.B,), start, dtype=torch.int32, device=dev) for _ in range(RL)]
         gen = torch.Generator().manual_seed(20261202)
         k_new = torch.randn((w.B, w.Hkv, w.d), generator=gen).to(dev, Kd.dtype)
@@ -371,6 +372,11 @@ def run_workload(w, delta: float, steps: int, warmup: int, min_rotation_mib: int
             ffd.decode_sparse_varlen(qd, Kr, Vr, Kqr, scr, ln, delta, w.T, max_len=w.L,
                                      out=out_s, lse=lse_s, workspace=ws)
 
+        def fused_step(r):
+            Kr, Vr, Kqr, scr = loop_reps[r % RL]
+            ffd.decode_sparse_append(qd, k_new, v_new, Kr, Vr, Kqr, scr, lens_l[r % RL], delta,
+                                     w.T, max_len=w.L, out=out_s, lse=lse_s, workspace=ws)
+
         def varlen_only(r):
             Kr, Vr, Kqr, scr = loop_reps[r % RL]
             ffd.decode_sparse_varlen(qd, Kr, Vr, Kqr, scr, lens_l[r % RL], delta, w.T,
@@ -379,10 +385,15 @@ def run_workload(w, delta: float, steps: int, warmup: int, min_rotation_mib: int
         timed_eager(loop_step, min(warmup, RL))
         us_loop = timed(loop_step, steps)
         us_varlen = timed(varlen_only, steps)
+        timed_eager(fused_step, min(warmup, RL))
+        us_fused = timed(fused_step, steps)
         torch.cuda.synchronize()
         loop = {"step": "append_token + decode_sparse_varlen", "us_per_token": us_loop,
                 "tokens_per_s": w.B * 1e6 / us_loop, "decode_varlen_us": us_varlen,
-                "append_us": us_loop - us_varlen, "start_len": start,
+                "append_us": us_loop - us_varlen,
+                "fused_step": "decode_sparse_append (append and decode in one launch)",
+                "fused_us_per_token": us_fused, "fused_tokens_per_s": w.B * 1e6 / us_fused,
+                "start_len": start,
                 "end_len": int(max(int(x.max()) for x in lens_l)), "cache_copies": RL}
         del loop_reps, lens_l
 
@@ -765,7 +776,8 @@ def main() -> int:
     if prim["decode_loop"]:
         lp = prim["decode_loop"]
         log(f"{w.name} decode loop: {lp['us_per_token']:.1f} us/token "
-            f"(append {lp['append_us']:.1f} us + varlen decode {lp['decode_varlen_us']:.1f} us)")
+            f"(append {lp['append_us']:.1f} us + varlen decode {lp['decode_varlen_us']:.1f} us); "
+            f"fused step {lp['fused_us_per_token']:.1f} us/token")
     if prim["residual_form"]:
         rf = prim["residual_form"]
         log(f"{w.name} residual form: sparse {rf['sparse_us']:.1f} us, {rf['GBps']:.0f} GB/s, "

@@ -207,6 +207,28 @@ ffd_status ffd_decode_dense_varlen(const ffd_dims* dims, const void* q, const vo
                                    size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * One decode-loop step in one launch (Sec. 3.3: one fused kernel per generated token; App. G /
+ * Table 9: the step replayed as a graph): ffd_append_token followed by ffd_decode_sparse_varlen,
+ * with the same results, bytes and lengths as that pair of calls when dims->seq_len is the
+ * capacity (the pair appends below the capacity; this call below dims->seq_len, the length its
+ * splits cover).  For every sequence b whose
+ * length l = seq_lens[b] satisfies 0 <= l < dims->seq_len: the rows k_new[b, g, :] and
+ * v_new[b, g, :] go to position l of K and V, the key block they complete (if any) is quantized
+ * into Kq/scales, the sequence attends over its first l + 1 tokens, and seq_lens[b] becomes
+ * l + 1.  Any other sequence is decoded at its clamped length and left unchanged.
+ *   k_new, v_new  [B, Hkv, d] in dims->dtype, 16-byte aligned
+ *   K, V, Kq, scales, seq_lens  updated in place (layouts of ffd_decode_sparse)
+ * dims->seq_len is the bound the splits cover (normally dims->seq_cap), as in the varlen call.
+ * The workspace's counter region also holds one count per sequence (its top B slots), returned to
+ * zero by the call; FFD_ERR_UNSUPPORTED when work units + B exceed its 65535 slots.
+ */
+ffd_status ffd_decode_sparse_append(const ffd_dims* dims, const void* q, const void* k_new,
+                                   const void* v_new, void* K, void* V, uint8_t* Kq,
+                                   uint16_t* scales, int32_t* seq_lens, float delta, int32_t block,
+                                   float* out, float* lse, uint8_t* keep_mask, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Selection comparators and fidelity diagnostics (Sec. 4.5 Table 3: top-delta against top-k and
  * top-p at a matched keep ratio; Sec. 5.1 Fig. 6: a Quest-style min/max scan as the comparator;
  * Sec. 3.2 Eq. 3 and Sec. 5.2 Fig. 5: the pseudo-max from exact scores and its gap to the true

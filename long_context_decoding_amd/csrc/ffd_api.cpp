@@ -17,7 +17,7 @@ using ffd::kWaves;
 // the ranked selection rules sort a row of block scores in LDS (8-byte keys)
 constexpr int kMaxRankedBlocks = 16384;
 // work units per call: a grid dimension of the score kernel, and the workspace's counter slots
-constexpr int64_t kMaxUnits = 65535;
+constexpr int64_t kMaxUnits = ffd::kCounterSlots;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -121,7 +121,8 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
                          const int8_t* Kr = nullptr, const float* res_scales = nullptr,
                          int bits = 0, const int32_t* seq_lens = nullptr,
                          const uint8_t* ext_mask = nullptr, int window = 0,
-                         bool noalloc = false)
+                         bool noalloc = false, const void* k_new = nullptr,
+                         const void* v_new = nullptr, int32_t* seq_lens_out = nullptr)
 {
     const bool res = bits != 0;
     ffd_status st = check_dims(dims, block);
@@ -190,6 +191,9 @@ ffd_status decode_common(const ffd_dims* dims, const void* q, const void* K, con
     p.stream = p.R >= (sparse ? ffd::kStreamBlocks : ffd::kStreamBlocksDense) ? 1 : 0;
     p.running = window != 0 ? 1 : 0;
     p.seq_lens = seq_lens;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.seq_lens_out = seq_lens_out;
     p.mask_stride = p.n_blocks;
     p.ext_mask = ext_mask;
     p.delta = delta;
@@ -360,6 +364,22 @@ ffd_status ffd_decode_sparse_varlen(const ffd_dims* dims, const void* q, const v
     if (!seq_lens) return FFD_ERR_INVALID_ARG;
     return decode_common(dims, q, K, V, Kq, scales, delta, block, out, lse, keep_mask, workspace,
                          workspace_bytes, stream, true, nullptr, nullptr, 0, seq_lens);
+}
+
+ffd_status ffd_decode_sparse_append(const ffd_dims* dims, const void* q, const void* k_new,
+                                   const void* v_new, void* K, void* V, uint8_t* Kq,
+                                   uint16_t* scales, int32_t* seq_lens, float delta, int32_t block,
+                                   float* out, float* lse, uint8_t* keep_mask, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream)
+{
+    if (!seq_lens || !k_new || !v_new || !K) return FFD_ERR_INVALID_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new)) return FFD_ERR_INVALID_ARG;
+    // the per-sequence counts take the top counter slots, above those of the work units
+    if (dims && check_dims(dims, block) == FFD_OK && n_units(dims) + dims->batch > kMaxUnits)
+        return FFD_ERR_UNSUPPORTED;
+    return decode_common(dims, q, K, V, Kq, scales, delta, block, out, lse, keep_mask, workspace,
+                         workspace_bytes, stream, true, nullptr, nullptr, 0, seq_lens, nullptr, 0,
+                         false, k_new, v_new, seq_lens);
 }
 
 ffd_status ffd_decode_sparse_running(const ffd_dims* dims, const void* q, const void* K,

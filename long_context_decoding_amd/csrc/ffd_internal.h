@@ -60,7 +60,20 @@ struct DecodeParams {
     int stream;               // the launch uses the kernels whose streamed reads (the scan's codes
                               // and scales, the exact stage's values, the dense step's keys) take
                               // the streaming (non-temporal) cache policy: set for long splits
+    // Fused decode-loop step (sparse, stored keys, with seq_lens): when k_new is set, the step's
+    // own token k_new/v_new [B][Hkv][d] (q's dtype) goes to position seq_lens[b] of K and V (if
+    // that is below L) and is attended to; the key block it completes is quantized into Kq and
+    // scales (K, V, Kq and scales are then written: the caller's buffers are mutable); and once
+    // every unit of sequence b has read its length, seq_lens_out[b] (= seq_lens) is advanced.
+    // The per-sequence count lives in counter slot kCounterSlots - 1 - b.
+    const void* k_new;
+    const void* v_new;
+    int32_t* seq_lens_out;
 };
+
+// Counter slots of a workspace (its fixed first region): one per work unit of any call, the fused
+// decode-loop step also using the top B slots for its per-sequence counts.
+constexpr int kCounterSlots = 65535;
 
 // Splits of at least this many blocks run the streaming-policy kernels.  Measured (alternating
 // builds, graph replay): sparse 128K x 8 (256 blocks per split) 214 -> 193 us, 256K (64 blocks)

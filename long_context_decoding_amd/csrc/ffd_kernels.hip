@@ -736,6 +736,81 @@ __device__ __forceinline__ void tile_compute_res(const TileRes& r, const v8bf* q
 }
 
 // ------------------------------------------------------------------------------------------
+// Low-bit key copy of one block (App. A, Eqs. 5-7)
+// ------------------------------------------------------------------------------------------
+// App. A quantizer of one whole block by a work-group of 256 threads (quantize_kernel runs one
+// per (b, kv head, block); the fused decode-loop step runs it at a block boundary).
+// Thread (rg, cg) = (t / 16, t % 16) loads channels 8 cg .. 8 cg + 7 of rows rg, rg + 16, ...
+// (16-byte loads, 16 threads per row), takes their absolute maxima over its rows, and the
+// per-channel maxima over the 16 row groups meet in LDS.  It then writes the codes of its eight
+// channels of each of its rows as one 4-byte word (low nibble = even channel).  The arithmetic is
+// quantize_block's, so the codes and scales are the same bytes: s = RN(amax / 7.5),
+// u = clamp(floor(RN(x * RN(7.5 / amax))) + 8, 0, 15), and u = 8 for an all-zero channel (its
+// stored reciprocal is 0).
+template <int T, bool BF16>
+__device__ __forceinline__ void quantize_block_wg(const void* __restrict__ K,
+                                                  uint8_t* __restrict__ Kq,
+                                                  uint16_t* __restrict__ scales, int cap, int bg,
+                                                  int j, float (*part)[D], float* inv_s)
+{
+    constexpr int RPT = T / 16;  // rows per thread
+    const int t = threadIdx.x, rg = t >> 4, cg = t & 15;
+    const size_t row0 = (size_t)bg * cap + (size_t)j * T;
+    float x[RPT][8];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const size_t e0 = (row0 + rg + 16 * r) * D + cg * 8;
+        if constexpr (BF16) {
+            const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const unsigned short*>(K) + e0);
+            x[r][0] = bf16_lo(v.x); x[r][1] = bf16_hi(v.x);
+            x[r][2] = bf16_lo(v.y); x[r][3] = bf16_hi(v.y);
+            x[r][4] = bf16_lo(v.z); x[r][5] = bf16_hi(v.z);
+            x[r][6] = bf16_lo(v.w); x[r][7] = bf16_hi(v.w);
+        } else {
+            const float4* fp = reinterpret_cast<const float4*>(static_cast<const float*>(K) + e0);
+            const float4 a = fp[0], b = fp[1];
+            x[r][0] = a.x; x[r][1] = a.y; x[r][2] = a.z; x[r][3] = a.w;
+            x[r][4] = b.x; x[r][5] = b.y; x[r][6] = b.z; x[r][7] = b.w;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float am = 0.0f;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) am = fmaxf(am, fabsf(x[r][i]));
+        part[rg][cg * 8 + i] = am;
+    }
+    __syncthreads();
+    if (t < D) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) amax = fmaxf(amax, part[g][t]);
+        float s = 0.0f, inv = 0.0f;
+        if (amax > 0.0f) {
+            s = __fdiv_rn(amax, 7.5f);
+            inv = __fdiv_rn(7.5f, amax);
+        }
+        scales[((size_t)bg * (cap / T) + j) * D + t] = scale_bits(s);
+        inv_s[t] = inv;
+    }
+    __syncthreads();
+    float iv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) iv[i] = inv_s[cg * 8 + i];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        u32 word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            int u = (int)floorf(__fmul_rn(x[r][i], iv[i])) + 8;
+            u = min(max(u, 0), 15);
+            word |= (u32)u << (4 * i);
+        }
+        *reinterpret_cast<u32*>(Kq + (row0 + rg + 16 * r) * (D / 2) + cg * 4) = word;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // Decode kernel (sparse and dense)
 // ------------------------------------------------------------------------------------------
 template <int G, int NW>
@@ -762,6 +837,10 @@ struct __attribute__((aligned(16))) DecodeShared {
             float mt[G];                                    // Alg. 1 pseudo-max of each head
             u32 bits[kMaxBlocksPerSplit];                   // heads that keep each block
         } run;
+        struct {                                            // fused decode-loop step: the block
+            float part[16][D];                              // the new token completes, quantized
+            float inv[D];                                   // by the work-group (before the scan)
+        } quant;
     } u;
     float4 q[G * D / 4];                   // the group's query rows (bf16 or fp32 bytes)
     uint8_t kbits[kMaxBlocksPerSplit];     // per-block head mask (bit h = query head h of group)
@@ -887,6 +966,18 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
     // this sequence's length: the common one, or (decode loops) its own from device memory
     int L_b = p.L;
     if (p.seq_lens) L_b = min(max(p.seq_lens[b], 0), p.L);
+    // fused decode-loop step: the new token at position pos = seq_lens[b] (if below L) is part of
+    // this step; nobody writes the length before every unit of the sequence has read it
+    int pos = -1;
+    if constexpr (SPARSE && !RES) {
+        if (p.k_new) {
+            const int l0 = p.seq_lens[b];
+            if (l0 >= 0 && l0 < p.L) {
+                pos = l0;
+                L_b = l0 + 1;
+            }
+        }
+    }
     const int nf_b = L_b / T;            // full blocks
     const int nb_b = (L_b + T - 1) / T;  // blocks, the last one possibly partial
     const int jb = split * p.R;
@@ -897,6 +988,41 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
     const char* Kbg = p.K ? static_cast<const char*>(p.K) + kv_off * esz : nullptr;
     const char* Vbg = static_cast<const char*>(p.V) + kv_off * esz;
     const int h0 = b * p.Hq + g * p.G + sub * G;  // first query row of the unit
+
+    if constexpr (SPARSE && !RES) {
+        if (pos >= 0) {
+            // The new key and value rows go to position pos.  The split that holds that block
+            // writes both (it alone reads them, in its exact stage); when the token completes
+            // the block, every work-group of the kv head also writes the key row and quantizes
+            // the block itself, because every one of them scans it as its local block: all
+            // write the same bytes, and each reads back only what it wrote itself (after the
+            // barrier), so no work-group waits for another.
+            static_assert(NW * 64 == 256, "the block quantizer runs on 256 threads");
+            const int jt = pos / T;
+            const bool completes = (pos + 1) % T == 0;
+            const bool owner = jt / p.R == split;
+            constexpr int kRow16 = (int)(D * (BF16 ? 2 : 4) / 16);  // 16-byte pieces of a row
+            const size_t src = (size_t)bg * D * esz;
+            const size_t dst = ((size_t)bg * p.cap + pos) * D * esz;
+            const int t = (int)threadIdx.x;
+            char* Kw = static_cast<char*>(const_cast<void*>(p.K));
+            char* Vw = static_cast<char*>(const_cast<void*>(p.V));
+            const char* kn = static_cast<const char*>(p.k_new);
+            const char* vn = static_cast<const char*>(p.v_new);
+            if ((owner || completes) && t < kRow16)
+                reinterpret_cast<uint4*>(Kw + dst)[t] = reinterpret_cast<const uint4*>(kn + src)[t];
+            if (owner && t >= kRow16 && t < 2 * kRow16)
+                reinterpret_cast<uint4*>(Vw + dst)[t - kRow16] =
+                    reinterpret_cast<const uint4*>(vn + src)[t - kRow16];
+            if (completes) {
+                __syncthreads();  // the key row is written
+                quantize_block_wg<T, BF16>(p.K, const_cast<uint8_t*>(p.Kq),
+                                           const_cast<uint16_t*>(p.scales), p.cap, bg, jt,
+                                           sh.u.quant.part, sh.u.quant.inv);
+                __syncthreads();  // codes and scales written
+            }
+        }
+    }
 
     WaveScratch<G>& ws = sh.wave[w];
     constexpr int NT = T / 16;
@@ -1286,8 +1412,22 @@ __global__ __launch_bounds__((RES ? kResWaves : kWaves) * 64, 2) void decode_ker
     }
     __syncthreads();
     if (!sh.is_last) return;
-    if (threadIdx.x == 0)  // ready for the next call
+    if (threadIdx.x == 0) {  // ready for the next call
         __hip_atomic_store(&p.counters[unit], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (SPARSE && !RES) {
+            if (p.k_new) {
+                // every work-group of this unit has read the length; the last unit of the
+                // sequence to get here advances it (and returns the count to zero)
+                unsigned long long* sc = p.counters + (kCounterSlots - 1 - b);
+                const unsigned long long seen =
+                    __hip_atomic_fetch_add(sc, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (seen == (unsigned long long)(p.Hkv * p.NSUB - 1)) {
+                    __hip_atomic_store(sc, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (pos >= 0) p.seq_lens_out[b] = pos + 1;
+                }
+            }
+        }
+    }
 
     const size_t base = (size_t)unit * p.S * G;
     if (fast) {
@@ -1501,75 +1641,13 @@ __device__ __forceinline__ void quantize_block(QuantParams p, int bg, int j, int
     }
 }
 
-// App. A quantizer of whole blocks: one work-group of 256 threads per (b, kv head, block).
-// Thread (rg, cg) = (t / 16, t % 16) loads channels 8 cg .. 8 cg + 7 of rows rg, rg + 16, ...
-// (16-byte loads, 16 threads per row), takes their absolute maxima over its rows, and the
-// per-channel maxima over the 16 row groups meet in LDS.  It then writes the codes of its eight
-// channels of each of its rows as one 4-byte word (low nibble = even channel).  The arithmetic is
-// quantize_block's, so the codes and scales are the same bytes: s = RN(amax / 7.5),
-// u = clamp(floor(RN(x * RN(7.5 / amax))) + 8, 0, 15), and u = 8 for an all-zero channel (its
-// stored reciprocal is 0).
 template <int T, bool BF16>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p)
 {
-    constexpr int RPT = T / 16;  // rows per thread
     __shared__ float part[16][D];
     __shared__ float inv_s[D];
-    const int t = threadIdx.x, rg = t >> 4, cg = t & 15;
-    const int bg = blockIdx.y, j = p.j_first + blockIdx.x;
-    const size_t row0 = (size_t)bg * p.cap + (size_t)j * T;
-    float x[RPT][8];
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-        const size_t e0 = (row0 + rg + 16 * r) * D + cg * 8;
-        if constexpr (BF16) {
-            const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const unsigned short*>(p.K) + e0);
-            x[r][0] = bf16_lo(v.x); x[r][1] = bf16_hi(v.x);
-            x[r][2] = bf16_lo(v.y); x[r][3] = bf16_hi(v.y);
-            x[r][4] = bf16_lo(v.z); x[r][5] = bf16_hi(v.z);
-            x[r][6] = bf16_lo(v.w); x[r][7] = bf16_hi(v.w);
-        } else {
-            const float4* fp = reinterpret_cast<const float4*>(static_cast<const float*>(p.K) + e0);
-            const float4 a = fp[0], b = fp[1];
-            x[r][0] = a.x; x[r][1] = a.y; x[r][2] = a.z; x[r][3] = a.w;
-            x[r][4] = b.x; x[r][5] = b.y; x[r][6] = b.z; x[r][7] = b.w;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float am = 0.0f;
-#pragma unroll
-        for (int r = 0; r < RPT; ++r) am = fmaxf(am, fabsf(x[r][i]));
-        part[rg][cg * 8 + i] = am;
-    }
-    __syncthreads();
-    if (t < D) {
-        float amax = 0.0f;
-#pragma unroll
-        for (int g = 0; g < 16; ++g) amax = fmaxf(amax, part[g][t]);
-        float s = 0.0f, inv = 0.0f;
-        if (amax > 0.0f) {
-            s = __fdiv_rn(amax, 7.5f);
-            inv = __fdiv_rn(7.5f, amax);
-        }
-        p.scales[((size_t)bg * (p.cap / T) + j) * D + t] = scale_bits(s);
-        inv_s[t] = inv;
-    }
-    __syncthreads();
-    float iv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) iv[i] = inv_s[cg * 8 + i];
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-        u32 word = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            int u = (int)floorf(__fmul_rn(x[r][i], iv[i])) + 8;
-            u = min(max(u, 0), 15);
-            word |= (u32)u << (4 * i);
-        }
-        *reinterpret_cast<u32*>(p.Kq + (row0 + rg + 16 * r) * (D / 2) + cg * 4) = word;
-    }
+    quantize_block_wg<T, BF16>(p.K, p.Kq, p.scales, p.cap, blockIdx.y, p.j_first + blockIdx.x, part,
+                               inv_s);
 }
 
 // One decode-loop step of the cache, in one launch.  One work-group per sequence b; thread

@@ -7,8 +7,9 @@ or cannot be loaded, every call raises.
 
 Names follow the C ABI: ``quantize_k_append``, ``decode_sparse``, ``decode_dense``,
 ``quantize_k_residual_append``, ``decode_sparse_residual``, ``append_token``,
-``decode_sparse_varlen``, ``decode_dense_varlen``, ``block_bounds``, ``block_scores``,
-``select_blocks``, ``decode_masked``, ``workspace_bytes``, ``workspace_init``, ``num_splits``.
+``decode_sparse_varlen``, ``decode_sparse_append``, ``decode_dense_varlen``, ``block_bounds``,
+``block_scores``, ``select_blocks``, ``decode_masked``, ``workspace_bytes``, ``workspace_init``,
+``num_splits``.
 """
 from __future__ import annotations
 
@@ -79,6 +80,9 @@ def lib():
         L.ffd_append_token.restype = i32
         L.ffd_decode_sparse_varlen.argtypes = [D, P, P, P, P, P, P, f32, i32, P, P, P, P, sz, P]
         L.ffd_decode_sparse_varlen.restype = i32
+        L.ffd_decode_sparse_append.argtypes = [D, P, P, P, P, P, P, P, P, f32, i32, P, P, P, P, sz,
+                                               P]
+        L.ffd_decode_sparse_append.restype = i32
         L.ffd_decode_dense_varlen.argtypes = [D, P, P, P, P, i32, P, P, P, sz, P]
         L.ffd_decode_dense_varlen.restype = i32
         L.ffd_block_bounds.argtypes = [D, P, i32, i32, i32, P, P, P]
@@ -456,6 +460,41 @@ def decode_sparse_varlen(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, Kq: 
     _check(lib().ffd_decode_sparse_varlen(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V), _ptr(Kq),
                                           _ptr(scales), _ptr(seq_lens), float(delta), block,
                                           _ptr(out), _ptr(lse), _ptr(keep_mask), _ptr(workspace),
+                                          workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def decode_sparse_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                         K: torch.Tensor, V: torch.Tensor, Kq: torch.Tensor, scales: torch.Tensor,
+                         seq_lens: torch.Tensor, delta: float, block: int,
+                         max_len: int | None = None, out: torch.Tensor | None = None,
+                         lse: torch.Tensor | None = None, keep_mask: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None, want_lse: bool = True,
+                         stream=None):
+    """One decode-loop step in one launch: append_token(k_new, v_new) then decode_sparse_varlen,
+    with the same results; K, V, Kq, scales and seq_lens are updated in place."""
+    B, Hkv, cap, d = K.shape
+    max_len = cap if max_len is None else max_len
+    dims = dims_of(q, K, max_len)
+    _need(V, "V", K.dtype, K.shape, K.device)
+    _need(q, "q", K.dtype, None, K.device)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(t, name, K.dtype, (B, Hkv, d), K.device)
+    _need(Kq, "Kq", torch.uint8, (B, Hkv, cap, d // 2), K.device)
+    _need(scales, "scales", torch.bfloat16, (B, Hkv, cap // block if block > 0 else 0, d),
+          K.device)
+    _need(seq_lens, "seq_lens", torch.int32, (B,), K.device)
+    out, lse = _decode_outputs(q, out, lse, want_lse, stream)
+    if keep_mask is not None:
+        _need(keep_mask, "keep_mask", torch.uint8,
+              (q.shape[0], q.shape[1], math.ceil(max_len / block)), q.device)
+    if workspace is None:
+        workspace = alloc_workspace(dims, block, q.device, stream)
+    _need(workspace, "workspace", torch.uint8, None, q.device)
+    _check(lib().ffd_decode_sparse_append(ctypes.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                          _ptr(K), _ptr(V), _ptr(Kq), _ptr(scales),
+                                          _ptr(seq_lens), float(delta), block, _ptr(out),
+                                          _ptr(lse), _ptr(keep_mask), _ptr(workspace),
                                           workspace.numel(), _stream(stream)))
     return out, lse
 

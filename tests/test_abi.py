@@ -249,6 +249,29 @@ def test_decode_loop_validation(L):
         ffd.FFD_ERR_INVALID_ARG
     assert dv(ctypes.byref(d), A, A, A, lens, 64, A, A, A, 16, None) == ffd.FFD_ERR_WORKSPACE
 
+    # the fused decode-loop step: (dims, q, k_new, v_new, K, V, Kq, scales, seq_lens, delta,
+    # block, out, lse, keep_mask, workspace, bytes, stream)
+    fs = L.ffd_decode_sparse_append
+
+    def fused(dd=d, k_new=A, v_new=A, K=A, seq=lens, delta=5.0, block=64, ws_bytes=1 << 30):
+        return fs(ctypes.byref(dd), A, k_new, v_new, K, A, A, A, seq, delta, block, A, A, None,
+                  A, ws_bytes, None)
+    assert fused(seq=None) == ffd.FFD_ERR_INVALID_ARG
+    assert fused(k_new=None) == ffd.FFD_ERR_INVALID_ARG
+    assert fused(v_new=None) == ffd.FFD_ERR_INVALID_ARG
+    assert fused(K=None) == ffd.FFD_ERR_INVALID_ARG
+    assert fused(k_new=MISALIGNED) == ffd.FFD_ERR_INVALID_ARG
+    assert fused(seq=lens_odd) == ffd.FFD_ERR_INVALID_ARG
+    assert fused(delta=float("nan")) == ffd.FFD_ERR_INVALID_ARG
+    assert fused(block=96) == ffd.FFD_ERR_UNSUPPORTED
+    assert fused(ws_bytes=16) == ffd.FFD_ERR_WORKSPACE
+    # the per-sequence counts need B slots above the work units' (65535 in all)
+    many = dims(B=32768, Hq=1, Hkv=1, seq_len=64, seq_cap=64)
+    assert fused(dd=many) == ffd.FFD_ERR_UNSUPPORTED
+    assert sv(ctypes.byref(many), A, A, A, A, A, lens, 5.0, 64, A, A, None, A, 16,
+              None) == ffd.FFD_ERR_WORKSPACE  # the varlen step itself takes that shape
+    assert fused(dd=dims(B=0)) == ffd.FFD_OK
+
 
 def test_comparator_validation(L):
     """Block scores, selection rules and masked decode reject bad arguments before any launch."""

@@ -3,9 +3,13 @@ token; Fig. 2: the key copy is quantized as blocks complete; App. G: the step re
 
 - per-sequence lengths read from device memory give, for every sequence, the oracle's result on
   that sequence's own prefix (masks bit-exact, out and lse within 2e-3);
-- one captured step (ffd_append_token + ffd_decode_sparse_varlen) replayed across several block
-  boundaries matches, after every replay, the oracle run on a host mirror of the growing cache;
-  the cache rows and the key copy of every completed block are byte-exact at the end.
+- one captured step (ffd_append_token + ffd_decode_sparse_varlen, or the fused
+  ffd_decode_sparse_append) replayed across several block boundaries matches, after every replay,
+  the oracle run on a host mirror of the growing cache; the cache rows and the key copy of every
+  completed block are byte-exact at the end;
+- the fused step gives, step after step, the same bytes as the pair of calls: outputs, masks,
+  caches, key copy and lengths, also for groups cut into several units, fp32, a sequence at the
+  capacity and one that starts empty.
 """
 import math
 
@@ -97,7 +101,8 @@ def _loop_setup(B, Hq, Hkv, T, cap, init, seed):
     return w, q0, K, V
 
 
-def test_graph_replayed_decode_loop():
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_replayed_decode_loop(fused):
     B, Hq, Hkv, T, cap = 2, 8, 2, 64, 8 * 64
     init = [60, 126]
     n_steps, delta = 80, 5.0
@@ -123,16 +128,21 @@ def test_graph_replayed_decode_loop():
     # load the kernels once outside the capture: sequences at capacity are left untouched
     full = torch.full((B,), cap, dtype=torch.int32, device=DEV)
     q_buf.copy_(to_dev(qs[0]))
-    ffd.append_token(k_buf, v_buf, Kd, Vd, full, T, Kq, sc)
-    ffd.decode_sparse_varlen(q_buf, Kd, Vd, Kq, sc, full, delta, T, workspace=ws)
+
+    def step(lens_t, **kw):
+        if fused:
+            ffd.decode_sparse_append(q_buf, k_buf, v_buf, Kd, Vd, Kq, sc, lens_t, delta, T, **kw)
+        else:
+            ffd.append_token(k_buf, v_buf, Kd, Vd, lens_t, T, Kq, sc)
+            ffd.decode_sparse_varlen(q_buf, Kd, Vd, Kq, sc, lens_t, delta, T, **kw)
+
+    step(full, workspace=ws)
     torch.cuda.synchronize()
     assert full.tolist() == [cap, cap]
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        ffd.append_token(k_buf, v_buf, Kd, Vd, lens_d, T, Kq, sc)
-        ffd.decode_sparse_varlen(q_buf, Kd, Vd, Kq, sc, lens_d, delta, T, out=out, lse=lse,
-                                 keep_mask=keep, workspace=ws)
+        step(lens_d, out=out, lse=lse, keep_mask=keep, workspace=ws)
     lens = list(init)
     for step in range(n_steps):
         q_buf.copy_(to_dev(qs[step]))
@@ -155,7 +165,7 @@ def test_graph_replayed_decode_loop():
                                           err_msg=f"step {step} b={b} L={lens[b]}")
             assert_close(o[b], ref["out"][0], TOL, f"out step {step} b={b} L={lens[b]}")
             assert_close(l[b], ref["lse"][0], TOL, f"lse step {step} b={b} L={lens[b]}")
-    log(f"decode loop: {n_steps} graph replays, lengths {init} -> {lens}")
+    log(f"decode loop (fused={fused}): {n_steps} graph replays, lengths {init} -> {lens}")
     assert lens_d.cpu().tolist() == lens
     K_dev = Kd.view(torch.int16).cpu().numpy().view(np.uint16)
     V_dev = Vd.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -190,3 +200,65 @@ def test_append_at_capacity_is_a_noop():
     Kq_o, sc_o = oracle.quantize_k(expect, T)
     np.testing.assert_array_equal(Kq.cpu().numpy()[1], Kq_o[1])
     np.testing.assert_array_equal(to_host(sc)[1], sc_o[1])
+
+
+@pytest.mark.parametrize("dtype,T,G,Hkv", [("bf16", 64, 4, 2), ("f32", 128, 1, 2),
+                                           ("bf16", 64, 12, 1), ("bf16", 128, 8, 2)])
+def test_fused_step_equals_append_then_decode(dtype, T, G, Hkv):
+    B, cap = 4, 4 * T
+    init = [T - 3, 2 * T - 2, cap, 0]  # crossing block boundaries, at the capacity, empty
+    n_steps, delta = T + 6, 5.0
+    w = W.small(f"fused_{dtype}_T{T}_G{G}", B=B, Hq=G * Hkv, Hkv=Hkv, L=cap, T=T, dtype=dtype,
+                seed=5 * T + G)
+    q, K, V, _ = W.make_inputs(w)
+    log(f"fused step {dtype} T={T} G={G} Hkv={Hkv}: lengths {init}, {n_steps} steps")
+    rng = np.random.default_rng(31 * T + G)
+    new = rng.standard_normal((n_steps, 2, B, Hkv, 128)).astype(np.float32)
+    if dtype == "bf16":
+        new = bf16(new)
+    qd = to_dev(q)
+    caches = []
+    for _ in range(2):
+        Kd, Vd = to_dev(K), to_dev(V)
+        Kq, sc = ffd.alloc_kq(Kd, T)
+        ffd.quantize_k_append(Kd, 0, cap, T, Kq, sc, seq_len=cap)
+        lens = torch.tensor(init, dtype=torch.int32, device=DEV)
+        ws = ffd.alloc_workspace(ffd.dims_of(qd, Kd, cap), T, DEV)
+        caches.append((Kd, Vd, Kq, sc, lens, ws))
+    (Ka, Va, Kqa, sca, la, wsa), (Kb, Vb, Kqb, scb, lb, wsb) = caches
+    nbc = cap // T
+    for step in range(n_steps):
+        kn, vn = to_dev(new[step, 0]), to_dev(new[step, 1])
+        keep_a = torch.full((B, w.Hq, nbc), 7, dtype=torch.uint8, device=DEV)
+        keep_b = keep_a.clone()
+        ffd.append_token(kn, vn, Ka, Va, la, T, Kqa, sca)
+        oa, lsa = ffd.decode_sparse_varlen(qd, Ka, Va, Kqa, sca, la, delta, T, keep_mask=keep_a,
+                                           workspace=wsa)
+        ob, lsb = ffd.decode_sparse_append(qd, kn, vn, Kb, Vb, Kqb, scb, lb, delta, T,
+                                           keep_mask=keep_b, workspace=wsb)
+        torch.cuda.synchronize()
+        msg = f"step {step}, lengths {la.tolist()}"
+        assert torch.equal(la, lb), msg
+        assert torch.equal(keep_a, keep_b), msg
+        assert torch.equal(oa, ob), msg
+        assert torch.equal(lsa, lsb), msg
+    for name, x, y in (("K", Ka, Kb), ("V", Va, Vb), ("Kq", Kqa, Kqb), ("scales", sca, scb)):
+        assert torch.equal(x, y), name
+    final = [min(L + n_steps, cap) if L < cap else L for L in init]
+    assert lb.tolist() == final
+    # and the whole loop against the oracle on the final cache (each sequence's own prefix)
+    Kh, Vh = to_host(Kb), to_host(Vb)
+    Kq_o, sc_o = oracle.quantize_k(Kh, T)
+    o, l = ob.cpu().numpy(), lsb.cpu().numpy()
+    for b, L in enumerate(final):
+        nf = L // T
+        np.testing.assert_array_equal(Kqb.cpu().numpy()[b, :, :nf * T], Kq_o[b, :, :nf * T])
+        np.testing.assert_array_equal(to_host(scb)[b, :, :nf], sc_o[b, :, :nf])
+        if L == 0:
+            assert (o[b] == 0).all() and np.isneginf(l[b]).all()
+            continue
+        sl = slice(b, b + 1)
+        ref = oracle.decode(q[sl], Kh[sl], Vh[sl], L, T, delta, Kq=Kq_o[sl], scales=sc_o[sl])
+        tol = 2e-3 if dtype == "bf16" else 1e-5
+        assert_close(o[b], ref["out"][0], tol, f"out b={b} L={L}")
+        assert_close(l[b], ref["lse"][0], tol, f"lse b={b} L={L}")

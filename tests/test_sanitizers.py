@@ -140,6 +140,8 @@ def test_abi_layer_under_sanitizers(tmp_path):
             "decode_sparse_varlen": lambda: L.ffd_decode_sparse_varlen(
                 D, A, A, A, A, A, A, 5.0, T, A, A, None, A, ws, None),
             "decode_dense_varlen": lambda: L.ffd_decode_dense_varlen(D, A, A, A, A, T, A, A, A, ws, None),
+            "decode_sparse_append": lambda: L.ffd_decode_sparse_append(
+                D, A, A, A, A, A, A, A, A, 5.0, T, A, A, None, A, ws, None),
             "quantize_k_append": lambda: L.ffd_quantize_k_append(D, A, 0, 4096, T, A, A, None),
             "quantize_k_residual_append": lambda: L.ffd_quantize_k_residual_append(
                 D, A, 0, 4096, T, 2, A, A, A, A, None),
