@@ -44,10 +44,18 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert ffd.abi_version() == 2
+    m = re.search(r"#define FFD_ABI_VERSION (\d+)", HEADER.read_text())
+    assert ffd.abi_version() == ffd.ABI_VERSION == int(m.group(1))
     for s in range(5):
         assert ffd.status_string(s)
     assert ffd.status_string(99) == "unknown status"
+
+
+def test_build_entry_post_check(L):
+    # the checks build() runs after compiling: package import, ABI version, both libraries
+    import __graft_entry__
+
+    __graft_entry__.check_built()
 
 
 def dims(**kw):
