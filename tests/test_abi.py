@@ -73,11 +73,21 @@ def sparse_call(L, d, block=64, delta=5.0, q=A, ws=A, ws_bytes=1 << 30, K=A, kee
 
 
 
+def ws_need(units, S, width, d=128):
+    """Bytes one call needs: the counter region, then (m, l) and o of every (unit, split, head
+    of the unit) record, each region on a 256-byte boundary."""
+    rec = units * S * width
+    return COUNTER_BYTES + -(-rec * 8 // 256) * 256 + rec * d * 4
+
+
 def test_workspace_and_splits(L):
     d = dims()
     S = ffd.num_splits(d, 64)
     assert S >= 1
-    rec = 1 * 8 * S * 4                       # (unit, split, query head of the unit)
+    # 64 blocks over 8 kv heads: one block per wave (16 splits) for the sparse step; the dense
+    # step keeps two blocks per split (32), and the workspace covers both
+    assert S == 16 and ffd.num_splits(d, 64, sparse=False) == 32
+    rec = 1 * 8 * 32 * 4                      # (unit, split, query head of the unit)
     r256 = lambda x: -(-x // 256) * 256
     assert ffd.workspace_bytes(d, 64) == COUNTER_BYTES + r256(rec * 8) + rec * 128 * 4
     big = dims(B=8, seq_len=131072, seq_cap=131072)
@@ -111,12 +121,13 @@ def test_group_sizes_and_units(L, Hq, Hkv, units, width):
     Sd = ffd.num_splits(d, 64, sparse=False)
     assert S >= 1 and Sd >= 1
     # one work-group per CU: the split count follows the unit count (4096 tokens: 64 blocks,
-    # so at most 32 splits of two blocks each)
-    assert S == min(-(-256 // units), 32)
-    rec = units * max(S, Sd) * width
-    r256 = lambda x: -(-x // 256) * 256
-    assert ffd.workspace_bytes(d, 64) == COUNTER_BYTES + r256(rec * 8) + rec * 128 * 4
-    assert sparse_call(L, d, ws_bytes=ffd.workspace_bytes(d, 64) - 1) == ffd.FFD_ERR_WORKSPACE
+    # so at most 32 splits of two blocks each); the sparse step takes one block per wave (16
+    # splits) when its work-groups still fill half of the 256 CUs
+    s0 = min(-(-256 // units), 32)
+    assert Sd == s0
+    assert S == (16 if s0 > 16 and units * 16 >= 128 else s0)
+    assert ffd.workspace_bytes(d, 64) == ws_need(units, max(S, Sd), width)
+    assert sparse_call(L, d, ws_bytes=ws_need(units, S, width) - 1) == ffd.FFD_ERR_WORKSPACE
 
 
 def test_too_many_units_unsupported(L):
@@ -149,7 +160,8 @@ def test_bad_arguments(L):
     assert sparse_call(L, d, K=MISALIGNED) == ffd.FFD_ERR_INVALID_ARG
     assert sparse_call(L, d, keep=MISALIGNED) == ffd.FFD_ERR_INVALID_ARG
     assert sparse_call(L, d, ws=None) == ffd.FFD_ERR_WORKSPACE
-    assert sparse_call(L, d, ws_bytes=ffd.workspace_bytes(d, 64) - 1) == ffd.FFD_ERR_WORKSPACE
+    assert sparse_call(L, d, ws_bytes=ws_need(8, ffd.num_splits(d, 64), 4) - 1) == \
+        ffd.FFD_ERR_WORKSPACE
     assert L.ffd_decode_dense(ctypes.byref(d), A, A, A, 64, A, A, A, 16, None) == \
         ffd.FFD_ERR_WORKSPACE
     assert L.ffd_decode_dense(ctypes.byref(d), A, A, None, 64, A, A, A, 1 << 30, None) == \
