@@ -149,6 +149,39 @@ def test_named_workload_full_size(name):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("L,T", [(4096, 64), (4096 + 3 * 64 + 9, 64), (8192, 128)])
+def test_short_context_one_block_per_wave(L, T):
+    """The 32/8-head shape with a sink block and 0.5% needle blocks at short contexts, where the
+    sparse step runs one scan block per wave and so fewer splits than the dense step (a ragged
+    tail among them): Kq and scales byte-exact, every head's mask bit-exact, out and lse within
+    the tolerance, sparse and dense."""
+    base = W.WORKLOADS["gqa4_256k_sink_needles"]
+    nb = L // T
+    w = base.with_(name=f"short_L{L}_T{T}", L=L, T=T, n_needles=max(1, round(0.005 * nb)),
+                   seed=base.seed + 3 * L + T)
+    q, K, V, _ = W.make_inputs(w)
+    qd, Kd, Vd = upload(w, q, K, V)
+    dims = ffd.dims_of(qd, Kd, w.L)
+    S, Sd = ffd.num_splits(dims, T), ffd.num_splits(dims, T, False)
+    log(f"[gpu] {w.name}: sparse splits {S}, dense splits {Sd}")
+    assert S == -(-L // T) // 4 and S < Sd
+    Kq_d, sc_d = gpu_quantize(w, Kd)
+    Kq, sc = oracle_quantize(w, K)
+    np.testing.assert_array_equal(Kq_d.cpu().numpy(), Kq)
+    np.testing.assert_array_equal(to_host(sc_d), sc)
+    tol = TOL[w.dtype]
+    for delta in (2.0, 5.0):
+        out, lse, keep = gpu_sparse(w, qd, Kd, Vd, Kq_d, sc_d, delta)
+        ref = oracle.decode(q, K, V, w.L, w.T, delta=delta, Kq=Kq, scales=sc)
+        np.testing.assert_array_equal(keep, ref["keep"], err_msg=f"mask delta={delta}")
+        assert_close(out, ref["out"], tol, f"out delta={delta}")
+        assert_close(lse, ref["lse"], tol, f"lse delta={delta}")
+    out, lse = gpu_dense(w, qd, Kd, Vd)
+    ref = oracle.decode(q, K, V, w.L, w.T, sparse=False)
+    assert_close(out, ref["out"], tol, "dense out")
+    assert_close(lse, ref["lse"], tol, "dense lse")
+
+
 # --------------------------------------------------------------------------------------------
 # Properties of the HIP path itself
 # --------------------------------------------------------------------------------------------
