@@ -262,3 +262,61 @@ def test_fused_step_equals_append_then_decode(dtype, T, G, Hkv):
         tol = 2e-3 if dtype == "bf16" else 1e-5
         assert_close(o[b], ref["out"][0], tol, f"out b={b} L={L}")
         assert_close(l[b], ref["lse"][0], tol, f"lse b={b} L={L}")
+
+
+def test_fused_step_streaming_kernels_128k():
+    """The fused step at a length whose splits run the streaming-policy kernels (32 splits of 33
+    blocks of 128), over the step that completes a block: bit-identical to the pair of calls at
+    every step, and the last step against the oracle for every head."""
+    T, Hkv, G = 128, 8, 4
+    nbc = 1040
+    cap = nbc * T
+    init = 1025 * T - 2  # the second step completes block 1024
+    n_steps, delta = 4, 5.0
+    base = W.WORKLOADS["gqa4_256k_sink_needles"]
+    w = base.with_(name="fused_stream_128k", L=cap, n_needles=5, seed=base.seed + 17)
+    q, K, V, _ = W.make_inputs(w)
+    qd = to_dev(q)
+    caches = []
+    for _ in range(2):
+        Kd, Vd = to_dev(K), to_dev(V)
+        Kq, sc = ffd.alloc_kq(Kd, T)
+        ffd.quantize_k_append(Kd, 0, cap, T, Kq, sc, seq_len=cap)
+        lens = torch.tensor([init], dtype=torch.int32, device=DEV)
+        ws = ffd.alloc_workspace(ffd.dims_of(qd, Kd, cap), T, DEV)
+        caches.append((Kd, Vd, Kq, sc, lens, ws))
+    S = ffd.num_splits(ffd.dims_of(qd, caches[0][0], cap), T)
+    assert S == 32 and -(-nbc // S) >= 32, "the splits must be long enough for the streaming kernels"
+    log(f"fused step at 128K: {S} splits of {-(-nbc // S)} blocks, lengths from {init}")
+    rng = np.random.default_rng(2026)
+    new = bf16(rng.standard_normal((n_steps, 2, 1, Hkv, 128)).astype(np.float32))
+    (Ka, Va, Kqa, sca, la, wsa), (Kb, Vb, Kqb, scb, lb, wsb) = caches
+    for step in range(n_steps):
+        kn, vn = to_dev(new[step, 0]), to_dev(new[step, 1])
+        keep_a = torch.full((1, Hkv * G, nbc), 7, dtype=torch.uint8, device=DEV)
+        keep_b = keep_a.clone()
+        ffd.append_token(kn, vn, Ka, Va, la, T, Kqa, sca)
+        oa, lsa = ffd.decode_sparse_varlen(qd, Ka, Va, Kqa, sca, la, delta, T, keep_mask=keep_a,
+                                           workspace=wsa)
+        ob, lsb = ffd.decode_sparse_append(qd, kn, vn, Kb, Vb, Kqb, scb, lb, delta, T,
+                                           keep_mask=keep_b, workspace=wsb)
+        torch.cuda.synchronize()
+        msg = f"step {step}, length {la.tolist()}"
+        assert torch.equal(la, lb), msg
+        assert torch.equal(keep_a, keep_b), msg
+        assert torch.equal(oa, ob), msg
+        assert torch.equal(lsa, lsb), msg
+    for name, x, y in (("K", Ka, Kb), ("V", Va, Vb), ("Kq", Kqa, Kqb), ("scales", sca, scb)):
+        assert torch.equal(x, y), name
+    L = init + n_steps
+    assert lb.tolist() == [L]
+    # the last step against the oracle over the grown cache
+    Kh, Vh = to_host(Kb), to_host(Vb)
+    nf = L // T
+    Kq_o, sc_o = oracle.quantize_k(Kh, T, 0, L)
+    np.testing.assert_array_equal(Kqb.cpu().numpy()[:, :, :nf * T], Kq_o[:, :, :nf * T])
+    np.testing.assert_array_equal(to_host(scb)[:, :, :nf], sc_o[:, :, :nf])
+    ref = oracle.decode(q, Kh, Vh, L, T, delta, Kq=Kq_o, scales=sc_o)
+    np.testing.assert_array_equal(keep_b.cpu().numpy()[:, :, :-(-L // T)], ref["keep"])
+    assert_close(ob.cpu().numpy(), ref["out"], TOL, "out")
+    assert_close(lsb.cpu().numpy(), ref["lse"], TOL, "lse")
