@@ -1,0 +1,141 @@
+"""GPU parity of the streaming-policy decode kernels against the CPU oracle.
+
+Long splits run the decode kernels whose once-read data (the scan's codes and scales, the exact
+stage's values, the dense step's keys and values) is loaded with the streaming cache policy:
+half of the decode kernels, one per group width, dtype, block size and mode.  The full-size
+workloads reach them only at a few shapes, so here the split count is forced down with
+FFD_NUM_SPLITS until small inputs get splits that long (at least 32 blocks for the sparse step,
+4 for the dense step); the running-max mode reaches them through its window.
+
+Bar as everywhere: masks bit-exact, out and lse within 2e-3 (bf16) or 1e-5 (fp32) absolute.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import selection as S
+from conftest import log
+from helpers import (DEV, TOL, assert_close, gpu_dense, gpu_quantize, gpu_sparse, to_dev,
+                     upload)
+from long_context_decoding_amd import ffd
+from long_context_decoding_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+INF = float("inf")
+STREAM_BLOCKS = 32  # the shortest sparse split that runs the streaming-policy kernels
+N_BLOCKS = 70       # 70 full blocks and a ragged tail: two splits of 36 blocks
+
+
+def long_split_case(dt, G, T, seed):
+    Hkv = 2 if G <= 4 else 1
+    L = N_BLOCKS * T + 9
+    return W.small(f"stream_{dt}_G{G}_T{T}", B=2 if G <= 4 else 1, Hq=G * Hkv, Hkv=Hkv, L=L, T=T,
+                   dtype=dt, seed=seed, plant="needles" if G % 2 else "powerlaw")
+
+
+def force_long_splits(monkeypatch, w, qd, Kd):
+    monkeypatch.setenv("FFD_NUM_SPLITS", "2")
+    S_ = ffd.num_splits(ffd.dims_of(qd, Kd, w.L), w.T)
+    R = math.ceil(w.n_blocks / S_)
+    assert S_ == 2 and R >= STREAM_BLOCKS, (S_, R)
+    return R
+
+
+@pytest.mark.parametrize("dt,G,T", [(dt, G, T) for dt in ("bf16", "f32") for G in (1, 2, 3, 8, 12)
+                                    for T in (64, 128)])
+def test_sparse_and_dense(dt, G, T, monkeypatch):
+    w = long_split_case(dt, G, T, seed=900 + 10 * G + T + (dt == "f32"))
+    q, K, V, _ = W.make_inputs(w)
+    qd, Kd, Vd = upload(w, q, K, V)
+    R = force_long_splits(monkeypatch, w, qd, Kd)
+    log(f"[gpu] {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv}: 2 splits of {R} blocks")
+    Kq_d, sc_d = gpu_quantize(w, Kd)
+    Kq, sc = oracle.quantize_k(K, w.T, 0, w.L)
+    tol = TOL[dt]
+    for delta in (0.5, 5.0, INF):
+        out, lse, keep = gpu_sparse(w, qd, Kd, Vd, Kq_d, sc_d, delta)
+        ref = oracle.decode(q, K, V, w.L, w.T, delta=delta, Kq=Kq, scales=sc)
+        np.testing.assert_array_equal(keep, ref["keep"], err_msg=f"mask delta={delta}")
+        assert_close(out, ref["out"], tol, f"out delta={delta}")
+        assert_close(lse, ref["lse"], tol, f"lse delta={delta}")
+    out, lse = gpu_dense(w, qd, Kd, Vd)
+    ref = oracle.decode(q, K, V, w.L, w.T, sparse=False)
+    assert_close(out, ref["out"], tol, "dense out")
+    assert_close(lse, ref["lse"], tol, "dense lse")
+
+
+@pytest.mark.parametrize("dt,G,T", [("bf16", 4, 64), ("f32", 1, 128), ("bf16", 8, 128),
+                                    ("bf16", 12, 64)])
+def test_masked_attention(dt, G, T, monkeypatch):
+    """Attention over a caller's mask (top-k on the exact block maxima) in long splits."""
+    w = long_split_case(dt, G, T, seed=700 + G + T)
+    q, K, V, _ = W.make_inputs(w)
+    qd, Kd, Vd = to_dev(q), to_dev(K), to_dev(V)
+    force_long_splits(monkeypatch, w, qd, Kd)
+    s_ex = ffd.block_scores(ffd.SCORE_EXACT, qd, Kd, T, w.L)
+    keep = ffd.select_blocks(ffd.SELECT_TOP_K, s_ex, N_BLOCKS // 5, T, w.L, w.Hkv)
+    out, lse = ffd.decode_masked(qd, Kd, Vd, keep, T, w.L)
+    torch.cuda.synchronize()
+    keep, out, lse = keep.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
+    for b in range(w.B):
+        for h in range(w.Hq):
+            o_ref, l_ref = oracle.attend_head(q[b, h], K[b, h // w.G], V[b, h // w.G], w.L, T,
+                                              keep=keep[b, h])
+            assert_close(out[b, h], o_ref, TOL[dt], f"masked out b={b} h={h}")
+            assert_close(lse[b, h], l_ref, TOL[dt], f"masked lse b={b} h={h}")
+
+
+@pytest.mark.parametrize("dt,G,T", [("bf16", 4, 64), ("f32", 2, 128), ("bf16", 8, 64)])
+def test_running_max_long_windows(dt, G, T):
+    """The running-maximum mode with windows of 32 and more blocks (each window is one split)."""
+    w = long_split_case(dt, G, T, seed=500 + G + T)
+    q, K, V, _ = W.make_inputs(w)
+    qd, Kd, Vd = to_dev(q), to_dev(K), to_dev(V)
+    nf, nb = w.n_full, w.n_blocks
+    Kq, sc = ffd.alloc_kq(Kd, T)
+    ffd.quantize_k_append(Kd, 0, w.L, T, Kq, sc, seq_len=w.L)
+    Kq_o, sc_o = oracle.quantize_k(K, T)
+    ref = oracle.decode(q, K, V, w.L, T, 5.0, Kq=Kq_o, scales=sc_o, want_shat=True)
+    for delta in (2.0, 5.0):
+        for window in (STREAM_BLOCKS, 50, nb):
+            log(f"[gpu] {w.name} running window={window} delta={delta}")
+            keep = torch.full((w.B, w.Hq, nb), 7, dtype=torch.uint8, device=DEV)
+            out, lse = ffd.decode_sparse_running(qd, Kd, Vd, Kq, sc, delta, T, window, w.L,
+                                                 keep_mask=keep)
+            torch.cuda.synchronize()
+            keep, out, lse = keep.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
+            for b in range(w.B):
+                for h in range(w.Hq):
+                    want = S.select_running(ref["shat"][b, h], float(ref["mtilde"][b, h]), nf, nb,
+                                            delta, window)
+                    np.testing.assert_array_equal(keep[b, h], want,
+                                                  err_msg=f"b={b} h={h} delta={delta} W={window}")
+                    g = h // w.G
+                    o_ref, l_ref = oracle.attend_head(q[b, h], K[b, g], V[b, g], w.L, T, keep=want)
+                    assert_close(out[b, h], o_ref, TOL[dt], f"out b={b} h={h} W={window}")
+                    assert_close(lse[b, h], l_ref, TOL[dt], f"lse b={b} h={h} W={window}")
+
+
+@pytest.mark.parametrize("bits,G,T", [(2, 1, 64), (4, 4, 128), (2, 8, 128), (4, 3, 64)])
+def test_residual_form(bits, G, T, monkeypatch):
+    """The storage form (thumbnail + 8-bit residual) in long splits."""
+    w = long_split_case("bf16", G, T, seed=300 + 10 * bits + G + T)
+    q, K, V, _ = W.make_inputs(w)
+    qd, Kd, Vd = upload(w, q, K, V)
+    force_long_splits(monkeypatch, w, qd, Kd)
+    kres_d = ffd.alloc_kres(Kd, T, bits)
+    ffd.quantize_k_residual_append(Kd, 0, w.L, T, bits, kres_d, seq_len=w.L)
+    kres_o = oracle.quantize_k_res(K, T, bits, 0, w.L)
+    for delta in (2.0, 5.0, INF):
+        keep = torch.full((w.B, w.Hq, w.n_blocks), 7, dtype=torch.uint8, device=DEV)
+        out, lse = ffd.decode_sparse_residual(qd, Kd, Vd, kres_d, bits, delta, T, w.L,
+                                              keep_mask=keep)
+        torch.cuda.synchronize()
+        ref = oracle.decode_res(q, K, V, *kres_o, w.L, T, bits, delta=delta)
+        np.testing.assert_array_equal(keep.cpu().numpy(), ref["keep"], err_msg=f"delta={delta}")
+        assert_close(out.cpu().numpy(), ref["out"], TOL["bf16"], f"out delta={delta}")
+        assert_close(lse.cpu().numpy(), ref["lse"], TOL["bf16"], f"lse delta={delta}")
