@@ -139,3 +139,40 @@ def test_residual_form(bits, G, T, monkeypatch):
         np.testing.assert_array_equal(keep.cpu().numpy(), ref["keep"], err_msg=f"delta={delta}")
         assert_close(out.cpu().numpy(), ref["out"], TOL["bf16"], f"out delta={delta}")
         assert_close(lse.cpu().numpy(), ref["lse"], TOL["bf16"], f"lse delta={delta}")
+
+
+@pytest.mark.parametrize("dt,G,T", [("bf16", 4, 64), ("f32", 1, 128), ("bf16", 8, 128)])
+def test_varlen_per_sequence(dt, G, T, monkeypatch):
+    """Per-sequence lengths from device memory (the decode loop's calls), sparse and dense, in
+    long splits: every sequence against the oracle on its own prefix."""
+    w = long_split_case(dt, G, T, seed=200 + G + T)
+    w = w.with_(B=4, L=(N_BLOCKS + 2) * T)
+    q, K, V, _ = W.make_inputs(w)
+    qd, Kd, Vd = to_dev(q), to_dev(K), to_dev(V)
+    force_long_splits(monkeypatch, w, qd, Kd)
+    cap = w.L
+    lens = np.array([cap, N_BLOCKS * T + 9, 40 * T, 3 * T + 5], dtype=np.int32)
+    Kq, sc = ffd.alloc_kq(Kd, T)
+    ffd.quantize_k_append(Kd, 0, cap, T, Kq, sc, seq_len=cap)
+    Kq_o, sc_o = oracle.quantize_k(K, T)
+    lens_d = torch.from_numpy(lens).to(DEV)
+    nbc = cap // T
+    tol = TOL[dt]
+    for delta in (2.0, 5.0):
+        keep = torch.full((w.B, w.Hq, nbc), 7, dtype=torch.uint8, device=DEV)
+        out, lse = ffd.decode_sparse_varlen(qd, Kd, Vd, Kq, sc, lens_d, delta, T, keep_mask=keep)
+        outd, lsed = ffd.decode_dense_varlen(qd, Kd, Vd, lens_d, T)
+        torch.cuda.synchronize()
+        out, lse, keep = out.cpu().numpy(), lse.cpu().numpy(), keep.cpu().numpy()
+        outd, lsed = outd.cpu().numpy(), lsed.cpu().numpy()
+        for b, L in enumerate(lens):
+            sl = slice(b, b + 1)
+            ref = oracle.decode(q[sl], K[sl], V[sl], int(L), T, delta, Kq=Kq_o[sl], scales=sc_o[sl])
+            nb = math.ceil(L / T)
+            np.testing.assert_array_equal(keep[b, :, :nb], ref["keep"][0, :, :nb],
+                                          err_msg=f"mask b={b} L={L} delta={delta}")
+            assert_close(out[b], ref["out"][0], tol, f"out b={b} L={L} delta={delta}")
+            assert_close(lse[b], ref["lse"][0], tol, f"lse b={b} L={L} delta={delta}")
+            dref = oracle.decode(q[sl], K[sl], V[sl], int(L), T, sparse=False)
+            assert_close(outd[b], dref["out"][0], tol, f"dense out b={b} L={L}")
+            assert_close(lsed[b], dref["lse"][0], tol, f"dense lse b={b} L={L}")
